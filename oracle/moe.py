@@ -1,0 +1,122 @@
+"""Fused W8A8 FP8 block-scaled MoE expert layer, stage by stage.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Stages follow the AlphaMoE page, section "Problem: the MoE expert bottleneck"
+(and its conceptual "before" kernel list): GEMM1 over gate and up, SwiGLU,
+intermediate FP8 requantisation, GEMM2 over down, combine.  The operand
+conventions follow the SM120 grouped-GEMM page, section 1: both operands are
+K-contiguous ("NT"), the gated GEMM's weight has 2*I rows with the gate rows
+first and the up rows second, activation scales are per row and 128 columns
+(1x128) and weight scales per 128x128 block.
+
+Precision: dequantisation, both GEMMs, SwiGLU and the combine run in float64.
+The intermediate requantisation decision (amax, s = amax/448, fl32(act/s),
+e4m3 encode) is taken in float32, on the float32 rounding of the activation,
+which is the precision the kernels take it in.  The output is rounded once to
+bfloat16 (via float32).
+
+Inputs (numpy, or anything indexable by expert for the weights):
+  x_q   uint8  [T, H]             e4m3 codes of the activations
+  x_s   f32    [T, H/128]         1x128 activation scales
+  w13_q uint8  [E][2I, H]         gate rows 0..I-1, up rows I..2I-1
+  w13_s f32    [E][2I/128, H/128] 128x128 block scales
+  w2_q  uint8  [E][H, I]
+  w2_s  f32    [E][H/128, I/128]
+  topk_ids     int  [T, K]        ids outside [0, E) are dropped slots
+  topk_weights f32  [T, K]
+"""
+
+import numpy as np
+
+from . import formats
+
+
+def silu_mul(g, u):
+    """SwiGLU in float64: g * sigmoid(g) * u = g * u / (1 + exp(-g))."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def expert_rows(topk_ids, E, tokens=None):
+    """Valid (token, slot) rows of each expert, ascending by src = t*K + j.
+
+    Returns {e: list of (t, j)} for the given tokens (all tokens by default).
+    """
+    ids = np.asarray(topk_ids)
+    T, K = ids.shape
+    toks = range(T) if tokens is None else sorted(int(t) for t in tokens)
+    rows = {}
+    for t in toks:
+        for j in range(K):
+            e = int(ids[t, j])
+            if 0 <= e < E:
+                rows.setdefault(e, []).append((t, j))
+    return rows
+
+
+def expert_ffn(xq_rows, xs_rows, w13_q, w13_s, w2_q, w2_s, stages=None):
+    """One expert on its gathered rows: GEMM1 -> SwiGLU -> requant -> GEMM2.
+
+    xq_rows/xs_rows are the gathered activation codes/scales of the rows.
+    Returns Y (float64 [n, H]), the expert's output per row before weighting.
+    """
+    A = formats.dequant_rows(xq_rows, xs_rows)                   # [n, H]
+    W13 = formats.dequant_blocks(np.asarray(w13_q), np.asarray(w13_s))   # [2I, H]
+    I = W13.shape[0] // 2
+    H1 = A @ W13.T                                               # GEMM1, [n, 2I]
+    g, u = H1[:, :I], H1[:, I:]
+    act = silu_mul(g, u).astype(np.float32)                      # SwiGLU, one fp32 rounding
+    q, s = formats.quantize_rows(act, 128)                       # requant (fp32 decision)
+    W2 = formats.dequant_blocks(np.asarray(w2_q), np.asarray(w2_s))      # [H, I]
+    Y = formats.dequant_rows(q, s) @ W2.T                        # GEMM2, [n, H]
+    if stages is not None:
+        stages.update(H1=H1, act=act, q=q, s=s, Y=Y)
+    return Y
+
+
+def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
+                  tokens=None, return_stages=False):
+    """Reference fused MoE layer.
+
+    Returns (out_bits, out) for the requested tokens (all tokens by default,
+    in ascending token order): out_bits uint16 bf16 patterns [n_tok, H] and
+    out float32 values of those patterns.  With return_stages=True a third
+    item maps each expert to its rows and per-stage intermediates.
+    """
+    ids = np.asarray(topk_ids)
+    wts = np.asarray(topk_weights, dtype=np.float32)
+    T, K = ids.shape
+    E = len(w13_q)
+    H = np.asarray(x_q).shape[1]
+    toks = list(range(T)) if tokens is None else sorted(int(t) for t in tokens)
+    pos = {t: i for i, t in enumerate(toks)}
+
+    rows = expert_rows(ids, E, toks)
+    Ysl = {}                      # (t, j) -> float64 [H]
+    stages = {}
+    for e in sorted(rows):
+        tj = rows[e]
+        tok_idx = np.array([t for t, _ in tj], dtype=np.int64)
+        st = {} if return_stages else None
+        Y = expert_ffn(np.asarray(x_q)[tok_idx], np.asarray(x_s)[tok_idx],
+                       w13_q[e], w13_s[e], w2_q[e], w2_s[e], st)
+        for r, (t, j) in enumerate(tj):
+            Ysl[(t, j)] = Y[r]
+        if return_stages:
+            st["rows"] = tj
+            stages[e] = st
+
+    # combine: weighted sum over the token's valid slots in ascending j
+    acc = np.zeros((len(toks), H), dtype=np.float64)
+    for t in toks:
+        for j in range(K):
+            if (t, j) in Ysl:
+                acc[pos[t]] += np.float64(wts[t, j]) * Ysl[(t, j)]
+    out_bits = formats.bf16_bits(acc.astype(np.float32))
+    out = formats.bf16_decode(out_bits).astype(np.float32)
+    if return_stages:
+        return out_bits, out, stages
+    return out_bits, out

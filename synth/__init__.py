@@ -1,0 +1,186 @@
+"""Seeded synthetic inputs for the FP8 block-scaled MoE expert path.
+
+This module builds the inputs that both the HIP path and the CPU oracle
+consume.  It holds the input recipe only: router logits -> softmax -> top-k ->
+renormalised weights, N(0,1) activations, N(0, 0.02^2) expert weights, and the
+harness quantisation of those fp32 values into the fp8 e4m3 codes plus fp32
+block scales that the expert path takes as input (1x128 for activations,
+128x128 for weights; scale = amax/448, codes from torch's own float8_e4m3fn
+cast after clamping to +-448).  None of the expert computation (GEMMs,
+SwiGLU, requantisation, combine) is here.
+
+Seeds: numpy streams come from SeedSequence([cfg, tag, idx, *extra]); torch
+streams (used for the large weight sets, generated where they will live) are
+seeded with a 63-bit integer drawn from the same SeedSequence.
+"""
+
+import numpy as np
+import torch
+
+# config ids
+CFG_TINY, CFG_GATED, CFG_LARGE, CFG_PREFILL, CFG_SKEWED = 1, 2, 3, 4, 5
+# stream tags
+TAG_LOGITS, TAG_X, TAG_W13, TAG_W2, TAG_GA_IN, TAG_GA_EXP = 0, 1, 2, 3, 4, 5
+
+E4M3_MAX = 448.0
+
+
+def rng(cfg, tag, idx=0, extra=()):
+    return np.random.default_rng(np.random.SeedSequence([cfg, tag, idx, *extra]))
+
+
+def torch_seed(cfg, tag, idx=0, extra=()):
+    ss = np.random.SeedSequence([cfg, tag, idx, *extra])
+    return int(ss.generate_state(1, dtype=np.uint64)[0]) & ((1 << 63) - 1)
+
+
+# ---------------------------------------------------------------- routing
+
+def router(T, E, K, cfg, extra=(), zipf_s=None):
+    """Top-k routing from seeded N(0,1) logits.
+
+    softmax over experts (float64), top-k by descending probability with ties
+    to the lower expert index, weights renormalised to sum 1, cast to float32.
+    zipf_s adds a per-expert bias -s*ln(e+1) to every token's logits (a Zipf
+    prior over expert popularity, identity rank order).
+    Returns (topk_ids int32 [T, K], topk_weights float32 [T, K]).
+    """
+    logits = rng(cfg, TAG_LOGITS, 0, extra).standard_normal((T, E))
+    if zipf_s is not None:
+        logits = logits - zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))[None, :]
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    p /= p.sum(axis=1, keepdims=True)
+    order = np.argsort(-p, axis=1, kind="stable")[:, :K]
+    w = np.take_along_axis(p, order, axis=1)
+    w = w / w.sum(axis=1, keepdims=True)
+    return order.astype(np.int32), w.astype(np.float32)
+
+
+# ---------------------------------------------------------------- quantisation (input recipe)
+
+def _scales_from_amax(amax):
+    s = amax / E4M3_MAX
+    return torch.where(amax == 0, torch.ones_like(s), s)
+
+
+def quant_rows_1x128(x):
+    """fp32 torch [R, C] -> (uint8 codes [R, C], fp32 scales [R, C/128]) on x's device."""
+    R, C = x.shape
+    xb = x.reshape(R, C // 128, 128)
+    s = _scales_from_amax(xb.abs().amax(dim=2))
+    q = (xb / s[:, :, None]).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(R, C), s.contiguous()
+
+
+def quant_blocks_128(w):
+    """fp32 torch [N, K] -> (uint8 codes [N, K], fp32 scales [N/128, K/128])."""
+    N, K = w.shape
+    wb = w.reshape(N // 128, 128, K // 128, 128)
+    s = _scales_from_amax(wb.abs().amax(dim=(1, 3)))
+    q = (wb / s[:, None, :, None]).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(N, K), s.contiguous()
+
+
+# ---------------------------------------------------------------- activations and weights
+
+def activations(T, H, cfg, extra=()):
+    """x ~ N(0,1) fp32 [T, H] (numpy)."""
+    return rng(cfg, TAG_X, 0, extra).standard_normal((T, H), dtype=np.float32)
+
+
+def expert_weights_fp32(E, N, K, cfg, tag, e, std=0.02):
+    """One expert's fp32 weight [N, K] ~ N(0, std^2) (numpy, seeded per expert)."""
+    return rng(cfg, tag, e).standard_normal((N, K), dtype=np.float32) * np.float32(std)
+
+
+def expert_weight_set(E, N, K, cfg, tag, device="cpu", std=0.02):
+    """All experts' quantised weights: (codes uint8 [E, N, K], scales fp32 [E, N/128, K/128]).
+
+    On "cpu" each expert comes from its numpy stream; on a GPU device each
+    expert is drawn with a torch generator on that device (seeded from the
+    same SeedSequence) so large sets never cross the host.
+    """
+    q = torch.empty((E, N, K), dtype=torch.uint8, device=device)
+    s = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=device)
+    dev = torch.device(device)
+    for e in range(E):
+        if dev.type == "cpu":
+            w = torch.from_numpy(expert_weights_fp32(E, N, K, cfg, tag, e, std))
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(torch_seed(cfg, tag, e))
+            w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * std
+        qe, se = quant_blocks_128(w)
+        q[e].copy_(qe)
+        s[e].copy_(se)
+    return q, s
+
+
+class MoEInputs:
+    """Host/device tensors of one MoE problem (torch tensors, one device)."""
+
+    def __init__(self, T, H, I, E, K, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights):
+        self.T, self.H, self.I, self.E, self.K = T, H, I, E, K
+        self.x_q, self.x_s = x_q, x_s
+        self.w13_q, self.w13_s = w13_q, w13_s
+        self.w2_q, self.w2_s = w2_q, w2_s
+        self.topk_ids, self.topk_weights = topk_ids, topk_weights
+
+    def to(self, device):
+        f = lambda t: t.to(device)
+        return MoEInputs(self.T, self.H, self.I, self.E, self.K, f(self.x_q), f(self.x_s),
+                         f(self.w13_q), f(self.w13_s), f(self.w2_q), f(self.w2_s),
+                         f(self.topk_ids), f(self.topk_weights))
+
+    def with_tokens(self, x_q, x_s, topk_ids, topk_weights):
+        T = x_q.shape[0]
+        return MoEInputs(T, self.H, self.I, self.E, self.K, x_q, x_s, self.w13_q, self.w13_s,
+                         self.w2_q, self.w2_s, topk_ids, topk_weights)
+
+
+def moe_tokens(T, H, E, K, cfg, extra=(), zipf_s=None, device="cpu"):
+    """Token-side inputs: (x_q, x_s, topk_ids, topk_weights) as torch tensors."""
+    ids, w = router(T, E, K, cfg, extra, zipf_s)
+    x = torch.from_numpy(activations(T, H, cfg, extra))
+    x_q, x_s = quant_rows_1x128(x)
+    return (x_q.to(device), x_s.to(device), torch.from_numpy(ids).to(device),
+            torch.from_numpy(w).to(device))
+
+
+def moe_problem(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weight_cfg=None,
+                weight_device=None):
+    """A full MoE problem.  Weights use weight_cfg (default cfg) so several token
+    sets can share one weight set."""
+    wc = cfg if weight_cfg is None else weight_cfg
+    wd = device if weight_device is None else weight_device
+    x_q, x_s, ids, w = moe_tokens(T, H, E, K, cfg, extra, zipf_s, device)
+    w13_q, w13_s = expert_weight_set(E, 2 * I, H, wc, TAG_W13, wd)
+    w2_q, w2_s = expert_weight_set(E, H, I, wc, TAG_W2, wd)
+    return MoEInputs(T, H, I, E, K, x_q, x_s, w13_q.to(device), w13_s.to(device),
+                     w2_q.to(device), w2_s.to(device), ids, w)
+
+
+# named configurations (token count T, hidden H, intermediate I, experts E, top-k K)
+TINY = dict(T=16, H=256, I=128, E=4, K=2)
+LARGE_DIMS = dict(H=7168, I=2048, E=256, K=8)      # decode (T=64) and prefill (T=8192)
+SKEWED_DIMS = dict(H=2048, I=768, E=128, K=8)      # T in {1, 33, 512, 4096}, Zipf(1.2) bias
+SKEWED_TS = (1, 33, 512, 4096)
+ZIPF_S = 1.2
+GATED_SHAPES = ((128, 128), (1024, 1024), (4096, 1024), (8192, 7168))
+
+
+# ---------------------------------------------------------------- gated activation inputs
+
+def gated_act_input(M, N, block_scaled=False, extra=()):
+    """bf16 [M, 2N] (gate | up) as a torch tensor.
+
+    Values ~ N(0,1); with block_scaled, each 1x32 block of the [M, 2N] input is
+    multiplied by 2^k, k uniform on {-8, ..., 8}, before the bf16 cast.
+    """
+    a = rng(CFG_GATED, TAG_GA_IN, 0, (M, N, *extra)).standard_normal((M, 2 * N), dtype=np.float32)
+    if block_scaled:
+        k = rng(CFG_GATED, TAG_GA_EXP, 0, (M, N, *extra)).integers(-8, 9, size=(M, 2 * N // 32))
+        a = (a.reshape(M, 2 * N // 32, 32) * np.ldexp(np.float32(1.0), k)[:, :, None]).astype(np.float32)
+        a = a.reshape(M, 2 * N)
+    return torch.from_numpy(a).to(torch.bfloat16)
