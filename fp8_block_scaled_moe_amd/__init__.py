@@ -1,0 +1,13 @@
+"""MI355X (gfx950) W8A8 FP8 block-scaled MoE expert path.
+
+The computation lives in libfp8moe.so (hand-written HIP kernels behind the C
+ABI of include/fp8moe.h); this package only loads it and marshals torch
+tensors into it.
+"""
+
+from ._lib import lib, Fp8MoeError, LIB_PATH  # noqa: F401
+from .ops import (  # noqa: F401
+    route_capacity, route_permute, fused_workspace_size, alloc_workspace, moe_fused_fp8,
+    gemm1_swiglu_quant, gemm2_weighted, combine, gated_act_fp8_quant, select_tile,
+    select_tile_classes,
+)

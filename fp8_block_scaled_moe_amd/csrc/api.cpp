@@ -1,0 +1,306 @@
+// C ABI of the FP8 MoE expert path: validation, status reporting, workspace
+// carving, tile selection and launch sequencing on the caller's stream.
+// Every check runs before anything is enqueued; nothing here allocates device
+// memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+#include <string>
+
+#include "fp8moe.h"
+#include "launch.h"
+#include "tile_select.h"
+
+using namespace fp8moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FP8MOE_OK;
+}
+
+int hip_fail(hipError_t err, const char* what) {
+  return fail(FP8MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool valid_tile_m(int t) { return t == 16 || t == 32 || t == 64 || t == 128; }
+bool valid_align(int a) { return a == 16 || a == 32 || a == 64 || a == 128; }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+constexpr size_t kAlignWs = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout of moe_fused_fp8 (each part 256-byte aligned).
+struct WsLayout {
+  size_t counts, m_indptr, padded, sorted_src, src_to_sorted, q, q_scale, Y, total;
+};
+
+WsLayout ws_layout(int64_t T, int H, int I, int E, int K) {
+  const int64_t R = T * K;
+  const int64_t cap = R + (int64_t)E * (128 - 1);  // worst case: align 128
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = round_up(off + bytes, kAlignWs); return at; };
+  w.counts = take(sizeof(int32_t) * E);
+  w.m_indptr = take(sizeof(int32_t) * (E + 1));
+  w.padded = take(sizeof(int32_t) * (E + 1));
+  w.sorted_src = take(sizeof(int32_t) * cap);
+  w.src_to_sorted = take(sizeof(int32_t) * (R > 0 ? R : 1));
+  w.q = take((size_t)cap * I);
+  w.q_scale = take(sizeof(float) * (size_t)cap * (I / 128));
+  w.Y = take(sizeof(uint16_t) * (size_t)(R > 0 ? R : 1) * H);
+  w.total = off;
+  return w;
+}
+
+int check_dims(int64_t T, int H, int I, int E, int K) {
+  if (T < 0) return fail(FP8MOE_ERR_SHAPE, "T must be >= 0 (got %lld)", (long long)T);
+  if (H <= 0 || I <= 0) return fail(FP8MOE_ERR_SHAPE, "H and I must be positive (got %d, %d)", H, I);
+  if (H % 128 || I % 128)
+    return fail(FP8MOE_ERR_ALIGN, "H and I must be multiples of 128 (got %d, %d)", H, I);
+  if (E < 1) return fail(FP8MOE_ERR_SHAPE, "E must be >= 1 (got %d)", E);
+  if (E > FP8MOE_MAX_EXPERTS) return fail(FP8MOE_ERR_LIMIT, "E=%d exceeds %d", E, FP8MOE_MAX_EXPERTS);
+  if (K < 1 || K > E) return fail(FP8MOE_ERR_TOPK, "top-k K=%d outside [1, E=%d]", K, E);
+  if (T * K + (int64_t)E * 127 >= kMaxRows)
+    return fail(FP8MOE_ERR_SHAPE, "T*K + E*127 = %lld overflows the int32 row space",
+                (long long)(T * K + (int64_t)E * 127));
+  return FP8MOE_OK;
+}
+
+int device_num_cu() {
+  static std::atomic<int> cached{0};
+  int v = cached.load();
+  if (v > 0) return v;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cached.store(n);
+  return n;
+}
+
+int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
+  if (requested != -1) return requested;
+  return select_tile_m(R, n, k, E, device_num_cu(), mi355x_classes(gated));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case FP8MOE_OK: return "ok";
+    case FP8MOE_ERR_NULL: return "null pointer";
+    case FP8MOE_ERR_SHAPE: return "invalid shape";
+    case FP8MOE_ERR_ALIGN: return "dimension not a multiple of the block size";
+    case FP8MOE_ERR_TOPK: return "top-k outside [1, E]";
+    case FP8MOE_ERR_TILE: return "unsupported tile or variant";
+    case FP8MOE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case FP8MOE_ERR_HIP: return "HIP runtime error";
+    case FP8MOE_ERR_LIMIT: return "beyond a library limit";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int64_t moe_route_capacity(int64_t T, int32_t K, int32_t E, int32_t align) {
+  if (T < 0 || K < 1 || E < 1) return fail(FP8MOE_ERR_SHAPE, "invalid T/K/E");
+  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
+  ok();
+  return T * K + (int64_t)E * (align - 1);
+}
+
+int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t align,
+                      int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
+                      int32_t* sorted_src, int32_t* src_to_sorted, void* stream) {
+  if (T < 0) return fail(FP8MOE_ERR_SHAPE, "T must be >= 0");
+  if (E < 1) return fail(FP8MOE_ERR_SHAPE, "E must be >= 1");
+  if (E > FP8MOE_MAX_EXPERTS) return fail(FP8MOE_ERR_LIMIT, "E=%d exceeds %d", E, FP8MOE_MAX_EXPERTS);
+  if (K < 1 || K > E) return fail(FP8MOE_ERR_TOPK, "top-k K=%d outside [1, E=%d]", K, E);
+  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
+  const int64_t cap = T * K + (int64_t)E * (align - 1);
+  if (cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "capacity %lld overflows int32", (long long)cap);
+  if (!counts || !m_indptr || !padded_indptr || !sorted_src) return fail(FP8MOE_ERR_NULL, "null output");
+  if (T > 0 && (!topk_ids || !src_to_sorted)) return fail(FP8MOE_ERR_NULL, "null topk_ids/src_to_sorted");
+  hipError_t err = launch_route_permute(topk_ids, (int)(T * K), E, align, (int)cap, counts, m_indptr,
+                                        padded_indptr, sorted_src, src_to_sorted, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "route_permute launch");
+  return ok();
+}
+
+int moe_fused_fp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, size_t* bytes) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
+  *bytes = ws_layout(T, H, I, E, K).total;
+  return ok();
+}
+
+int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                  const void* w2, const float* w2_scale, const int32_t* topk_ids,
+                  const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                  void* out, void* workspace, size_t workspace_bytes, int32_t tile_m, int32_t tile_n,
+                  void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (tile_m != -1 && !valid_tile_m(tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
+  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
+  if (T == 0) return ok();
+  if (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  const WsLayout L = ws_layout(T, H, I, E, K);
+  if (!workspace) return fail(FP8MOE_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % kAlignWs) return fail(FP8MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(FP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+
+  const int64_t R = T * K;
+  const int tm1 = pick_tile_m(tile_m, R, I, H, E, true);
+  const int tm2 = pick_tile_m(tile_m, R, H, I, E, false);
+  const int align = tm1 > tm2 ? tm1 : tm2;
+  const int64_t cap = R + (int64_t)E * (align - 1);
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* m_indptr = reinterpret_cast<int32_t*>(ws + L.m_indptr);
+  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
+  int32_t* sorted_src = reinterpret_cast<int32_t*>(ws + L.sorted_src);
+  int32_t* src_to_sorted = reinterpret_cast<int32_t*>(ws + L.src_to_sorted);
+  uint8_t* q = ws + L.q;
+  float* q_scale = reinterpret_cast<float*>(ws + L.q_scale);
+  uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t err = launch_route_permute(topk_ids, (int)R, E, align, (int)cap, counts, m_indptr, padded,
+                                        sorted_src, src_to_sorted, s);
+  if (err != hipSuccess) return hip_fail(err, "route_permute launch");
+  GroupedRows g{padded, sorted_src, cap, E, K};
+  err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
+                     g, H, I, q, q_scale, tm1, s);
+  if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
+  err = launch_gemm2(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2,
+                     256, s);
+  if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
+  err = launch_combine(Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return ok();
+}
+
+int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                           const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
+                           int32_t I, int32_t E, int32_t K, int32_t align, void* q, float* q_scale,
+                           int64_t cap, int32_t tile_m, void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
+  if (tile_m != -1 && (!valid_tile_m(tile_m) || align % tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d must be in {16,32,64,128} and divide align %d", tile_m, align);
+  if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
+  if (T == 0 || cap == 0) return ok();
+  if (!x || !x_scale || !w13 || !w13_scale || !padded_indptr || !sorted_src || !q || !q_scale)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
+  while (align % tm) tm >>= 1;
+  GroupedRows g{padded_indptr, sorted_src, cap, E, K};
+  hipError_t err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
+                                w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
+  return ok();
+}
+
+int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, const float* w2_scale,
+                       const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
+                       int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y,
+                       int64_t cap, int32_t tile_m, int32_t tile_n, void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
+  if (tile_m != -1 && (!valid_tile_m(tile_m) || align % tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d must be in {16,32,64,128} and divide align %d", tile_m, align);
+  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
+  if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
+  if (T == 0 || cap == 0) return ok();
+  if (!q || !q_scale || !w2 || !w2_scale || !padded_indptr || !sorted_src || !topk_weights || !Y)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
+  while (align % tm) tm >>= 1;
+  GroupedRows g{padded_indptr, sorted_src, cap, E, K};
+  hipError_t err = launch_gemm2(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2),
+                                w2_scale, topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm, 256,
+                                (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
+  return ok();
+}
+
+int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E, int32_t K, void* out,
+                void* stream) {
+  if (T < 0 || H <= 0 || E < 1) return fail(FP8MOE_ERR_SHAPE, "invalid T/H/E");
+  if (H % 128) return fail(FP8MOE_ERR_ALIGN, "H must be a multiple of 128");
+  if (K < 1 || K > E) return fail(FP8MOE_ERR_TOPK, "top-k K=%d outside [1, E=%d]", K, E);
+  if (T * K >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "T*K overflows int32");
+  if (T == 0) return ok();
+  if (!Y || !topk_ids || !out) return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  hipError_t err = launch_combine(static_cast<const uint16_t*>(Y), topk_ids, (int)T, H, E, K,
+                                  static_cast<uint16_t*>(out), (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return ok();
+}
+
+int gated_act_fp8_quant(const void* in, int64_t M, int32_t N, void* out, uint8_t* scale_e8m0, int32_t variant,
+                        void* stream) {
+  if (M < 0 || N <= 0) return fail(FP8MOE_ERR_SHAPE, "invalid M=%lld N=%d", (long long)M, N);
+  if (N % 32) return fail(FP8MOE_ERR_ALIGN, "N=%d must be a multiple of 32", N);
+  if (variant < -1 || variant > 1) return fail(FP8MOE_ERR_TILE, "variant %d not in {-1,0,1}", variant);
+  if (M == 0) return ok();
+  if (!in || !out || !scale_e8m0) return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  const int v = variant >= 0 ? variant : (M * (int64_t)N < ((int64_t)1 << 20) ? 0 : 1);
+  hipError_t err = launch_gated_act(static_cast<const uint16_t*>(in), M, N, static_cast<uint8_t*>(out),
+                                    scale_e8m0, v, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "gated_act launch");
+  return ok();
+}
+
+int moe_select_tile(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t num_cu, int32_t gated,
+                    int32_t* tile_m, int32_t* tile_n) {
+  if (total_rows < 0 || n <= 0 || k <= 0 || E < 1 || num_cu < 1)
+    return fail(FP8MOE_ERR_SHAPE, "invalid selector arguments");
+  if (!tile_m || !tile_n) return fail(FP8MOE_ERR_NULL, "null output");
+  const TileClasses tc = mi355x_classes(gated != 0);
+  *tile_m = select_tile_m(total_rows, n, k, E, num_cu, tc);
+  *tile_n = tc.tile_n_128;
+  return ok();
+}
+
+int moe_select_tile_classes(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t num_cu,
+                            int32_t narrow, int32_t tile_n_narrow, int32_t tile_n_32, int32_t tile_n_64,
+                            int32_t tile_n_128, int32_t* tile_m) {
+  if (total_rows < 0 || n <= 0 || k <= 0 || E < 1 || num_cu < 1 || narrow < 1 || tile_n_narrow < 1 ||
+      tile_n_32 < 1 || tile_n_64 < 1 || tile_n_128 < 1)
+    return fail(FP8MOE_ERR_SHAPE, "invalid selector arguments");
+  if (!tile_m) return fail(FP8MOE_ERR_NULL, "null output");
+  const TileClasses tc{narrow, tile_n_narrow, tile_n_32, tile_n_64, tile_n_128};
+  *tile_m = select_tile_m(total_rows, n, k, E, num_cu, tc);
+  return ok();
+}
+
+}  // extern "C"

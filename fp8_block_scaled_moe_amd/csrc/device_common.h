@@ -1,0 +1,64 @@
+// Device-side helpers shared by the gfx950 kernels of the FP8 MoE expert path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr float kE4m3Max = 448.0f;
+constexpr int kScaleBlock = 128;     // 1x128 activation / 128x128 weight scale granularity
+constexpr int kNumXcd = 8;           // MI355X: 8 accelerator dies, workgroups dealt round-robin
+
+// One 16x16x128 fp8 (e4m3) MFMA: c += a . b over 128 K.
+// Lane l holds A row (l % 16) and B column (l % 16), K bytes [32*(l/16), +32);
+// the result lane l holds rows 4*(l/16) + r (r = 0..3) of column l % 16.
+// The scaled form with both E8M0 scales at 127 (2^0) is the plain product.
+__device__ __forceinline__ v4f mfma16x16x128_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Saturating fp32 -> e4m3 of four values packed little-endian into a dword.
+// The hardware conversion rounds to nearest-even and keeps subnormals but turns
+// magnitudes >= 464 into NaN, so values are clamped to +-448 first.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
+  b = fminf(fmaxf(b, -kE4m3Max), kE4m3Max);
+  c = fminf(fmaxf(c, -kE4m3Max), kE4m3Max);
+  d = fminf(fmaxf(d, -kE4m3Max), kE4m3Max);
+  uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__device__ __forceinline__ uint32_t one_e4m3(float a) {
+  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, a, 0, false) & 0xffu;
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Largest e in [0, E) with padded[e] <= p (p < padded[E]): the expert owning padded row p.
+__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ padded, int E, int p) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (padded[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace fp8moe

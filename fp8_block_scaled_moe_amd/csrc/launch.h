@@ -1,0 +1,41 @@
+// Internal launcher interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8moe {
+
+constexpr int kMaxExperts = 1024;
+
+// Geometry of one grouped-GEMM launch over the padded row space.
+struct GroupedRows {
+  const int32_t* padded_indptr;  // [E+1]
+  const int32_t* sorted_src;     // [cap]
+  int64_t cap;                   // rows in the padded row space
+  int E, K;                      // experts, top-k (token = src / K)
+};
+
+size_t route_lds_bytes(int E);
+hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int cap,
+                                int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
+                                int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream);
+
+// GEMM1 + SwiGLU + 1x128 requant.  tile_m in {16, 32, 64, 128}.
+hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
+                        const float* w13_scale, const GroupedRows& g, int H, int I,
+                        uint8_t* q, float* q_scale, int tile_m, hipStream_t stream);
+
+// GEMM2 with the top-k weight epilogue, Y indexed by source row.  tile_m in {16, 32, 64, 128}.
+hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w2,
+                        const float* w2_scale, const float* topk_weights, const GroupedRows& g,
+                        int H, int I, uint16_t* Y, int tile_m, int tile_n, hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t* Y, const int32_t* topk_ids, int T, int H, int E, int K,
+                          uint16_t* out, hipStream_t stream);
+
+hipError_t launch_gated_act(const uint16_t* in, int64_t M, int N, uint8_t* out, uint8_t* scale,
+                            int variant, hipStream_t stream);
+
+}  // namespace fp8moe

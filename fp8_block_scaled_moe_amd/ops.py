@@ -1,0 +1,180 @@
+"""Thin torch-facing wrappers over the C ABI (argument marshalling only).
+
+Every computation happens in the HIP kernels of libfp8moe.so; these functions
+check dtypes/shapes/devices, allocate outputs with torch, pass raw pointers
+and the current HIP stream, and raise Fp8MoeError on a non-zero status.
+"""
+
+import ctypes
+
+import torch
+
+from ._lib import lib, check, Fp8MoeError  # noqa: F401
+
+ALIGNS = (16, 32, 64, 128)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _u8(t):
+    """fp8 e4m3 tensors may be passed as torch.float8_e4m3fn or as uint8 codes."""
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+# ---------------------------------------------------------------- routing
+
+def route_capacity(T, K, E, align):
+    v = lib().moe_route_capacity(T, K, E, align)
+    if v < 0:
+        check(int(v))
+    return int(v)
+
+
+def route_permute(topk_ids, E, align):
+    """Routing on the device.  Returns a dict of int32 device tensors."""
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    T, K = topk_ids.shape
+    cap = route_capacity(T, K, E, align)
+    dev = topk_ids.device
+    mk = lambda n: torch.empty(max(n, 0), dtype=torch.int32, device=dev)
+    r = {"counts": mk(E), "m_indptr": mk(E + 1), "padded_indptr": mk(E + 1),
+         "sorted_src": mk(cap), "src_to_sorted": mk(T * K)}
+    check(lib().moe_route_permute(_p(topk_ids), T, K, E, align, _p(r["counts"]), _p(r["m_indptr"]),
+                                  _p(r["padded_indptr"]), _p(r["sorted_src"]), _p(r["src_to_sorted"]),
+                                  _stream(dev)))
+    return r
+
+
+# ---------------------------------------------------------------- fused layer
+
+def fused_workspace_size(T, H, I, E, K):
+    n = ctypes.c_size_t(0)
+    check(lib().moe_fused_fp8_workspace_size(T, H, I, E, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace(T, H, I, E, K, device):
+    """A device workspace for moe_fused_fp8 (torch allocations are 256-byte aligned)."""
+    return torch.empty(fused_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
+
+
+def moe_fused_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
+                  out=None, workspace=None, tile_m=-1, tile_n=-1):
+    """Fused W8A8 FP8 block-scaled MoE layer.  Returns bf16 [T, H]."""
+    x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
+    _need(x, torch.uint8, "x", 2)
+    _need(x_scale, torch.float32, "x_scale", 2)
+    _need(w13, torch.uint8, "w13", 3)
+    _need(w13_scale, torch.float32, "w13_scale", 3)
+    _need(w2, torch.uint8, "w2", 3)
+    _need(w2_scale, torch.float32, "w2_scale", 3)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    K = topk_ids.shape[1]
+    if H2 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
+        raise ValueError("inconsistent x / w13 / w2 shapes")
+    if tuple(x_scale.shape) != (T, H // 128) or tuple(w13_scale.shape) != (E, 2 * I // 128, H // 128) \
+            or tuple(w2_scale.shape) != (E, H // 128, I // 128):
+        raise ValueError("inconsistent scale shapes")
+    if tuple(topk_ids.shape) != (T, K) or tuple(topk_weights.shape) != (T, K):
+        raise ValueError("topk_ids / topk_weights must be [T, K]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", 2)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, K, dev)
+    check(lib().moe_fused_fp8(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
+                              _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
+                              workspace.numel() * workspace.element_size(), tile_m, tile_n, _stream(dev)))
+    return out
+
+
+def gemm1_swiglu_quant(x, x_scale, w13, w13_scale, route, T, K, align, tile_m=-1):
+    """GEMM1 + SwiGLU + requant stage over a routing result.  Returns (q uint8 [cap, I], q_scale [cap, I/128])."""
+    x, w13 = _u8(x), _u8(w13)
+    E, I2, H = w13.shape
+    I = I2 // 2
+    cap = route["sorted_src"].numel()
+    dev = x.device
+    q = torch.zeros((cap, I), dtype=torch.uint8, device=dev)
+    qs = torch.zeros((cap, I // 128), dtype=torch.float32, device=dev)
+    check(lib().moe_gemm1_swiglu_quant(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(route["padded_indptr"]),
+                                       _p(route["sorted_src"]), T, H, I, E, K, align, _p(q), _p(qs), cap, tile_m,
+                                       _stream(dev)))
+    return q, qs
+
+
+def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1):
+    """GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H] (rows of dropped slots are zero here)."""
+    w2 = _u8(w2)
+    E, H, I = w2.shape
+    cap = route["sorted_src"].numel()
+    dev = q.device
+    Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev)
+    check(lib().moe_gemm2_weighted(_p(q), _p(q_scale), _p(w2), _p(w2_scale), _p(route["padded_indptr"]),
+                                   _p(route["sorted_src"]), _p(topk_weights), T, H, I, E, K, align, _p(Y), cap,
+                                   tile_m, tile_n, _stream(dev)))
+    return Y
+
+
+def combine(Y, topk_ids, E):
+    T, K = topk_ids.shape
+    H = Y.shape[1]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=Y.device)
+    check(lib().moe_combine(_p(Y), _p(topk_ids), T, H, E, K, _p(out), _stream(Y.device)))
+    return out
+
+
+# ---------------------------------------------------------------- gated activation
+
+def gated_act_fp8_quant(x, variant=-1, out=None, scale=None):
+    """bf16 [M, 2N] -> (fp8 codes uint8 [M, N], E8M0 uint8 [M, N/32])."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, N2 = x.shape
+    N = N2 // 2
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((M, max(N // 32, 0)), dtype=torch.uint8, device=dev)
+    check(lib().gated_act_fp8_quant(_p(x), M, N, _p(out), _p(scale), variant, _stream(dev)))
+    return out, scale
+
+
+# ---------------------------------------------------------------- cost model (host only)
+
+def select_tile(total_rows, n, k, E, num_cu=256, gated=False):
+    tm, tn = ctypes.c_int32(0), ctypes.c_int32(0)
+    check(lib().moe_select_tile(total_rows, n, k, E, num_cu, int(gated), ctypes.byref(tm), ctypes.byref(tn)))
+    return tm.value, tn.value
+
+
+def select_tile_classes(total_rows, n, k, E, num_cu, narrow, tile_n):
+    """tile_n: dict class -> width for the classes (narrow, 32, 64, 128)."""
+    tm = ctypes.c_int32(0)
+    check(lib().moe_select_tile_classes(total_rows, n, k, E, num_cu, narrow, tile_n[narrow], tile_n[32],
+                                        tile_n[64], tile_n[128], ctypes.byref(tm)))
+    return tm.value

@@ -1,0 +1,207 @@
+/*
+ * fp8moe.h -- C ABI of the MI355X (gfx950) W8A8 FP8 block-scaled MoE expert path.
+ *
+ * The path is the five-stage expert computation described on the "Blackwell
+ * W8A8 AlphaMoE expert-kernel fusion" page (flashinfer PR 4287 analysis),
+ * section "Problem: the MoE expert bottleneck": GEMM1 over gate+up, SwiGLU,
+ * intermediate FP8 requantisation, GEMM2 over down, combine.  Its operand
+ * conventions follow the grouped FP8 GEMM op of the "SM120 MoE GEMM
+ * wave+residue cost model" page (flashinfer PR 4318 analysis), section 1:
+ * K-contiguous ("NT") operands, an int32 m_indptr prefix over the routed rows,
+ * 1x128 activation scales and 128x128 weight scales, a gated GEMM whose weight
+ * holds the gate rows first and the up rows second, and -1 meaning "choose the
+ * tile automatically".  The standalone gated activation + MXFP8 quantiser is
+ * the kernel of the "SwiGLU + MXFP8 kernel for R200 (SM107)" page (flashinfer
+ * PR 8023 analysis), section 1.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers, allocated and owned by the caller.
+ *     Row-major, densely packed, no strides.  The library never allocates or
+ *     frees device memory and never synchronises the host.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     All work is enqueued on that stream in order.
+ *   - fp8 means OCP e4m3fn bytes (max 448, 0x7F/0xFF NaN).  bf16 is stored as
+ *     uint16 bit patterns.  fp32 scales multiply the decoded fp8 values.
+ *   - Return value: FP8MOE_OK (0) or a negative FP8MOE_ERR_* status.  Argument
+ *     validation happens before anything is enqueued, so an error return
+ *     means nothing was launched (except FP8MOE_ERR_HIP, which reports a failed
+ *     launch).  moe_last_error() gives a message for the last failure on the
+ *     calling thread.  No C++ exception crosses this interface.
+ *   - Entry points are thread-safe; calls on one stream are ordered; calls
+ *     that share a workspace must not overlap in time.
+ */
+#ifndef FP8MOE_H
+#define FP8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define FP8MOE_OK               0
+#define FP8MOE_ERR_NULL        -1  /* a required pointer is NULL                     */
+#define FP8MOE_ERR_SHAPE       -2  /* a size is negative, zero where it must not be,
+                                      or overflows the int32 row index space         */
+#define FP8MOE_ERR_ALIGN       -3  /* H or I not a multiple of 128; N not of 32;
+                                      align not in {16,32,64,128}                     */
+#define FP8MOE_ERR_TOPK        -4  /* top-k K outside [1, E]                          */
+#define FP8MOE_ERR_TILE        -5  /* tile_m / tile_n / variant not supported         */
+#define FP8MOE_ERR_WORKSPACE   -6  /* workspace NULL, too small or not 256-B aligned  */
+#define FP8MOE_ERR_HIP         -7  /* a HIP runtime call or kernel launch failed      */
+#define FP8MOE_ERR_LIMIT       -8  /* beyond a library limit (E > FP8MOE_MAX_EXPERTS) */
+
+#define FP8MOE_MAX_EXPERTS   1024
+
+/* Text for a status code (static storage). */
+const char* moe_status_string(int status);
+/* Message of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ---------------------------------------------------------------- routing
+ * Routing / permutation of the T*K (token, slot) rows by expert.  Row
+ * src = t*K + j is slot j of token t.  A slot whose id is outside [0, E) is
+ * dropped.  Within an expert, rows keep ascending src order (deterministic,
+ * stable).  Each expert's segment is padded to a multiple of `align` (the
+ * "aligned" MoE of the AlphaMoE page; m_indptr as on the SM120 page, section 1).
+ *
+ * moe_route_capacity: rows the padded map can need, T*K + E*(align-1);
+ *   negative status on invalid arguments (host only, no GPU needed).
+ *
+ * moe_route_permute outputs (device, int32, all fully written):
+ *   counts        [E]        rows per expert
+ *   m_indptr      [E+1]      exclusive prefix of counts
+ *   padded_indptr [E+1]      exclusive prefix of counts rounded up to align
+ *   sorted_src    [cap]      src of each padded row position, -1 for padding
+ *                            and for every position past padded_indptr[E]
+ *   src_to_sorted [T*K]      position of row src in sorted_src, -1 if dropped
+ * Inputs: topk_ids [T, K] int32.  T == 0 writes counts/indptrs as zeros and
+ * sorted_src as -1.  Limits: 1 <= E <= FP8MOE_MAX_EXPERTS, 1 <= K <= E,
+ * align in {16, 32, 64, 128}, T*K + E*(align-1) < 2^31.
+ */
+int64_t moe_route_capacity(int64_t T, int32_t K, int32_t E, int32_t align);
+int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t align,
+                      int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
+                      int32_t* sorted_src, int32_t* src_to_sorted, void* stream);
+
+/* ---------------------------------------------------------------- fused MoE layer
+ * out[t, :] = bf16( sum over valid slots j of topk_weights[t, j] * FFN_{topk_ids[t, j]}(x[t]) )
+ * with FFN_e(x) = W2_e . requant( silu(W13_e[:I] . x) * (W13_e[I:] . x) ), where every
+ * product is of dequantised fp8 operands accumulated in fp32, the per-block
+ * scales are applied to the fp32 accumulators once per 128-wide K step, and
+ * requant is the intermediate 1x128 FP8 requantisation (s = amax/448 per row
+ * and 128 columns of I, q = e4m3(act / s)).  Stages as on the AlphaMoE page,
+ * section "Problem"; operand layouts as on the SM120 page, section 1.
+ *
+ *   x        fp8  [T, H]              activations
+ *   x_scale  fp32 [T, H/128]          1x128 activation scales
+ *   w13      fp8  [E, 2I, H]          rows 0..I-1 gate, rows I..2I-1 up
+ *   w13_scale fp32 [E, 2I/128, H/128] 128x128 block scales
+ *   w2       fp8  [E, H, I]
+ *   w2_scale fp32 [E, H/128, I/128]
+ *   topk_ids int32 [T, K]             ids outside [0, E) are dropped slots
+ *   topk_weights fp32 [T, K]
+ *   out      bf16 [T, H]              overwritten (never accumulated into);
+ *                                     a token with no valid slot gets zeros
+ *   workspace / workspace_bytes       device scratch of at least
+ *                                     moe_fused_fp8_workspace_size() bytes,
+ *                                     256-byte aligned, owned by the caller
+ *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128: token rows
+ *            per GEMM tile (16 is the swap-AB class: tokens on the 16-wide
+ *            MFMA side); applies to both GEMMs when given
+ *   tile_n   -1 (auto) or 256: GEMM2 output columns per tile (GEMM1 always
+ *            covers 128 columns of I, one requantisation block, per tile)
+ * Requires H % 128 == 0, I % 128 == 0, 1 <= K <= E <= FP8MOE_MAX_EXPERTS.
+ * T == 0 returns FP8MOE_OK and launches nothing.  Deterministic: no atomics
+ * decide any value; two calls give bit-identical outputs.
+ */
+int moe_fused_fp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                 size_t* bytes);
+int moe_fused_fp8(const void* x, const float* x_scale,
+                  const void* w13, const float* w13_scale,
+                  const void* w2, const float* w2_scale,
+                  const int32_t* topk_ids, const float* topk_weights,
+                  int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                  void* out, void* workspace, size_t workspace_bytes,
+                  int32_t tile_m, int32_t tile_n, void* stream);
+
+/* ---------------------------------------------------------------- stages of the fused layer
+ * The three compute stages moe_fused_fp8 runs after routing, exposed so each
+ * can be checked on its own.  They consume moe_route_permute's outputs (with
+ * `align` a multiple of the tile_m used).
+ *
+ * moe_gemm1_swiglu_quant: for every padded row p < padded_indptr[E] of
+ *   expert e (padded_indptr[e] <= p < padded_indptr[e+1]) with source row
+ *   src = sorted_src[p] (token src / K; a pad row reads zeros):
+ *     h = x[token] . w13[e]^T (fp32, scales folded per 128-K step),
+ *     act = silu(h[:I]) * h[I:],
+ *     q_scale[p, b] = amax(act[b*128:(b+1)*128]) / 448 (1 if zero),
+ *     q[p, c] = e4m3(act[c] / q_scale[p, c/128]).
+ *   q fp8 [cap, I], q_scale fp32 [cap, I/128].  Rows of tiles that hold
+ *   only padding, and rows >= padded_indptr[E], are not written.
+ * moe_gemm2_weighted: for every row p with src = sorted_src[p] >= 0:
+ *     Y[src, :] = bf16( topk_weights[src] * (deq(q[p]) . w2[e]^T) ).
+ *   Y bf16 [T*K, H]; rows of dropped slots are not written.
+ *   `align` is the one the routing was built with; tile_m (-1 auto, else
+ *   16/32/64/128) must divide it (auto picks the largest allowed size not
+ *   above the cost model's choice).  cap is the length of sorted_src.
+ * moe_combine: out[t, :] = bf16( sum over j with 0 <= topk_ids[t, j] < E of
+ *   Y[t*K + j, :] ) summed in fp32 in ascending j; zeros for tokens with no
+ *   valid slot.
+ */
+int moe_gemm1_swiglu_quant(const void* x, const float* x_scale,
+                           const void* w13, const float* w13_scale,
+                           const int32_t* padded_indptr, const int32_t* sorted_src,
+                           int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                           void* q, float* q_scale, int64_t cap,
+                           int32_t tile_m, void* stream);
+int moe_gemm2_weighted(const void* q, const float* q_scale,
+                       const void* w2, const float* w2_scale,
+                       const int32_t* padded_indptr, const int32_t* sorted_src,
+                       const float* topk_weights,
+                       int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                       void* Y, int64_t cap, int32_t tile_m, int32_t tile_n, void* stream);
+int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E,
+                int32_t K, void* out, void* stream);
+
+/* ---------------------------------------------------------------- gated activation + MXFP8
+ * SwiGLU + MXFP8 quantisation (PR 8023 page, title and section 1):
+ *   in   bf16 [M, 2N]   gate = in[:, :N], up = in[:, N:]
+ *   act = silu(gate) * up in fp32
+ *   per row and 32-column block: e = smallest integer with amax <= 448 * 2^e,
+ *   clamped to [-127, 127] (amax == 0 gives -127); scale_e8m0 = e + 127
+ *   out  fp8 [M, N]     e4m3(act * 2^-e) (never saturates by construction)
+ *   scale_e8m0 uint8 [M, N/32], row-major, unswizzled
+ * variant: -1 auto (small below 2^20 output elements, large at or above, the
+ * page's size routing), 0 small (one 8-element group per thread, many
+ * workgroups per CU), 1 large (grid-stride streaming).
+ * Requires N % 32 == 0, M >= 0; M == 0 launches nothing.
+ */
+int gated_act_fp8_quant(const void* in, int64_t M, int32_t N, void* out, uint8_t* scale_e8m0,
+                        int32_t variant, void* stream);
+
+/* ---------------------------------------------------------------- tile cost model (host only)
+ * The tile_m ladder of the SM120 page, section 2 (wave+residue choice between
+ * 64 and 128, TileN per class from its review notes), for one grouped GEMM
+ * with `total_rows` routed rows, logical output width n (I for the gated
+ * GEMM1, H for GEMM2), depth k, E experts and num_cu compute units (256 on
+ * MI355X).  gated != 0 selects GEMM1's tiles.  Writes tile_m in {16,32,64,128}
+ * and tile_n (columns of the logical output per tile).  Pure host code.
+ */
+int moe_select_tile(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t num_cu,
+                    int32_t gated, int32_t* tile_m, int32_t* tile_n);
+/* The same ladder with the tile classes given explicitly: the narrow
+ * (swap-AB) class height and the tile width of each class (narrow, 32, 64,
+ * 128).  Lets the ladder be checked against the outcomes the SM120 page
+ * states for its own hardware (narrow 8; TileN 128/128/128/64). */
+int moe_select_tile_classes(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t num_cu,
+                            int32_t narrow, int32_t tile_n_narrow, int32_t tile_n_32,
+                            int32_t tile_n_64, int32_t tile_n_128, int32_t* tile_m);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MOE_H */

@@ -180,11 +180,22 @@ def quantize_blocks(w, block=128):
     return q, s
 
 
+_DECODE_TABLE = None
+
+
+def e4m3_decode_table(codes):
+    """e4m3_decode through a 256-entry table of its own values (same results, faster)."""
+    global _DECODE_TABLE
+    if _DECODE_TABLE is None:
+        _DECODE_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
+    return _DECODE_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 def dequant_rows(q, s, block=128):
     """float64 values of row-block-quantised codes: decode(q) * s (exact in float64)."""
     q = np.asarray(q)
     R, C = q.shape
-    v = e4m3_decode(q).reshape(R, C // block, block)
+    v = e4m3_decode_table(q).reshape(R, C // block, block)
     return (v * np.asarray(s, dtype=np.float64)[:, :, None]).reshape(R, C)
 
 
@@ -192,5 +203,5 @@ def dequant_blocks(q, s, block=128):
     """float64 values of block-quantised codes [N, K] with scales [N/b, K/b]."""
     q = np.asarray(q)
     N, K = q.shape
-    v = e4m3_decode(q).reshape(N // block, block, K // block, block)
+    v = e4m3_decode_table(q).reshape(N // block, block, K // block, block)
     return (v * np.asarray(s, dtype=np.float64)[:, None, :, None]).reshape(N, K)

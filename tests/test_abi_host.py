@@ -1,0 +1,170 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+function include/fp8moe.h declares, rejects invalid arguments before any launch,
+and its tile cost model matches the oracle's ladder bit for bit."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp8_block_scaled_moe_amd as fm
+from fp8_block_scaled_moe_amd._lib import lib
+from oracle import tile_select as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8moe.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_TOPK, E_TILE, E_WS, E_HIP, E_LIMIT = 0, -1, -2, -3, -4, -5, -6, -7, -8
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 12, names
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in fp8moe.h but not exported"
+
+
+def test_status_strings():
+    L = lib()
+    for s in (OK, E_NULL, E_SHAPE, E_ALIGN, E_TOPK, E_TILE, E_WS, E_HIP, E_LIMIT):
+        assert L.moe_status_string(s).decode()
+    assert L.moe_status_string(-99).decode() == "unknown status"
+
+
+def test_route_capacity():
+    assert fm.route_capacity(64, 8, 256, 16) == 64 * 8 + 256 * 15
+    assert fm.route_capacity(0, 8, 128, 128) == 128 * 127
+    assert lib().moe_route_capacity(4, 2, 4, 24) == E_ALIGN
+    assert lib().moe_route_capacity(-1, 2, 4, 16) == E_SHAPE
+
+
+def test_route_permute_validation():
+    f = lib().moe_route_permute
+    args = lambda T, K, E, a: f(FAKE, T, K, E, a, FAKE, FAKE, FAKE, FAKE, FAKE, NULL)
+    assert args(-1, 2, 4, 16) == E_SHAPE
+    assert args(4, 0, 4, 16) == E_TOPK
+    assert args(4, 5, 4, 16) == E_TOPK
+    assert args(4, 2, 0, 16) == E_SHAPE
+    assert args(4, 2, 2000, 16) == E_LIMIT
+    assert args(4, 2, 4, 48) == E_ALIGN
+    assert args(2 ** 28, 8, 8, 16) == E_SHAPE
+    assert f(NULL, 4, 2, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == E_NULL
+    assert f(FAKE, 4, 2, 4, 16, NULL, FAKE, FAKE, FAKE, FAKE, NULL) == E_NULL
+    assert "top-k" in lib().moe_last_error().decode() or lib().moe_last_error().decode()
+
+
+def _fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE):
+    return lib().moe_fused_fp8(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn, NULL)
+
+
+def test_fused_validation():
+    assert _fused(T=-1) == E_SHAPE
+    assert _fused(H=200) == E_ALIGN
+    assert _fused(I=100) == E_ALIGN
+    assert _fused(H=0) == E_SHAPE
+    assert _fused(K=5) == E_TOPK
+    assert _fused(K=0) == E_TOPK
+    assert _fused(E=0) == E_SHAPE
+    assert _fused(E=1025, K=2) == E_LIMIT
+    assert _fused(tm=48) == E_TILE
+    assert _fused(tn=128) == E_TILE
+    assert _fused(ptr=NULL) == E_NULL
+    assert _fused(out=NULL) == E_NULL
+    assert _fused(ws=NULL) == E_WS
+    assert _fused(ws=ctypes.c_void_p(0x1010)) == E_WS            # misaligned
+    assert _fused(wsb=1024) == E_WS                                # too small
+    assert "workspace" in lib().moe_last_error().decode()
+    # T == 0: nothing to do, no launch, null pointers allowed
+    assert _fused(T=0, ptr=NULL, ws=NULL, out=NULL) == OK
+    assert lib().moe_last_error().decode() == ""
+
+
+def test_workspace_size():
+    n = fm.fused_workspace_size(16, 256, 128, 4, 2)
+    R, cap = 32, 32 + 4 * 127
+    assert n >= cap * 128 + cap * 4 + R * 256 * 2 + cap * 4
+    big = fm.fused_workspace_size(8192, 7168, 2048, 256, 8)
+    assert big < 2 ** 31
+    with pytest.raises(fm.Fp8MoeError):
+        fm.fused_workspace_size(16, 100, 128, 4, 2)
+
+
+def test_stage_validation():
+    L = lib()
+    g1 = lambda **k: L.moe_gemm1_swiglu_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("T", 16), 256, 128, 4, 2,
+                                              k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1), NULL)
+    assert g1(align=24) == E_ALIGN
+    assert g1(align=16, tm=32) == E_TILE          # tile must divide align
+    assert g1(cap=-1) == E_SHAPE
+    assert g1(T=0) == OK
+    g2 = lambda **k: L.moe_gemm2_weighted(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 256, 128, 4, 2,
+                                          k.get("align", 16), FAKE, 100, k.get("tm", -1), k.get("tn", -1), NULL)
+    assert g2(tn=64) == E_TILE
+    assert g2(align=32, tm=64) == E_TILE
+    assert L.moe_combine(FAKE, FAKE, 4, 100, 4, 2, FAKE, NULL) == E_ALIGN
+    assert L.moe_combine(FAKE, FAKE, 4, 128, 4, 9, FAKE, NULL) == E_TOPK
+    assert L.moe_combine(NULL, FAKE, 4, 128, 4, 2, FAKE, NULL) == E_NULL
+    assert L.moe_combine(NULL, NULL, 0, 128, 4, 2, NULL, NULL) == OK
+
+
+def test_gated_act_validation():
+    f = lib().gated_act_fp8_quant
+    assert f(FAKE, 4, 48, FAKE, FAKE, -1, NULL) == E_ALIGN
+    assert f(FAKE, -1, 64, FAKE, FAKE, -1, NULL) == E_SHAPE
+    assert f(FAKE, 4, 0, FAKE, FAKE, -1, NULL) == E_SHAPE
+    assert f(FAKE, 4, 64, FAKE, FAKE, 2, NULL) == E_TILE
+    assert f(NULL, 4, 64, FAKE, FAKE, -1, NULL) == E_NULL
+    assert f(NULL, 0, 64, NULL, NULL, -1, NULL) == OK
+
+
+# ---------------------------------------------------------------- cost model vs oracle
+
+MI_GATED = {16: 128, 32: 128, 64: 128, 128: 128}
+MI_PLAIN = {16: 256, 32: 256, 64: 256, 128: 256}
+
+
+def test_select_tile_matches_oracle_sweep():
+    rng = np.random.default_rng(0)
+    for _ in range(3000):
+        E = int(rng.choice([1, 4, 8, 32, 64, 128, 256, 512]))
+        R = int(rng.integers(0, 8 * 8192 + 1)) if rng.random() < 0.7 else int(rng.integers(0, 64))
+        n = int(rng.choice([128, 256, 768, 2048, 7168, 4096, 640]))
+        k = int(rng.choice([256, 768, 2048, 2176, 7168]))
+        cu = int(rng.choice([1, 84, 188, 256, 304]))
+        for gated, cls in ((1, MI_GATED), (0, MI_PLAIN)):
+            tm, tn = fm.select_tile(R, n, k, E, cu, bool(gated))
+            assert tm == S.select_tile_m(R, n, k, E, cu, 16, cls), (R, n, k, E, cu, gated)
+            assert tn == cls[128]
+        page = {8: 128, 32: 128, 64: 128, 128: 64}
+        assert fm.select_tile_classes(R, n, k, E, cu, 8, page) == S.select_tile_m(R, n, k, E, cu, 8, page)
+
+
+def test_select_tile_page_golden_through_abi():
+    from tests.test_oracle_tile_select import load_cases, PAGE_TILE_N
+    for name, m, E, n, k, cu, exp, src in load_cases():
+        assert fm.select_tile_classes(m * E, n, k, E, cu, 8, PAGE_TILE_N) == exp, (name, src)
+
+
+@pytest.mark.parametrize("R,n,k,E,gated,expect", [
+    (64 * 8, 2048, 7168, 256, True, 16),        # decode, GEMM1 -> swap-AB class
+    (64 * 8, 7168, 2048, 256, False, 16),       # decode, GEMM2
+    (8192 * 8, 2048, 7168, 256, True, 128),     # prefill, GEMM1
+    (8192 * 8, 7168, 2048, 256, False, 128),    # prefill, GEMM2
+    (1 * 8, 768, 2048, 128, True, 16),          # skewed T=1
+    (33 * 8, 768, 2048, 128, True, 16),         # skewed T=33
+    (512 * 8, 768, 2048, 128, True, 32),        # skewed T=512
+    (4096 * 8, 768, 2048, 128, True, 128),      # skewed T=4096
+])
+def test_select_tile_at_the_workloads(R, n, k, E, gated, expect):
+    assert fm.select_tile(R, n, k, E, 256, gated)[0] == expect

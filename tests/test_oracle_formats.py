@@ -221,3 +221,9 @@ def test_dequant_is_exact_product():
     assert d[0, 0] == 0.375 and d[0, 1] == 448 * 0.375 and d[0, 2] == 2.0 ** -9 * 0.375
     assert d[0, 3] == -1.125 * 0.375
     assert math.isclose(d.sum(), 32 * 0.375 * (1 + 448 + 2.0 ** -9 - 1.125), rel_tol=0, abs_tol=1e-12)
+
+
+def test_decode_table_equals_decode():
+    a = F.e4m3_decode(ALL_CODES)
+    b = F.e4m3_decode_table(ALL_CODES)
+    assert np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])

@@ -173,56 +173,11 @@ def test_subset_of_tokens_matches_full_run():
 
 # ---------------------------------------------------------------- crafted all-exact case
 
-def _code(v):
-    return int(F.e4m3_encode_sat(np.float32(v)))
-
-
 def test_crafted_exact_case_bit_identical():
-    """Every stage is exact: gate in {0} U [18, 64] (sigmoid rounds to 1),
-    act values fp8-representable with each 128-block max = 448 * 2^j, power-
-    of-two routing weights; the output is derived by hand below."""
-    T, H, I, E, K = 3, 128, 128, 2, 2
-    # x = 2^t on every element (code 1.0, scale 2^t)
-    x_q = np.full((T, H), _code(1.0), np.uint8)
-    x_s = np.array([[2.0 ** t] for t in range(T)], np.float32)
-    # expert e: gate row c = G[e][c] at column 0, up row c = U[e][c] at column 0 (scale 1/H)
-    G = [np.zeros(I), np.zeros(I)]
-    U = [np.zeros(I), np.zeros(I)]
-    G[0][:4] = [56, 24, 18, 0];  U[0][:4] = [8, 2, -1, 5]        # acts 448, 48, -18, 0
-    G[1][:3] = [32, 20, 64];     U[1][:3] = [0.25, -0.5, 7]      # acts 8, -10, 448
-    w13_q = np.zeros((E, 2 * I, H), np.uint8)
-    for e in range(E):
-        for c in range(I):
-            w13_q[e, c, :] = _code(G[e][c] / H)
-            w13_q[e, I + c, :] = _code(U[e][c] / H)
-    # G/H and U/H are fp8-representable (powers of two times small mantissas)
-    for e in range(E):
-        assert np.all(F.e4m3_decode(w13_q[e, :I, 0]) * H == G[e])
-        assert np.all(F.e4m3_decode(w13_q[e, I:, 0]) * H == U[e])
-    w13_s = np.ones((E, 2, 1), np.float32)
-    # w2 row n picks act column n % 4 with weight 1 (expert 0) or 2 (expert 1)
-    w2_q = np.zeros((E, H, I), np.uint8)
-    for n in range(H):
-        w2_q[0, n, n % 4] = _code(1.0)
-        w2_q[1, n, n % 3] = _code(2.0)
-    w2_s = np.ones((E, 1, 1), np.float32)
-    ids = np.array([[0, 1], [1, 0], [0, 0]], np.int32)
-    wts = np.array([[0.75, 0.25], [0.5, 0.5], [0.5, 0.25]], np.float32)
-    bits, out = M.moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, ids, wts)
-    # hand derivation: h = 2^t * (G, U) (x row sums to H*2^t, weight rows are G/H);
-    # act = 4^t * G*U; block amax = 448 * 4^t -> s = 4^t, q = G*U exactly;
-    # Y0[n] = act0[n % 4], Y1[n] = 2 * act1[n % 3]
-    act0 = np.array([448, 48, -18, 0], float)
-    act1 = np.array([8, -10, 448], float)
-    expect = np.zeros((T, H))
-    for t in range(T):
-        for j in range(K):
-            for n in range(H):
-                y = 4.0 ** t * (act0[n % 4] if ids[t, j] == 0 else 2 * act1[n % 3])
-                expect[t, n] += float(wts[t, j]) * y
-    # the exact float64 sum is rounded once to bfloat16 (torch's cast)
-    expect_bf16 = torch.from_numpy(expect.astype(np.float32)).to(torch.bfloat16).float().numpy()
-    assert np.all(expect.astype(np.float32) == expect)          # exact before the bf16 rounding
+    """Every stage is exact (see tests/cases.py); the output is derived by hand."""
+    from tests.cases import crafted_exact_case
+    args, expect_bf16 = crafted_exact_case()
+    bits, out = M.moe_reference(*args)
     assert np.array_equal(out, expect_bf16)
 
 
