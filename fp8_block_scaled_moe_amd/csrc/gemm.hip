@@ -35,24 +35,23 @@
 
 namespace fp8moe {
 
-constexpr int kThreads = 256;  // 4 wave64s
 constexpr int kTN = 256;       // weight rows per tile
 constexpr int kKB = 128;       // K per step (= scale block)
 
+// Workgroup shape per tile_m: 8 wave64s (2 x 4, wave tile 64 x 64) for 128
+// rows, 4 wave64s otherwise (2 x 2 for 64 rows, 1 x 4 for 16 and 32 rows).
 template <int TM>
 struct TileCfg {
+  static constexpr int WAVES = TM == 128 ? 8 : 4;
+  static constexpr int THREADS = WAVES * 64;
   static constexpr int WM = TM >= 64 ? 2 : 1;
-  static constexpr int WN = 4 / WM;
+  static constexpr int WN = WAVES / WM;
   static constexpr int WTM = TM / WM;      // rows per wave
   static constexpr int WTN = kTN / WN;     // weight rows per wave
   static constexpr int MI = WTM / 16;      // 16-row sub-tiles per wave
   static constexpr int NJ = WTN / 16;      // 16-col sub-tiles per wave
   static constexpr int A_BYTES = TM * kKB;
   static constexpr int B_BYTES = kTN * kKB;
-  static constexpr int A_CHUNKS = TM * 8;          // 16-byte chunks per stage
-  static constexpr int B_CHUNKS = kTN * 8;
-  static constexpr int A_ITERS = (A_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int B_ITERS = B_CHUNKS / kThreads;
 };
 
 // byte offset of 16-byte chunk c of row r in a swizzled [rows][128] LDS tile
@@ -93,104 +92,213 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded, c
 }
 
 // ------------------------------------------------------------------------------------------
-// Main loop shared by both GEMMs.  Computes acc[i][j] for the wave's MI x NJ sub-tiles.
-//   a_row[i]/a_ok: per-thread source pointers of the A chunks this thread loads
-//   b_row[i]: per-thread weight-row pointers of the B chunks (nullptr = beyond N)
-//   sa_src: per-thread pointer to the A scale of row tid (nullptr when tid >= TM or pad),
-//           advanced by one float per K step
-//   sb_g/sb_u: per-wave weight-scale pointers (gate/up, or the single block), advanced per step
-template <int TM, bool GATED>
-struct Mainloop {
+// Asynchronous global -> LDS ring.
+//
+// Each stage holds one 128-wide K step: A [TM][128], B [256][128] (both
+// swizzled) and the TM A-row scales.  Stages are filled with
+// global_load_lds_dwordx4: one wave instruction writes 1 KB of LDS, lane i at
+// byte 16*i, i.e. 8 rows x 8 chunks; the lane fetches from global memory the
+// logical chunk that the swizzle places at its slot.  Every wave issues the
+// same number of loads per stage (LW), so "stage kb has landed" is a single
+// immediate vmcnt: the loads of the stages issued after it may stay in flight.
+// A barrier then publishes the stage to all waves and frees the buffer that
+// was consumed in the previous step, which is refilled NS-1 steps ahead.
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) through the builtin, so the compiler's own
+// wait tracking knows which LDS DMA has landed (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 left at 7, lgkmcnt 11:8 = 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every LDS DMA in flight.  The empty asm statements keep
+// the compiler from moving memory accesses across it, the scheduling barriers
+// keep a step's register-only work (MFMAs) from sliding into the next step,
+// which would keep two steps' operand fragments live at once.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs on its side of the barrier
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const float* g, float* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+template <int TM>
+struct Ring {
   using C = TileCfg<TM>;
-  uint8_t* lds;  // 2 stages of [A | B | sa]
+  static constexpr int NS = TM >= 64 ? 3 : 2;                 // LDS stages
+  static constexpr int SA_BYTES = (TM * 4 + 15) / 16 * 16;
+  static constexpr int STAGE = C::A_BYTES + C::B_BYTES + SA_BYTES;
+  static constexpr int A_TOTAL = TM / 8;                      // 1-KB A loads per stage
+  static constexpr int A_PER_WAVE = A_TOTAL >= C::WAVES ? A_TOTAL / C::WAVES : 1;
+  static constexpr int B_PER_WAVE = kTN / 8 / C::WAVES;
+  static constexpr int SA_ROWS = TM / C::WAVES;               // scale rows per wave
+  static constexpr int LW = A_PER_WAVE + B_PER_WAVE + 1;      // loads per wave per stage
+  static_assert(LW * (NS - 2) <= 63, "vmcnt range");
+};
 
-  static constexpr int STAGE = C::A_BYTES + C::B_BYTES + TM * 4;
+// Per-thread load plan: byte offsets (from a wave-uniform base) of the chunks
+// this lane fetches for k-step 0; k-step kb adds kb*128 (kb for scales).
+template <int TM>
+struct LoadPlan {
+  using R = Ring<TM>;
+  uint32_t a_off[R::A_PER_WAVE];
+  uint32_t b_off[R::B_PER_WAVE];
+  uint32_t sa_off;     // in floats
+};
 
-  __device__ __forceinline__ void run(v4f (&acc)[C::MI][C::NJ], const uint8_t* const (&a_src)[C::A_ITERS],
-                                      const uint8_t* const (&b_src)[C::B_ITERS], const float* sa_src,
-                                      const float* sb_g, const float* sb_u, int KT, int tid, int lane,
-                                      int wm, int wn) {
-    v4i ra[C::A_ITERS];
-    v4i rb[C::B_ITERS];
-    float rsa = 0.f;
+template <int TM>
+__device__ __forceinline__ void issue_stage(uint8_t* stage, const LoadPlan<TM>& lp, const uint8_t* a_base,
+                                            const uint8_t* b_base, const float* sa_base, int kb, int wave,
+                                            int lane) {
+  using R = Ring<TM>;
+  using C = TileCfg<TM>;
+  // address = wave-uniform base + 32-bit lane offset (the K step folded into
+  // the offset), so each load is one VGPR offset on an SGPR base
+  const uint32_t kofs = (uint32_t)kb * kKB;
+#pragma unroll
+  for (int j = 0; j < R::A_PER_WAVE; ++j) {
+    const int ai = (wave * R::A_PER_WAVE + j) % R::A_TOTAL;
+    dma16(a_base + (lp.a_off[j] + kofs), stage + ai * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < R::B_PER_WAVE; ++j) {
+    const int bi = wave * R::B_PER_WAVE + j;
+    dma16(b_base + (lp.b_off[j] + kofs), stage + C::A_BYTES + bi * 1024);
+  }
+  float* sa = reinterpret_cast<float*>(stage + C::A_BYTES + C::B_BYTES);
+  if (lane < R::SA_ROWS) dma4(sa_base + (lp.sa_off + (uint32_t)kb), sa + wave * R::SA_ROWS);
+}
 
-    auto gload = [&](int kb) {
+// One K step: refill `nxt` (when asked) and multiply out of `cur`.  The two
+// stage pointers are distinct __restrict__ parameters of an inlined function,
+// so the LDS reads of `cur` carry alias-scope metadata saying they do not
+// touch the stage being refilled; without it the compiler would wait for every
+// outstanding LDS DMA (vmcnt(0)) before the first read and serialise the ring.
+// The real ordering is enforced by wait_stage + block_barrier in the caller.
+template <int TM, bool GATED>
+__device__ __forceinline__ void ring_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int kb_refill, v4f (&acc)[TileCfg<TM>::MI][TileCfg<TM>::NJ],
+                                          const LoadPlan<TM>& lp, const uint8_t* a_base, const uint8_t* b_base,
+                                          const float* sa_base, float sbg, float sbu, int wave, int lane, int wm,
+                                          int wn) {
+  using C = TileCfg<TM>;
+  issue_stage<TM>(nxt, lp, a_base, b_base, sa_base, kb_refill, wave, lane);
+  const uint8_t* A = cur;
+  const uint8_t* B = cur + C::A_BYTES;
+  const float* SA = reinterpret_cast<const float*>(B + C::B_BYTES);
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v8i af[C::MI];
+  v4f sv[C::MI];
 #pragma unroll
-      for (int i = 0; i < C::A_ITERS; ++i) {
-        if (a_src[i]) ra[i] = *reinterpret_cast<const v4i*>(a_src[i] + (size_t)kb * kKB);
-        else ra[i] = v4i{0, 0, 0, 0};
-      }
+  for (int i = 0; i < C::MI; ++i) {
+    af[i] = lds_frag(A, wm * C::WTM + 16 * i, lane);
+    sv[i] = *reinterpret_cast<const v4f*>(SA + wm * C::WTM + 16 * i + 4 * (lane >> 4));
+  }
+  // gate sub-tiles (j < NJ/2) use the gate block scale, up sub-tiles the up one
 #pragma unroll
-      for (int i = 0; i < C::B_ITERS; ++i) {
-        if (b_src[i]) rb[i] = *reinterpret_cast<const v4i*>(b_src[i] + (size_t)kb * kKB);
-        else rb[i] = v4i{0, 0, 0, 0};
-      }
-      rsa = sa_src ? sa_src[kb] : 0.f;
-    };
-    auto sstore = [&](int buf) {
-      uint8_t* A = lds + buf * STAGE;
-      uint8_t* B = A + C::A_BYTES;
-      float* SA = reinterpret_cast<float*>(B + C::B_BYTES);
+  for (int h = 0; h < (GATED ? 2 : 1); ++h) {
+    const float sb = h ? sbu : sbg;
+    v4f c[C::MI];
 #pragma unroll
-      for (int i = 0; i < C::A_ITERS; ++i) {
-        const int cid = tid + i * kThreads;
-        if (cid < C::A_CHUNKS) *reinterpret_cast<v4i*>(A + swz(cid >> 3, cid & 7)) = ra[i];
-      }
+    for (int i = 0; i < C::MI; ++i) c[i] = sv[i] * sb;
+    constexpr int JN = GATED ? C::NJ / 2 : C::NJ;
 #pragma unroll
-      for (int i = 0; i < C::B_ITERS; ++i) {
-        const int cid = tid + i * kThreads;
-        *reinterpret_cast<v4i*>(B + swz(cid >> 3, cid & 7)) = rb[i];
-      }
-      if (tid < TM) SA[tid] = rsa;
-    };
-
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kb = 0; kb < KT; ++kb) {
-      const int buf = kb & 1;
-      if (kb + 1 < KT) gload(kb + 1);
-      const uint8_t* A = lds + buf * STAGE;
-      const uint8_t* B = A + C::A_BYTES;
-      const float* SA = reinterpret_cast<const float*>(B + C::B_BYTES);
-      const float sbg = sb_g[kb];
-      const float sbu = GATED ? sb_u[kb] : sbg;
-      v8i af[C::MI];
-      v4f cg[C::MI], cu[C::MI];
+    for (int jj = 0; jj < JN; ++jj) {
+      const int j = h * JN + jj;
+      const v8i bf = lds_frag(B, wn * C::WTN + 16 * j, lane);
 #pragma unroll
       for (int i = 0; i < C::MI; ++i) {
-        af[i] = lds_frag(A, wm * C::WTM + 16 * i, lane);
-        const v4f s = *reinterpret_cast<const v4f*>(SA + wm * C::WTM + 16 * i + 4 * (lane >> 4));
-        cg[i] = s * sbg;
-        cu[i] = s * sbu;
+        const v4f pr = mfma16x16x128_fp8(af[i], bf, zero);
+        acc[i][j] += pr * c[i];
       }
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        const v8i bf = lds_frag(B, wn * C::WTN + 16 * j, lane);
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i) {
-          const v4f p = mfma16x16x128_fp8(af[i], bf, zero);
-          const v4f c = (GATED && j >= C::NJ / 2) ? cu[i] : cg[i];
-          acc[i][j] += p * c;
-        }
-      }
-      if (kb + 1 < KT) sstore(buf ^ 1);
-      __syncthreads();
     }
   }
-};
+  // MFMAs and folds are pure register work: without this the compiler sinks
+  // them past later barriers and keeps several steps' fragments live at once.
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
+}
+
+// Main loop shared by both GEMMs: acc[i][j] for the wave's MI x NJ sub-tiles.
+// st0..st2 are distinct __shared__ arrays (st2 unused when NS == 2); the loop is
+// unrolled by NS so every step reads and refills statically known stages and
+// the compiler can tell the in-flight DMA never targets the stage being read.
+// Every step refills (past the last K step it re-reads the last one, which
+// is never consumed), so each step issues the same LW loads per wave and one
+// constant wait -- all but the newest NS-2 stages landed -- is always right.
+// sb_g/sb_u: the wave's weight-scale rows (gate/up, or the single block), one float per K step.
+template <int TM, bool GATED>
+__device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st2,
+                                         v4f (&acc)[TileCfg<TM>::MI][TileCfg<TM>::NJ], const LoadPlan<TM>& lp,
+                                         const uint8_t* a_base, const uint8_t* b_base, const float* sa_base,
+                                         const float* sb_g, const float* sb_u, int KT, int wave, int lane, int wm,
+                                         int wn) {
+  using R = Ring<TM>;
+  constexpr int NS = R::NS;
+  issue_stage<TM>(st0, lp, a_base, b_base, sa_base, 0, wave, lane);
+  if constexpr (NS == 3) issue_stage<TM>(st1, lp, a_base, b_base, sa_base, min(1, KT - 1), wave, lane);
+
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int kb) {
+    wait_vmcnt<R::LW * (NS - 2)>();
+    block_barrier();
+    const float sbg = sb_g[kb];
+    const float sbu = GATED ? sb_u[kb] : sbg;
+    ring_step<TM, GATED>(cur, nxt, min(kb + NS - 1, KT - 1), acc, lp, a_base, b_base, sa_base, sbg, sbu, wave,
+                         lane, wm, wn);
+  };
+  // whole rounds in the loop, the remainder after it: the loop's back edge is
+  // then only reached after a full round, which keeps the compiler's view of
+  // the in-flight DMA exact
+  int kb = 0;
+  if constexpr (NS == 3) {
+    for (; kb + 3 <= KT; kb += 3) {
+      step(st0, st2, kb);
+      step(st1, st0, kb + 1);
+      step(st2, st1, kb + 2);
+    }
+    if (kb < KT) step(st0, st2, kb);
+    if (kb + 1 < KT) step(st1, st0, kb + 1);
+  } else {
+    for (; kb + 2 <= KT; kb += 2) {
+      step(st0, st1, kb);
+      step(st1, st0, kb + 1);
+    }
+    if (kb < KT) step(st0, st1, kb);
+  }
+  wait_vmcnt<0>();  // no LDS DMA may outlive the workgroup
+  block_barrier();  // every wave is done with the ring before the epilogue
+}
+
+// Logical chunk stored at (row r, physical chunk pc) under the swizzle.
+__device__ __forceinline__ int unswz_chunk(int r, int pc) { return pc ^ ((r >> 1) & 7); }
 
 // ------------------------------------------------------------------------------------------
 // GEMM1 + SwiGLU + 1x128 FP8 requantisation.
 template <int TM>
-__global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
+__global__ __launch_bounds__(TileCfg<TM>::THREADS) void gemm1_swiglu_quant_kernel(
     const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
     const float* __restrict__ w13_scale, const int32_t* __restrict__ padded,
     const int32_t* __restrict__ sorted_src, int E, int K, int H, int I, uint8_t* __restrict__ q,
     float* __restrict__ q_scale) {
   using C = TileCfg<TM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Mainloop<TM, true>::STAGE];
+  using R = Ring<TM>;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[R::NS == 3 ? R::STAGE : 16];
+  __shared__ float red[C::WN * TM];
 
   const int NT = I / 128;
   TileCoord tc;
@@ -203,35 +311,32 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   const int KT = H / kKB;
   const int HB = H / kKB;
 
-  // A: gathered token rows
-  const uint8_t* a_src[C::A_ITERS];
+  // load plan: A = gathered token rows (a pad row reads token 0; its result is never used)
+  LoadPlan<TM> lp;
 #pragma unroll
-  for (int i = 0; i < C::A_ITERS; ++i) {
-    const int cid = tid + i * kThreads;
-    a_src[i] = nullptr;
-    if (cid < C::A_CHUNKS) {
-      const int src = sorted_src[tc.p0 + (cid >> 3)];
-      if (src >= 0) a_src[i] = x + (size_t)(src / K) * H + (cid & 7) * 16;
-    }
+  for (int j = 0; j < R::A_PER_WAVE; ++j) {
+    const int ai = (wave * R::A_PER_WAVE + j) % R::A_TOTAL;
+    const int r = ai * 8 + (lane >> 3);
+    const int src = sorted_src[tc.p0 + r];
+    const uint32_t tok = src >= 0 ? (uint32_t)(src / K) : 0u;
+    lp.a_off[j] = tok * (uint32_t)H + (uint32_t)(unswz_chunk(r, lane & 7) * 16);
   }
-  // B: 256 weight rows = per wave: WTN/2 gate rows then WTN/2 up rows of its columns
-  const uint8_t* b_src[C::B_ITERS];
-  const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
+  // B = 256 weight rows: per wave, WTN/2 gate rows then WTN/2 up rows of its columns
 #pragma unroll
-  for (int i = 0; i < C::B_ITERS; ++i) {
-    const int cid = tid + i * kThreads;
-    const int br = cid >> 3;
+  for (int j = 0; j < R::B_PER_WAVE; ++j) {
+    const int br = (wave * R::B_PER_WAVE + j) * 8 + (lane >> 3);
     const int wb = br / C::WTN, within = br % C::WTN;
     const int half = C::WTN / 2;
     const int h = within / half, c = within % half;
-    const int wrow = h * I + n0 + wb * half + c;
-    b_src[i] = wexp + (size_t)wrow * H + (cid & 7) * 16;
+    const uint32_t wrow = (uint32_t)(h * I + n0 + wb * half + c);
+    lp.b_off[j] = wrow * (uint32_t)H + (uint32_t)(unswz_chunk(br, lane & 7) * 16);
   }
-  const float* sa_src = nullptr;
-  if (tid < TM) {
-    const int src = sorted_src[tc.p0 + tid];
-    if (src >= 0) sa_src = x_scale + (size_t)(src / K) * HB;
+  {
+    const int r = wave * R::SA_ROWS + (lane < R::SA_ROWS ? lane : 0);
+    const int src = sorted_src[tc.p0 + r];
+    lp.sa_off = (src >= 0 ? (uint32_t)(src / K) : 0u) * (uint32_t)HB;
   }
+  const uint8_t* b_base = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
   const int IB2 = 2 * I / 128;
   const float* sb_g = w13_scale + ((size_t)tc.e * IB2 + n0 / 128) * HB;
   const float* sb_u = w13_scale + ((size_t)tc.e * IB2 + (I + n0) / 128) * HB;
@@ -242,8 +347,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Mainloop<TM, true> ml{lds};
-  ml.run(acc, a_src, b_src, sa_src, sb_g, sb_u, KT, tid, lane, wm, wn);
+  mainloop<TM, true>(st0, st1, st2, acc, lp, x, b_base, x_scale, sb_g, sb_u, KT, wave, lane, wm, wn);
 
   // ---- epilogue: act = silu(g) * u; per row amax over the tile's 128 columns of I
   constexpr int NH = C::NJ / 2;
@@ -264,8 +368,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
       for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
       rmax[i][r] = m;
     }
-  // cross-wave max: waves with the same wm share rows (LDS free after the main loop)
-  float* red = reinterpret_cast<float*>(lds);  // [WN][TM]
+  // cross-wave max: waves with the same wm share rows
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
@@ -294,13 +397,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
 // ------------------------------------------------------------------------------------------
 // GEMM2 with the top-k weight epilogue.
 template <int TM>
-__global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
+__global__ __launch_bounds__(TileCfg<TM>::THREADS) void gemm2_weighted_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ w2,
     const float* __restrict__ w2_scale, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src, int E, int H, int I,
     uint16_t* __restrict__ Y) {
   using C = TileCfg<TM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Mainloop<TM, false>::STAGE];
+  using R = Ring<TM>;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[R::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[R::NS == 3 ? R::STAGE : 16];
 
   const int NT = (H + kTN - 1) / kTN;
   TileCoord tc;
@@ -313,29 +419,22 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   const int KT = I / kKB;
   const int IB = I / kKB;
 
-  const uint8_t* a_src[C::A_ITERS];
+  // A = q rows p0.. (pad rows hold whatever GEMM1 left there; their outputs are never stored)
+  LoadPlan<TM> lp;
 #pragma unroll
-  for (int i = 0; i < C::A_ITERS; ++i) {
-    const int cid = tid + i * kThreads;
-    a_src[i] = nullptr;
-    if (cid < C::A_CHUNKS) {
-      const int p = tc.p0 + (cid >> 3);
-      if (sorted_src[p] >= 0) a_src[i] = q + (size_t)p * I + (cid & 7) * 16;
-    }
+  for (int j = 0; j < R::A_PER_WAVE; ++j) {
+    const int ai = (wave * R::A_PER_WAVE + j) % R::A_TOTAL;
+    const int r = ai * 8 + (lane >> 3);
+    lp.a_off[j] = (uint32_t)(tc.p0 + r) * (uint32_t)I + (uint32_t)(unswz_chunk(r, lane & 7) * 16);
   }
-  const uint8_t* b_src[C::B_ITERS];
-  const uint8_t* wexp = w2 + (size_t)tc.e * H * (size_t)I;
 #pragma unroll
-  for (int i = 0; i < C::B_ITERS; ++i) {
-    const int cid = tid + i * kThreads;
-    const int wrow = n0 + (cid >> 3);
-    b_src[i] = wrow < H ? wexp + (size_t)wrow * I + (cid & 7) * 16 : nullptr;
+  for (int j = 0; j < R::B_PER_WAVE; ++j) {
+    const int br = (wave * R::B_PER_WAVE + j) * 8 + (lane >> 3);
+    const uint32_t wrow = (uint32_t)min(n0 + br, H - 1);   // rows past H: any valid row, outputs masked
+    lp.b_off[j] = wrow * (uint32_t)I + (uint32_t)(unswz_chunk(br, lane & 7) * 16);
   }
-  const float* sa_src = nullptr;
-  if (tid < TM) {
-    const int p = tc.p0 + tid;
-    if (sorted_src[p] >= 0) sa_src = q_scale + (size_t)p * IB;
-  }
+  lp.sa_off = (uint32_t)(tc.p0 + wave * R::SA_ROWS + (lane < R::SA_ROWS ? lane : 0)) * (uint32_t)IB;
+  const uint8_t* b_base = w2 + (size_t)tc.e * H * (size_t)I;
   // the wave's WTN columns lie in one 128-column scale block (clamped for a partial last tile)
   const int HB = H / 128;
   const int nb = min((n0 + wn * C::WTN) / 128, HB - 1);
@@ -347,8 +446,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  Mainloop<TM, false> ml{lds};
-  ml.run(acc, a_src, b_src, sa_src, sb, sb, KT, tid, lane, wm, wn);
+  mainloop<TM, false>(st0, st1, st2, acc, lp, q, b_base, q_scale, sb, sb, KT, wave, lane, wm, wn);
 
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -377,9 +475,9 @@ static unsigned grid_for(int64_t cap, int tm, int nt) {
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
                         const float* w13_scale, const GroupedRows& g, int H, int I,
                         uint8_t* q, float* q_scale, int tile_m, hipStream_t stream) {
-  const dim3 grid(grid_for(g.cap, tile_m, I / 128)), block(kThreads);
+  const dim3 grid(grid_for(g.cap, tile_m, I / 128));
 #define FP8MOE_G1(TMV)                                                                        \
-  hipLaunchKernelGGL(gemm1_swiglu_quant_kernel<TMV>, grid, block, 0, stream, x, x_scale, w13, \
+  hipLaunchKernelGGL(gemm1_swiglu_quant_kernel<TMV>, grid, dim3(TileCfg<TMV>::THREADS), 0, stream, x, x_scale, w13, \
                      w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, q, q_scale)
   switch (tile_m) {
     case 16: FP8MOE_G1(16); break;
@@ -396,9 +494,9 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
                         const float* w2_scale, const float* topk_weights, const GroupedRows& g,
                         int H, int I, uint16_t* Y, int tile_m, int tile_n, hipStream_t stream) {
   if (tile_n != kTN) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(g.cap, tile_m, (H + kTN - 1) / kTN)), block(kThreads);
+  const dim3 grid(grid_for(g.cap, tile_m, (H + kTN - 1) / kTN));
 #define FP8MOE_G2(TMV)                                                                          \
-  hipLaunchKernelGGL(gemm2_weighted_kernel<TMV>, grid, block, 0, stream, q, q_scale, w2, w2_scale, \
+  hipLaunchKernelGGL(gemm2_weighted_kernel<TMV>, grid, dim3(TileCfg<TMV>::THREADS), 0, stream, q, q_scale, w2, w2_scale, \
                      topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, Y)
   switch (tile_m) {
     case 16: FP8MOE_G2(16); break;
