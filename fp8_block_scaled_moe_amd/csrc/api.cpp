@@ -75,6 +75,8 @@ int check_dims(int64_t T, int H, int I, int E, int K) {
   if (H <= 0 || I <= 0) return fail(FP8MOE_ERR_SHAPE, "H and I must be positive (got %d, %d)", H, I);
   if (H % 128 || I % 128)
     return fail(FP8MOE_ERR_ALIGN, "H and I must be multiples of 128 (got %d, %d)", H, I);
+  if (H > FP8MOE_MAX_DIM || I > FP8MOE_MAX_DIM)
+    return fail(FP8MOE_ERR_LIMIT, "H=%d and I=%d must be at most %d", H, I, FP8MOE_MAX_DIM);
   if (E < 1) return fail(FP8MOE_ERR_SHAPE, "E must be >= 1 (got %d)", E);
   if (E > FP8MOE_MAX_EXPERTS) return fail(FP8MOE_ERR_LIMIT, "E=%d exceeds %d", E, FP8MOE_MAX_EXPERTS);
   if (K < 1 || K > E) return fail(FP8MOE_ERR_TOPK, "top-k K=%d outside [1, E=%d]", K, E);

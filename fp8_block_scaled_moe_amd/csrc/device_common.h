@@ -51,14 +51,4 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// Largest e in [0, E) with padded[e] <= p (p < padded[E]): the expert owning padded row p.
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ padded, int E, int p) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (padded[mid] <= p) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 }  // namespace fp8moe

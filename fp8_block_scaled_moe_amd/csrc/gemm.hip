@@ -2,80 +2,105 @@
 //
 //   GEMM1: h = x[token] . w13[e]^T over gate+up, then SwiGLU and the 1x128
 //          FP8 requantisation in the epilogue (AlphaMoE page, section
-//          "Problem": stages 1-3 fused so the activation never touches HBM
-//          in fp32/bf16; operand layout of the SM120 page, section 1: both
+//          "Problem": stages 1-3 fused so the activation never reaches HBM in
+//          fp32/bf16; operand layout of the SM120 page, section 1: both
 //          operands K-contiguous, gate rows first, then up rows).
 //   GEMM2: y = deq(q) . w2[e]^T, epilogue Y[src] = bf16(topk_weight[src] * y)
 //          (stage 4; the combine is a separate gather-reduce).
 //
-// Block scaling: per 128-wide K step the MFMA accumulates the raw fp8 dot
-// product p = sum_k qa*qb into a zero accumulator; the fp32 result is folded
-// as acc += p * (sa[row] * sb[nblock]), one FMA per output element and step.
-// One v_mfma 16x16x128 covers exactly one scale block, so no K step ever
-// straddles two scales.
+// Block scaling: one v_mfma 16x16x128 covers exactly one 128-wide scale
+// block.  It accumulates the raw fp8 dot product into a zero accumulator and
+// the fp32 result is folded as acc += p * (s_token * s_block), one FMA per
+// output element and K step.
 //
-// Tiling: a workgroup of 4 wave64s owns TM routed rows x 256 weight rows.
-// TM (tile_m) is 16/32 (waves side by side along N, wave tile TM x 64) or
-// 64/128 (2 x 2 waves, wave tile TM/2 x 128).  A (gathered token rows) and B
-// (weight rows) are staged through LDS in 16-byte chunks, double-buffered;
-// each row of 128 bytes has its chunks XOR-swizzled by (row >> 1) & 7 so the
-// 16 rows an MFMA operand read touches spread over distinct banks.
-// For GEMM1 the 256 weight rows are 128 gate + 128 up rows of one 128-column
-// block of I; each wave holds matching gate and up sub-tiles in the same
-// lanes, so SwiGLU is lane-local and the requant amax needs one 16-lane
-// reduction plus a cross-wave max through LDS.
+// Weight streaming.  For these shapes the layer is a stream of expert
+// weights (every active expert's weights are read once, ~256 routed rows
+// share them at prefill, 1-3 at decode), so the design maximises weight bytes
+// in flight:
+//   * a workgroup is 8 wave64s owning 256 weight rows x TM routed rows;
+//   * each wave owns 32 weight rows (two 16-row MFMA operands) and loads them
+//     straight from global memory into a ring of VGPRs D K-steps deep -- no
+//     LDS, no barrier on the weight path, up to D x 4 KB in flight per wave;
+//   * the TM token rows, shared by all 8 waves, go through a small LDS double
+//     buffer (register-staged two steps ahead), one barrier per K step;
+//   * the token-row scales of the whole tile are staged in LDS once.
+// The MFMA puts weight rows on its A side and tokens on its B side, so the
+// lane layout of the result is: token = lane % 16, four consecutive weight
+// rows 4*(lane/16) + r.  The fold then needs one scalar per lane and token
+// sub-tile, and epilogue stores are 4 consecutive columns per lane.
+// Inside each 128-byte K block both operands take K bytes {16g..16g+15} and
+// {64+16g..64+16g+15} for lane group g = lane/16 (the same permutation of K
+// on both sides leaves the dot product unchanged), so one 16-byte weight load
+// of a lane group covers 64 contiguous bytes of each row.
+//
+// GEMM1: wave w owns I columns [n0 + 16w, n0 + 16w + 16): its two operands
+// are the gate rows and the up rows of those columns, so SwiGLU is lane-local
+// and the per-row amax over the tile's 128 columns (one requant block) is a
+// two-step shuffle plus a max over the 8 waves through LDS.
+//
+// Token rows in LDS: [TM][128] bytes, 16-byte chunks XOR-swizzled per row so
+// the 16 rows an operand read touches fall in distinct banks.
 //
 // Workgroup -> tile mapping is XCD-aware: MI355X deals workgroups round-robin
-// over its 8 XCDs, each with its own L2.  Workgroup b runs on XCD b % 8, and
-// is given tile L = (b % 8) * per_xcd + b / 8 of the row-major (m-tile,
-// n-tile) list, so every XCD streams a contiguous range of experts: the
-// m-tiles of one expert run together and share each weight tile in L2.
+// over its 8 XCDs, each with its own L2.  Workgroup b runs on XCD b % 8 and
+// takes tile (b % 8) * per_xcd + b / 8 of the expert-major (m-tile, n-tile)
+// list, so each XCD streams a contiguous range of experts and the m-tiles of
+// one expert run together, sharing every weight tile through that L2.
 #include "device_common.h"
 #include "launch.h"
 
 namespace fp8moe {
 
-constexpr int kTN = 256;       // weight rows per tile
-constexpr int kKB = 128;       // K per step (= scale block)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTN = 256;   // weight rows per tile, 32 per wave
+constexpr int kKB = 128;   // K per step (= scale block)
 
-// Workgroup shape per tile_m: 8 wave64s (2 x 4, wave tile 64 x 64) for 128
-// rows, 4 wave64s otherwise (2 x 2 for 64 rows, 1 x 4 for 16 and 32 rows).
 template <int TM>
-struct TileCfg {
-  static constexpr int WAVES = TM == 128 ? 8 : 4;
-  static constexpr int THREADS = WAVES * 64;
-  static constexpr int WM = TM >= 64 ? 2 : 1;
-  static constexpr int WN = WAVES / WM;
-  static constexpr int WTM = TM / WM;      // rows per wave
-  static constexpr int WTN = kTN / WN;     // weight rows per wave
-  static constexpr int MI = WTM / 16;      // 16-row sub-tiles per wave
-  static constexpr int NJ = WTN / 16;      // 16-col sub-tiles per wave
+struct Cfg {
+  static constexpr int TS = TM / 16;                                 // token sub-tiles
+  static constexpr int D = TM >= 128 ? 4 : (TM >= 64 ? 6 : 8);      // weight ring depth (even)
   static constexpr int A_BYTES = TM * kKB;
-  static constexpr int B_BYTES = kTN * kKB;
+  static constexpr int A_CHUNKS = TM * 8;                            // 16-byte chunks per K step
+  static constexpr int A_PER_THREAD = (A_CHUNKS + kThreads - 1) / kThreads;
+  static_assert(D % 2 == 0, "the token double buffer follows the parity of the unrolled step");
 };
 
-// byte offset of 16-byte chunk c of row r in a swizzled [rows][128] LDS tile
-__device__ __forceinline__ int swz(int r, int c) { return r * kKB + ((c ^ ((r >> 1) & 7)) << 4); }
+// dynamic LDS: two token buffers, the tile's token scales [KT][TM], the epilogue max [8][TM]
+template <int TM>
+constexpr size_t lds_bytes_for(int KT) {
+  return 2 * (size_t)Cfg<TM>::A_BYTES + 4 * (size_t)TM * KT + 4 * (size_t)kWaves * TM;
+}
 
-// MFMA operand fragment for the 16 rows starting at row0: lane l reads row
-// row0 + l%16, K bytes [32*(l/16), +32) = chunks 2*(l/16) and 2*(l/16)+1.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row0, int lane) {
-  const int r = row0 + (lane & 15);
-  const int c = (lane >> 4) << 1;
-  const v4i lo = *reinterpret_cast<const v4i*>(tile + swz(r, c));
-  const v4i hi = *reinterpret_cast<const v4i*>(tile + swz(r, c + 1));
-  v8i out;
-  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
-  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
-  return out;
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * kKB + ((c ^ swz_key(r)) << 4); }
+
+__device__ __forceinline__ v8i join(const v4i& lo, const v4i& hi) {
+  v8i o;
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = lo[2]; o[3] = lo[3];
+  o[4] = hi[0]; o[5] = hi[1]; o[6] = hi[2]; o[7] = hi[3];
+  return o;
+}
+
+// Token operand of sub-tile ts: lane l reads row 16*ts + l%16, chunks g and 4+g.
+__device__ __forceinline__ v8i token_frag(const uint8_t* As, int ts, int lane) {
+  const int r = 16 * ts + (lane & 15);
+  const int g = lane >> 4;
+  return join(*reinterpret_cast<const v4i*>(As + swz(r, g)), *reinterpret_cast<const v4i*>(As + swz(r, g + 4)));
+}
+
+// Weight operand: rowp = start of the lane's weight row + 16*g.
+__device__ __forceinline__ v8i weight_frag(const uint8_t* rowp, int kb) {
+  const uint8_t* p = rowp + (size_t)kb * kKB;
+  return join(*reinterpret_cast<const v4i*>(p), *reinterpret_cast<const v4i*>(p + 64));
 }
 
 // Tile coordinates of workgroup blockIdx.x; false if it has no tile.
 struct TileCoord { int mt, nt, e, p0; };
 
 template <int TM>
-__device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src,
-                                           int E, int NT, TileCoord& tc) {
+__device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
+                                           const int32_t* __restrict__ sorted_src, int E, int NT, TileCoord& tc) {
   const int total_rows = padded[E];
   const int tiles = (total_rows / TM) * NT;
   const int per_xcd = (tiles + kNumXcd - 1) / kNumXcd;
@@ -87,218 +112,160 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded, c
   tc.nt = L - tc.mt * NT;
   tc.p0 = tc.mt * TM;
   if (sorted_src[tc.p0] < 0) return false;  // segment padding only: nothing to compute
-  tc.e = expert_of_row(padded, E, tc.p0);
+  // expert owning row p0 = (number of e in [0, E) with padded[e] <= p0) - 1:
+  // padded is non-decreasing, so those e form a prefix.  One round of
+  // coalesced loads and a wave sum instead of a chain of dependent loads.
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int e = lane; e < E; e += 64) cnt += padded[e] <= tc.p0 ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  tc.e = __builtin_amdgcn_readfirstlane(cnt - 1);
   return true;
 }
 
-// ------------------------------------------------------------------------------------------
-// Asynchronous global -> LDS ring.
-//
-// Each stage holds one 128-wide K step: A [TM][128], B [256][128] (both
-// swizzled) and the TM A-row scales.  Stages are filled with
-// global_load_lds_dwordx4: one wave instruction writes 1 KB of LDS, lane i at
-// byte 16*i, i.e. 8 rows x 8 chunks; the lane fetches from global memory the
-// logical chunk that the swizzle places at its slot.  Every wave issues the
-// same number of loads per stage (LW), so "stage kb has landed" is a single
-// immediate vmcnt: the loads of the stages issued after it may stay in flight.
-// A barrier then publishes the stage to all waves and frees the buffer that
-// was consumed in the previous step, which is refilled NS-1 steps ahead.
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) through the builtin, so the compiler's own
-// wait tracking knows which LDS DMA has landed (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4 left at 7, lgkmcnt 11:8 = 0).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
-}
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those would wait for every LDS DMA in flight.  The empty asm statements keep
-// the compiler from moving memory accesses across it, the scheduling barriers
-// keep a step's register-only work (MFMAs) from sliding into the next step,
-// which would keep two steps' operand fragments live at once.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs on its side of the barrier
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const float* g, float* l) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)l, 4, 0, 0);
-}
-
+// Per-tile description of the operands the main loop streams.
 template <int TM>
-struct Ring {
-  using C = TileCfg<TM>;
-  static constexpr int NS = TM >= 64 ? 3 : 2;                 // LDS stages
-  static constexpr int SA_BYTES = (TM * 4 + 15) / 16 * 16;
-  static constexpr int STAGE = C::A_BYTES + C::B_BYTES + SA_BYTES;
-  static constexpr int A_TOTAL = TM / 8;                      // 1-KB A loads per stage
-  static constexpr int A_PER_WAVE = A_TOTAL >= C::WAVES ? A_TOTAL / C::WAVES : 1;
-  static constexpr int B_PER_WAVE = kTN / 8 / C::WAVES;
-  static constexpr int SA_ROWS = TM / C::WAVES;               // scale rows per wave
-  static constexpr int LW = A_PER_WAVE + B_PER_WAVE + 1;      // loads per wave per stage
-  static_assert(LW * (NS - 2) <= 63, "vmcnt range");
+struct Operands {
+  const uint8_t* a_src[Cfg<TM>::A_PER_THREAD];  // this thread's token-row chunks (k step 0), or nullptr
+  const uint8_t* w_row[2];                      // this lane's two weight rows (+16*g)
+  const float* sb[2];                           // the wave's two block-scale rows (one float per K step)
 };
 
-// Per-thread load plan: byte offsets (from a wave-uniform base) of the chunks
-// this lane fetches for k-step 0; k-step kb adds kb*128 (kb for scales).
-template <int TM>
-struct LoadPlan {
-  using R = Ring<TM>;
-  uint32_t a_off[R::A_PER_WAVE];
-  uint32_t b_off[R::B_PER_WAVE];
-  uint32_t sa_off;     // in floats
-};
-
-template <int TM>
-__device__ __forceinline__ void issue_stage(uint8_t* stage, const LoadPlan<TM>& lp, const uint8_t* a_base,
-                                            const uint8_t* b_base, const float* sa_base, int kb, int wave,
-                                            int lane) {
-  using R = Ring<TM>;
-  using C = TileCfg<TM>;
-  // address = wave-uniform base + 32-bit lane offset (the K step folded into
-  // the offset), so each load is one VGPR offset on an SGPR base
-  const uint32_t kofs = (uint32_t)kb * kKB;
-#pragma unroll
-  for (int j = 0; j < R::A_PER_WAVE; ++j) {
-    const int ai = (wave * R::A_PER_WAVE + j) % R::A_TOTAL;
-    dma16(a_base + (lp.a_off[j] + kofs), stage + ai * 1024);
-  }
-#pragma unroll
-  for (int j = 0; j < R::B_PER_WAVE; ++j) {
-    const int bi = wave * R::B_PER_WAVE + j;
-    dma16(b_base + (lp.b_off[j] + kofs), stage + C::A_BYTES + bi * 1024);
-  }
-  float* sa = reinterpret_cast<float*>(stage + C::A_BYTES + C::B_BYTES);
-  if (lane < R::SA_ROWS) dma4(sa_base + (lp.sa_off + (uint32_t)kb), sa + wave * R::SA_ROWS);
+// The token scales of the tile -> LDS, layout [kb][l16][ts] so a lane's TS
+// values for one K step are contiguous.  row_scale(r) gives the row's scale
+// vector (nullptr for a pad row).  Each thread keeps one row and walks its K
+// steps, so after the one row lookup its loads are independent.
+template <int TM, typename RowScale>
+__device__ __forceinline__ void stage_token_scales(float* SAs, int KT, RowScale row_scale, int tid) {
+  constexpr int TS = Cfg<TM>::TS;
+  constexpr int TPR = kThreads / TM;   // threads per row
+  const int r = tid / TPR, part = tid % TPR;
+  const float* rs = row_scale(r);
+  float* dst = SAs + (r & 15) * TS + (r >> 4);
+  for (int kb = part; kb < KT; kb += TPR) dst[kb * TM] = rs ? rs[kb] : 0.f;
 }
 
-// One K step: refill `nxt` (when asked) and multiply out of `cur`.  The two
-// stage pointers are distinct __restrict__ parameters of an inlined function,
-// so the LDS reads of `cur` carry alias-scope metadata saying they do not
-// touch the stage being refilled; without it the compiler would wait for every
-// outstanding LDS DMA (vmcnt(0)) before the first read and serialise the ring.
-// The real ordering is enforced by wait_stage + block_barrier in the caller.
-template <int TM, bool GATED>
-__device__ __forceinline__ void ring_step(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int kb_refill, v4f (&acc)[TileCfg<TM>::MI][TileCfg<TM>::NJ],
-                                          const LoadPlan<TM>& lp, const uint8_t* a_base, const uint8_t* b_base,
-                                          const float* sa_base, float sbg, float sbu, int wave, int lane, int wm,
-                                          int wn) {
-  using C = TileCfg<TM>;
-  issue_stage<TM>(nxt, lp, a_base, b_base, sa_base, kb_refill, wave, lane);
-  const uint8_t* A = cur;
-  const uint8_t* B = cur + C::A_BYTES;
-  const float* SA = reinterpret_cast<const float*>(B + C::B_BYTES);
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  v8i af[C::MI];
-  v4f sv[C::MI];
+template <int TS>
+__device__ __forceinline__ void read_token_scales(const float* p, float (&sa)[TS]) {
+  if constexpr (TS >= 4) {
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    af[i] = lds_frag(A, wm * C::WTM + 16 * i, lane);
-    sv[i] = *reinterpret_cast<const v4f*>(SA + wm * C::WTM + 16 * i + 4 * (lane >> 4));
-  }
-  // gate sub-tiles (j < NJ/2) use the gate block scale, up sub-tiles the up one
-#pragma unroll
-  for (int h = 0; h < (GATED ? 2 : 1); ++h) {
-    const float sb = h ? sbu : sbg;
-    v4f c[C::MI];
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) c[i] = sv[i] * sb;
-    constexpr int JN = GATED ? C::NJ / 2 : C::NJ;
-#pragma unroll
-    for (int jj = 0; jj < JN; ++jj) {
-      const int j = h * JN + jj;
-      const v8i bf = lds_frag(B, wn * C::WTN + 16 * j, lane);
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) {
-        const v4f pr = mfma16x16x128_fp8(af[i], bf, zero);
-        acc[i][j] += pr * c[i];
-      }
+    for (int q = 0; q < TS / 4; ++q) {
+      const v4f v = *reinterpret_cast<const v4f*>(p + 4 * q);
+      sa[4 * q] = v[0]; sa[4 * q + 1] = v[1]; sa[4 * q + 2] = v[2]; sa[4 * q + 3] = v[3];
     }
-  }
-  // MFMAs and folds are pure register work: without this the compiler sinks
-  // them past later barriers and keeps several steps' fragments live at once.
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
-}
-
-// Main loop shared by both GEMMs: acc[i][j] for the wave's MI x NJ sub-tiles.
-// st0..st2 are distinct __shared__ arrays (st2 unused when NS == 2); the loop is
-// unrolled by NS so every step reads and refills statically known stages and
-// the compiler can tell the in-flight DMA never targets the stage being read.
-// Every step refills (past the last K step it re-reads the last one, which
-// is never consumed), so each step issues the same LW loads per wave and one
-// constant wait -- all but the newest NS-2 stages landed -- is always right.
-// sb_g/sb_u: the wave's weight-scale rows (gate/up, or the single block), one float per K step.
-template <int TM, bool GATED>
-__device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st2,
-                                         v4f (&acc)[TileCfg<TM>::MI][TileCfg<TM>::NJ], const LoadPlan<TM>& lp,
-                                         const uint8_t* a_base, const uint8_t* b_base, const float* sa_base,
-                                         const float* sb_g, const float* sb_u, int KT, int wave, int lane, int wm,
-                                         int wn) {
-  using R = Ring<TM>;
-  constexpr int NS = R::NS;
-  issue_stage<TM>(st0, lp, a_base, b_base, sa_base, 0, wave, lane);
-  if constexpr (NS == 3) issue_stage<TM>(st1, lp, a_base, b_base, sa_base, min(1, KT - 1), wave, lane);
-
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int kb) {
-    wait_vmcnt<R::LW * (NS - 2)>();
-    block_barrier();
-    const float sbg = sb_g[kb];
-    const float sbu = GATED ? sb_u[kb] : sbg;
-    ring_step<TM, GATED>(cur, nxt, min(kb + NS - 1, KT - 1), acc, lp, a_base, b_base, sa_base, sbg, sbu, wave,
-                         lane, wm, wn);
-  };
-  // whole rounds in the loop, the remainder after it: the loop's back edge is
-  // then only reached after a full round, which keeps the compiler's view of
-  // the in-flight DMA exact
-  int kb = 0;
-  if constexpr (NS == 3) {
-    for (; kb + 3 <= KT; kb += 3) {
-      step(st0, st2, kb);
-      step(st1, st0, kb + 1);
-      step(st2, st1, kb + 2);
-    }
-    if (kb < KT) step(st0, st2, kb);
-    if (kb + 1 < KT) step(st1, st0, kb + 1);
   } else {
-    for (; kb + 2 <= KT; kb += 2) {
-      step(st0, st1, kb);
-      step(st1, st0, kb + 1);
-    }
-    if (kb < KT) step(st0, st1, kb);
+#pragma unroll
+    for (int q = 0; q < TS; ++q) sa[q] = p[q];
   }
-  wait_vmcnt<0>();  // no LDS DMA may outlive the workgroup
-  block_barrier();  // every wave is done with the ring before the epilogue
 }
 
-// Logical chunk stored at (row r, physical chunk pc) under the swizzle.
-__device__ __forceinline__ int unswz_chunk(int r, int pc) { return pc ^ ((r >> 1) & 7); }
+// ------------------------------------------------------------------------------------------
+// Main loop: acc[ts][w] for the wave's two weight sub-tiles x TS token sub-tiles.
+template <int TM, bool GATED>
+__device__ __forceinline__ void ws_mainloop(uint8_t* smem, const Operands<TM>& op, int KT, int tid, int lane,
+                                            v4f (&acc)[Cfg<TM>::TS][2]) {
+  using C = Cfg<TM>;
+  constexpr int TS = C::TS, D = C::D, AP = C::A_PER_THREAD;
+  uint8_t* As[2] = {smem, smem + C::A_BYTES};
+  const float* SAs = reinterpret_cast<const float*>(smem + 2 * C::A_BYTES);
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  v8i wr[D][2];   // weight ring: slot s holds K step k with k % D == s
+  v4i ra[2][AP];  // token rows staged in registers, indexed by K-step parity
+
+  auto load_w = [&](int s, int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag(op.w_row[w], k);
+  };
+  auto load_a = [&](int par, int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i)
+      if (op.a_src[i]) ra[par][i] = *reinterpret_cast<const v4i*>(op.a_src[i] + (size_t)k * kKB);
+  };
+  auto store_a = [&](int par) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+      const int cid = tid + i * kThreads;
+      if (cid < C::A_CHUNKS) *reinterpret_cast<v4i*>(As[par] + swz(cid >> 3, cid & 7)) = ra[par][i];
+    }
+  };
+  // one K step (slot s = k % D, parity s & 1 = k & 1)
+  auto step = [&](int k, int s, bool more_a1, bool more_a3, bool more_w) __attribute__((always_inline)) {
+    const int par = s & 1;
+    if (more_a1) store_a(par ^ 1);          // token rows of step k+1 -> the other buffer
+    if (more_a3) load_a(par ^ 1, k + 3);    // that register set is free again: fetch step k+3
+    float sa[TS];
+    read_token_scales<TS>(SAs + (size_t)k * TM + (lane & 15) * TS, sa);
+    const float sb0 = op.sb[0][k];
+    const float sb1 = GATED ? op.sb[1][k] : sb0;
+    // software pipeline over the token sub-tiles: operands are read two
+    // sub-tiles ahead, and the fold of sub-tile ts waits until the MFMAs of
+    // ts+1 are issued, so neither LDS latency nor MFMA latency is exposed
+    v8i af[3];
+    v4f pr[2][2];
+    af[0] = token_frag(As[par], 0, lane);
+    if (TS > 1) af[1] = token_frag(As[par], 1, lane);
+    auto fold = [&](int ts) __attribute__((always_inline)) {
+      acc[ts][0] += pr[ts & 1][0] * (sa[ts] * sb0);
+      acc[ts][1] += pr[ts & 1][1] * (sa[ts] * sb1);
+    };
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) {
+      if (ts + 2 < TS) af[(ts + 2) % 3] = token_frag(As[par], ts + 2, lane);
+      pr[ts & 1][0] = mfma16x16x128_fp8(wr[s][0], af[ts % 3], zero);
+      pr[ts & 1][1] = mfma16x16x128_fp8(wr[s][1], af[ts % 3], zero);
+      if (ts >= 1) fold(ts - 1);
+    }
+    fold(TS - 1);
+    // MFMAs and folds are pure register work: pin them to this step, or the
+    // compiler sinks them past later barriers and keeps old ring slots alive
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) {
+      asm volatile("" : "+v"(acc[ts][0]));
+      asm volatile("" : "+v"(acc[ts][1]));
+    }
+    if (more_w) load_w(s, k + D);
+    __syncthreads();
+  };
+
+  // prologue: weights of steps 0..D-1, token rows of steps 0..2
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < KT) load_w(s, s);
+  load_a(0, 0);
+  if (KT > 1) load_a(1, 1);
+  store_a(0);
+  if (KT > 2) load_a(0, 2);
+  __syncthreads();
+
+  int kb = 0;
+  // steady state: every step refills, no guards (the back edge always follows a full round)
+  for (; kb + 2 * D <= KT; kb += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) step(kb + s, s, true, true, true);
+  }
+  // last rounds
+  for (; kb < KT; kb += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int k = kb + s;
+      if (k < KT) step(k, s, k + 1 < KT, k + 3 < KT, k + D < KT);
+    }
+  }
+}
 
 // ------------------------------------------------------------------------------------------
 // GEMM1 + SwiGLU + 1x128 FP8 requantisation.
 template <int TM>
-__global__ __launch_bounds__(TileCfg<TM>::THREADS) void gemm1_swiglu_quant_kernel(
+__global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
     const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
     const float* __restrict__ w13_scale, const int32_t* __restrict__ padded,
     const int32_t* __restrict__ sorted_src, int E, int K, int H, int I, uint8_t* __restrict__ q,
     float* __restrict__ q_scale) {
-  using C = TileCfg<TM>;
-  using R = Ring<TM>;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[R::NS == 3 ? R::STAGE : 16];
-  __shared__ float red[C::WN * TM];
+  using C = Cfg<TM>;
+  constexpr int TS = C::TS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int NT = I / 128;
   TileCoord tc;
@@ -306,107 +273,82 @@ __global__ __launch_bounds__(TileCfg<TM>::THREADS) void gemm1_swiglu_quant_kerne
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int g = lane >> 4, l16 = lane & 15;
   const int n0 = tc.nt * 128;             // first column of I in this tile
-  const int KT = H / kKB;
-  const int HB = H / kKB;
+  const int c0 = n0 + 16 * wave;          // the wave's 16 columns of I
+  const int KT = H / kKB, HB = H / kKB;
+  float* SAs = reinterpret_cast<float*>(smem + 2 * C::A_BYTES);
+  float* red = SAs + (size_t)TM * KT;
 
-  // load plan: A = gathered token rows (a pad row reads token 0; its result is never used)
-  LoadPlan<TM> lp;
+  Operands<TM> op;
 #pragma unroll
-  for (int j = 0; j < R::A_PER_WAVE; ++j) {
-    const int ai = (wave * R::A_PER_WAVE + j) % R::A_TOTAL;
-    const int r = ai * 8 + (lane >> 3);
-    const int src = sorted_src[tc.p0 + r];
-    const uint32_t tok = src >= 0 ? (uint32_t)(src / K) : 0u;
-    lp.a_off[j] = tok * (uint32_t)H + (uint32_t)(unswz_chunk(r, lane & 7) * 16);
+  for (int i = 0; i < C::A_PER_THREAD; ++i) {
+    const int cid = tid + i * kThreads;
+    op.a_src[i] = nullptr;
+    if (cid < C::A_CHUNKS) {
+      const int src = sorted_src[tc.p0 + (cid >> 3)];
+      const size_t tok = src >= 0 ? (size_t)(src / K) : 0;  // a pad row reads token 0; never stored
+      op.a_src[i] = x + tok * H + (cid & 7) * 16;
+    }
   }
-  // B = 256 weight rows: per wave, WTN/2 gate rows then WTN/2 up rows of its columns
-#pragma unroll
-  for (int j = 0; j < R::B_PER_WAVE; ++j) {
-    const int br = (wave * R::B_PER_WAVE + j) * 8 + (lane >> 3);
-    const int wb = br / C::WTN, within = br % C::WTN;
-    const int half = C::WTN / 2;
-    const int h = within / half, c = within % half;
-    const uint32_t wrow = (uint32_t)(h * I + n0 + wb * half + c);
-    lp.b_off[j] = wrow * (uint32_t)H + (uint32_t)(unswz_chunk(br, lane & 7) * 16);
-  }
-  {
-    const int r = wave * R::SA_ROWS + (lane < R::SA_ROWS ? lane : 0);
-    const int src = sorted_src[tc.p0 + r];
-    lp.sa_off = (src >= 0 ? (uint32_t)(src / K) : 0u) * (uint32_t)HB;
-  }
-  const uint8_t* b_base = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
+  const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
+  op.w_row[0] = wexp + (size_t)(c0 + l16) * H + 16 * g;          // gate rows
+  op.w_row[1] = wexp + (size_t)(I + c0 + l16) * H + 16 * g;      // up rows
   const int IB2 = 2 * I / 128;
-  const float* sb_g = w13_scale + ((size_t)tc.e * IB2 + n0 / 128) * HB;
-  const float* sb_u = w13_scale + ((size_t)tc.e * IB2 + (I + n0) / 128) * HB;
+  op.sb[0] = w13_scale + ((size_t)tc.e * IB2 + n0 / 128) * HB;
+  op.sb[1] = w13_scale + ((size_t)tc.e * IB2 + (I + n0) / 128) * HB;
 
-  v4f acc[C::MI][C::NJ];
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  stage_token_scales<TM>(SAs, KT, [&](int r) -> const float* {
+    const int src = sorted_src[tc.p0 + r];
+    return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
+  }, tid);
 
-  mainloop<TM, true>(st0, st1, st2, acc, lp, x, b_base, x_scale, sb_g, sb_u, KT, wave, lane, wm, wn);
-
-  // ---- epilogue: act = silu(g) * u; per row amax over the tile's 128 columns of I
-  constexpr int NH = C::NJ / 2;
-  float rmax[C::MI][4];
+  v4f acc[TS][2];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+  for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  ws_mainloop<TM, true>(smem, op, KT, tid, lane, acc);
+
+  // ---- epilogue: act = silu(gate) * up; per token row amax over the tile's 128 columns
+  float act[TS][4];
+#pragma unroll
+  for (int ts = 0; ts < TS; ++ts) {
+    float m = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float m = 0.f;
-#pragma unroll
-      for (int j = 0; j < NH; ++j) {
-        const float a = silu_mul(acc[i][j][r], acc[i][j + NH][r]);
-        acc[i][j][r] = a;
-        m = fmaxf(m, fabsf(a));
-      }
-      // max over the 16 lanes holding the same row (lanes differ in l % 16)
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
-      rmax[i][r] = m;
+      act[ts][r] = silu_mul(acc[ts][0][r], acc[ts][1][r]);
+      m = fmaxf(m, fabsf(act[ts][r]));
     }
-  // cross-wave max: waves with the same wm share rows
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[wn * TM + wm * C::WTM + 16 * i + 4 * (lane >> 4) + r] = rmax[i][r];
+    m = fmaxf(m, __shfl_xor(m, 16));   // lanes l16, l16+16, +32, +48 hold the same token
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (g == 0) red[wave * TM + 16 * ts + l16] = m;
   }
   __syncthreads();
   const int IB = I / 128;
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+  for (int ts = 0; ts < TS; ++ts) {
+    const int row = 16 * ts + l16;
+    float amax = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * C::WTM + 16 * i + 4 * (lane >> 4) + r;
-      float amax = 0.f;
-#pragma unroll
-      for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, red[w * TM + row]);
-      const float s = amax > 0.f ? amax / kE4m3Max : 1.0f;
-      const size_t prow = (size_t)(tc.p0 + row);
-      uint8_t* qrow = q + prow * I + n0 + wn * NH * 16;
-#pragma unroll
-      for (int j = 0; j < NH; ++j) qrow[16 * j + (lane & 15)] = (uint8_t)one_e4m3(acc[i][j][r] / s);
-      if (wn == 0 && (lane & 15) == 0) q_scale[prow * IB + n0 / 128] = s;
-    }
+    for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w * TM + row]);
+    const float s = amax > 0.f ? amax / kE4m3Max : 1.0f;
+    const size_t prow = (size_t)(tc.p0 + row);
+    *reinterpret_cast<uint32_t*>(q + prow * I + c0 + 4 * g) =
+        pack4_e4m3(act[ts][0] / s, act[ts][1] / s, act[ts][2] / s, act[ts][3] / s);
+    if (wave == 0 && g == 0) q_scale[prow * IB + n0 / 128] = s;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // GEMM2 with the top-k weight epilogue.
 template <int TM>
-__global__ __launch_bounds__(TileCfg<TM>::THREADS) void gemm2_weighted_kernel(
+__global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ w2,
     const float* __restrict__ w2_scale, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src, int E, int H, int I,
     uint16_t* __restrict__ Y) {
-  using C = TileCfg<TM>;
-  using R = Ring<TM>;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[R::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[R::NS == 3 ? R::STAGE : 16];
+  using C = Cfg<TM>;
+  constexpr int TS = C::TS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int NT = (H + kTN - 1) / kTN;
   TileCoord tc;
@@ -414,55 +356,61 @@ __global__ __launch_bounds__(TileCfg<TM>::THREADS) void gemm2_weighted_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int g = lane >> 4, l16 = lane & 15;
   const int n0 = tc.nt * kTN;
-  const int KT = I / kKB;
-  const int IB = I / kKB;
+  const int c0 = n0 + 32 * wave;          // the wave's 32 output columns
+  const int KT = I / kKB, IB = I / kKB;
+  float* SAs = reinterpret_cast<float*>(smem + 2 * C::A_BYTES);
 
-  // A = q rows p0.. (pad rows hold whatever GEMM1 left there; their outputs are never stored)
-  LoadPlan<TM> lp;
+  // token rows: q rows p0.. (a pad row holds whatever is there; its outputs are never stored)
+  Operands<TM> op;
 #pragma unroll
-  for (int j = 0; j < R::A_PER_WAVE; ++j) {
-    const int ai = (wave * R::A_PER_WAVE + j) % R::A_TOTAL;
-    const int r = ai * 8 + (lane >> 3);
-    lp.a_off[j] = (uint32_t)(tc.p0 + r) * (uint32_t)I + (uint32_t)(unswz_chunk(r, lane & 7) * 16);
+  for (int i = 0; i < C::A_PER_THREAD; ++i) {
+    const int cid = tid + i * kThreads;
+    op.a_src[i] = cid < C::A_CHUNKS ? q + (size_t)(tc.p0 + (cid >> 3)) * I + (cid & 7) * 16 : nullptr;
   }
+  const uint8_t* wexp = w2 + (size_t)tc.e * H * (size_t)I;
 #pragma unroll
-  for (int j = 0; j < R::B_PER_WAVE; ++j) {
-    const int br = (wave * R::B_PER_WAVE + j) * 8 + (lane >> 3);
-    const uint32_t wrow = (uint32_t)min(n0 + br, H - 1);   // rows past H: any valid row, outputs masked
-    lp.b_off[j] = wrow * (uint32_t)I + (uint32_t)(unswz_chunk(br, lane & 7) * 16);
+  for (int w = 0; w < 2; ++w) {
+    const int row = min(c0 + 16 * w + l16, H - 1);   // rows past H: any valid row, outputs masked
+    op.w_row[w] = wexp + (size_t)row * I + 16 * g;
   }
-  lp.sa_off = (uint32_t)(tc.p0 + wave * R::SA_ROWS + (lane < R::SA_ROWS ? lane : 0)) * (uint32_t)IB;
-  const uint8_t* b_base = w2 + (size_t)tc.e * H * (size_t)I;
-  // the wave's WTN columns lie in one 128-column scale block (clamped for a partial last tile)
   const int HB = H / 128;
-  const int nb = min((n0 + wn * C::WTN) / 128, HB - 1);
-  const float* sb = w2_scale + ((size_t)tc.e * HB + nb) * IB;
+  const int nb = min(c0 / 128, HB - 1);
+  op.sb[0] = op.sb[1] = w2_scale + ((size_t)tc.e * HB + nb) * IB;
 
-  v4f acc[C::MI][C::NJ];
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  stage_token_scales<TM>(SAs, KT, [&](int r) -> const float* {
+    const int p = tc.p0 + r;
+    return sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
+  }, tid);
 
-  mainloop<TM, false>(st0, st1, st2, acc, lp, q, b_base, q_scale, sb, sb, KT, wave, lane, wm, wn);
+  v4f acc[TS][2];
+#pragma unroll
+  for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  ws_mainloop<TM, false>(smem, op, KT, tid, lane, acc);
 
+  int src[TS];
+  float wt[TS];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+  for (int ts = 0; ts < TS; ++ts) {
+    src[ts] = sorted_src[tc.p0 + 16 * ts + l16];
+    wt[ts] = src[ts] >= 0 ? topk_weights[src[ts]] : 0.f;
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * C::WTM + 16 * i + 4 * (lane >> 4) + r;
-      const int src = sorted_src[tc.p0 + row];
-      if (src < 0) continue;
-      const float w = topk_weights[src];
-      uint16_t* yrow = Y + (size_t)src * H;
+  for (int ts = 0; ts < TS; ++ts) {
+    if (src[ts] < 0) continue;
+    uint16_t* yrow = Y + (size_t)src[ts] * H;
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        const int col = n0 + wn * C::WTN + 16 * j + (lane & 15);
-        if (col < H) yrow[col] = f32_to_bf16(w * acc[i][j][r]);
+    for (int w = 0; w < 2; ++w) {
+      const int col = c0 + 16 * w + 4 * g;
+      if (col < H) {
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16(wt[ts] * acc[ts][w][0]) | ((uint32_t)f32_to_bf16(wt[ts] * acc[ts][w][1]) << 16);
+        v.y = (uint32_t)f32_to_bf16(wt[ts] * acc[ts][w][2]) | ((uint32_t)f32_to_bf16(wt[ts] * acc[ts][w][3]) << 16);
+        *reinterpret_cast<uint2*>(yrow + col) = v;
       }
     }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -472,12 +420,36 @@ static unsigned grid_for(int64_t cap, int tm, int nt) {
   return (unsigned)(g > 0 ? g : kNumXcd);
 }
 
+size_t gemm_lds_bytes(int tile_m, int KT) {
+  switch (tile_m) {
+    case 16: return lds_bytes_for<16>(KT);
+    case 32: return lds_bytes_for<32>(KT);
+    case 64: return lds_bytes_for<64>(KT);
+    default: return lds_bytes_for<128>(KT);
+  }
+}
+
+template <typename Kern>
+static hipError_t allow_lds(Kern k) {
+  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxGemmLds);
+}
+
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
                         const float* w13_scale, const GroupedRows& g, int H, int I,
                         uint8_t* q, float* q_scale, int tile_m, hipStream_t stream) {
-  const dim3 grid(grid_for(g.cap, tile_m, I / 128));
-#define FP8MOE_G1(TMV)                                                                        \
-  hipLaunchKernelGGL(gemm1_swiglu_quant_kernel<TMV>, grid, dim3(TileCfg<TMV>::THREADS), 0, stream, x, x_scale, w13, \
+  static const hipError_t attr = [] {
+    hipError_t e = allow_lds(gemm1_swiglu_quant_kernel<16>);
+    if (e == hipSuccess) e = allow_lds(gemm1_swiglu_quant_kernel<32>);
+    if (e == hipSuccess) e = allow_lds(gemm1_swiglu_quant_kernel<64>);
+    if (e == hipSuccess) e = allow_lds(gemm1_swiglu_quant_kernel<128>);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  const size_t lds = gemm_lds_bytes(tile_m, H / kKB);
+  if (lds > kMaxGemmLds) return hipErrorInvalidValue;
+  const dim3 grid(grid_for(g.cap, tile_m, I / 128)), block(kThreads);
+#define FP8MOE_G1(TMV)                                                                          \
+  hipLaunchKernelGGL(gemm1_swiglu_quant_kernel<TMV>, grid, block, lds, stream, x, x_scale, w13, \
                      w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, q, q_scale)
   switch (tile_m) {
     case 16: FP8MOE_G1(16); break;
@@ -494,9 +466,19 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
                         const float* w2_scale, const float* topk_weights, const GroupedRows& g,
                         int H, int I, uint16_t* Y, int tile_m, int tile_n, hipStream_t stream) {
   if (tile_n != kTN) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(g.cap, tile_m, (H + kTN - 1) / kTN));
-#define FP8MOE_G2(TMV)                                                                          \
-  hipLaunchKernelGGL(gemm2_weighted_kernel<TMV>, grid, dim3(TileCfg<TMV>::THREADS), 0, stream, q, q_scale, w2, w2_scale, \
+  static const hipError_t attr = [] {
+    hipError_t e = allow_lds(gemm2_weighted_kernel<16>);
+    if (e == hipSuccess) e = allow_lds(gemm2_weighted_kernel<32>);
+    if (e == hipSuccess) e = allow_lds(gemm2_weighted_kernel<64>);
+    if (e == hipSuccess) e = allow_lds(gemm2_weighted_kernel<128>);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  const size_t lds = gemm_lds_bytes(tile_m, I / kKB);
+  if (lds > kMaxGemmLds) return hipErrorInvalidValue;
+  const dim3 grid(grid_for(g.cap, tile_m, (H + kTN - 1) / kTN)), block(kThreads);
+#define FP8MOE_G2(TMV)                                                                                  \
+  hipLaunchKernelGGL(gemm2_weighted_kernel<TMV>, grid, block, lds, stream, q, q_scale, w2, w2_scale, \
                      topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, Y)
   switch (tile_m) {
     case 16: FP8MOE_G2(16); break;

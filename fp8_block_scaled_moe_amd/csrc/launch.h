@@ -8,6 +8,8 @@
 namespace fp8moe {
 
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxDim = 16384;             // largest H and I (token scales of a tile are staged in LDS)
+constexpr size_t kMaxGemmLds = 160 * 1024; // LDS of one gfx950 workgroup
 
 // Geometry of one grouped-GEMM launch over the padded row space.
 struct GroupedRows {
@@ -21,6 +23,9 @@ size_t route_lds_bytes(int E);
 hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int cap,
                                 int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
                                 int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream);
+
+// Dynamic LDS of a grouped-GEMM launch with tile_m rows and KT K steps.
+size_t gemm_lds_bytes(int tile_m, int KT);
 
 // GEMM1 + SwiGLU + 1x128 requant.  tile_m in {16, 32, 64, 128}.
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,

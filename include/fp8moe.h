@@ -51,9 +51,11 @@ extern "C" {
 #define FP8MOE_ERR_TILE        -5  /* tile_m / tile_n / variant not supported         */
 #define FP8MOE_ERR_WORKSPACE   -6  /* workspace NULL, too small or not 256-B aligned  */
 #define FP8MOE_ERR_HIP         -7  /* a HIP runtime call or kernel launch failed      */
-#define FP8MOE_ERR_LIMIT       -8  /* beyond a library limit (E > FP8MOE_MAX_EXPERTS) */
+#define FP8MOE_ERR_LIMIT       -8  /* beyond a library limit (E > FP8MOE_MAX_EXPERTS,
+                                      H or I > FP8MOE_MAX_DIM)                        */
 
 #define FP8MOE_MAX_EXPERTS   1024
+#define FP8MOE_MAX_DIM      16384  /* largest H and I */
 
 /* Text for a status code (static storage). */
 const char* moe_status_string(int status);
@@ -113,7 +115,8 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *            MFMA side); applies to both GEMMs when given
  *   tile_n   -1 (auto) or 256: GEMM2 output columns per tile (GEMM1 always
  *            covers 128 columns of I, one requantisation block, per tile)
- * Requires H % 128 == 0, I % 128 == 0, 1 <= K <= E <= FP8MOE_MAX_EXPERTS.
+ * Requires H % 128 == 0, I % 128 == 0, H, I <= FP8MOE_MAX_DIM,
+ * 1 <= K <= E <= FP8MOE_MAX_EXPERTS.
  * T == 0 returns FP8MOE_OK and launches nothing.  Deterministic: no atomics
  * decide any value; two calls give bit-identical outputs.
  */
