@@ -12,10 +12,24 @@ The line also carries:
                 peak (5.0 PFLOP/s).
   decode        the same layer at T=64 (HBM-bound: expert weights streamed),
                 us per layer and algorithmic GB/s against 8 TB/s.
+  gated_act     the standalone SwiGLU + MXFP8 quantiser on the four shapes and
+                two input distributions, caches flushed before each call.
+  skewed        Zipf-skewed routing (H=2048, I=768, E=128, top-8) at
+                T=1/33/512/4096: auto tile vs every forced tile_m (regret).
+  stream_GBps   a plain elementwise kernel reading and writing 2 GiB each: the
+                achievable-bandwidth reference, and the kernel whose HBM
+                counters calibrate the traffic figure.
   stages        per-stage average times of both workloads.
   cpu_baseline  the CPU oracle timed on a bounded sample of prefill tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                      [--no-extras] [--profile] [--traffic-kib F,W]
+
+--profile runs only the prefill layer, its stages and the 2 GiB stream kernel
+(for rocprofv3 passes).  --traffic-kib takes GEMM1's FETCH_SIZE and WRITE_SIZE
+per dispatch and the stream kernel's (KiB, as rocprofv3 --pmc reports them:
+"gemm1_fetch,gemm1_write,stream_fetch,stream_write") and fills roofline.traffic
+with GEMM1's HBM bytes scaled by the stream kernel's known-size calibration.
 """
 
 import argparse
@@ -63,6 +77,95 @@ def event_time_ms(fn, steps, warmup):
     stop.record(s)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
+
+
+_FLUSH = None
+
+
+def flush_caches():
+    """Overwrite 512 MB so L2 and the 256 MB Infinity Cache hold nothing of the next call's inputs."""
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    _FLUSH.fill_(1)
+
+
+def cold_time_ms(fn, iters):
+    """Average ms of fn with the caches flushed before each call (flush not timed)."""
+    s = torch.cuda.current_stream()
+    total = 0.0
+    for _ in range(iters):
+        flush_caches()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+    return total / iters
+
+
+STREAM_BYTES = 2 << 30
+
+
+def stream_bandwidth_gbs(steps=5):
+    """Achievable-bandwidth reference and counter calibration: one plain elementwise
+    kernel that reads 2 GiB and writes 2 GiB (int32 bitwise not), read + write bytes."""
+    src = torch.zeros(STREAM_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = event_time_ms(lambda: torch.bitwise_not(src, out=dst), steps, 2)
+    del src, dst
+    return 2 * STREAM_BYTES / (ms * 1e-3) / 1e9
+
+
+def gated_act_bench(iters=20):
+    """SwiGLU + MXFP8 quant over the four shapes and two input distributions, caches flushed."""
+    rows = []
+    for M, N in synth.GATED_SHAPES:
+        for bs in (False, True):
+            x = synth.gated_act_input(M, N, block_scaled=bs).cuda()
+            q = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((M, N // 32), dtype=torch.uint8, device="cuda")
+            variants = (-1, 0, 1) if M * N <= (1 << 20) else (-1,)
+            for v in variants:
+                fn = lambda: fm.gated_act_fp8_quant(x, v, out=q, scale=sc)
+                fn()
+                ms = cold_time_ms(fn, iters)
+                nbytes = 4 * M * N + M * N + M * N // 32
+                rows.append({"M": M, "N": N, "inputs": "block-scaled" if bs else "unit-normal",
+                             "variant": {-1: "auto", 0: "small", 1: "large"}[v], "us": round(ms * 1e3, 2),
+                             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    return rows
+
+
+def skewed_bench(iters=10):
+    """Zipf-skewed routing, H=2048 I=768 E=128 top-8: auto tile vs every forced tile_m, caches flushed."""
+    d = synth.SKEWED_DIMS
+    w13 = synth.expert_weight_set(d["E"], 2 * d["I"], d["H"], synth.CFG_SKEWED, synth.TAG_W13, "cuda")
+    w2 = synth.expert_weight_set(d["E"], d["H"], d["I"], synth.CFG_SKEWED, synth.TAG_W2, "cuda")
+    out = []
+    for T in synth.SKEWED_TS:
+        x_q, x_s, ids, w = synth.moe_tokens(T, d["H"], d["E"], d["K"], synth.CFG_SKEWED, extra=(T,),
+                                            zipf_s=synth.ZIPF_S)
+        p = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), *w13, *w2, ids.cuda(),
+                            w.cuda())
+        ws = fm.alloc_workspace(T, d["H"], d["I"], d["E"], d["K"], "cuda")
+        o = torch.empty((T, d["H"]), dtype=torch.bfloat16, device="cuda")
+        res = {}
+        for tm in (-1, 16, 32, 64, 128):
+            fn = lambda: fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids,
+                                          p.topk_weights, out=o, workspace=ws, tile_m=tm)
+            fn()
+            res[tm] = cold_time_ms(fn, iters)
+        nbytes, active = algorithmic_bytes(p)
+        best = min(res[t] for t in (16, 32, 64, 128))
+        auto_tm = fm.select_tile(T * d["K"], d["I"], d["H"], d["E"], 256, True)[0]
+        out.append({"T": T, "active_experts": int(active), "auto_tile_m_gemm1": auto_tm,
+                    "us_auto": round(res[-1] * 1e3, 2),
+                    "us_by_tile_m": {str(t): round(res[t] * 1e3, 2) for t in (16, 32, 64, 128)},
+                    "regret": round(res[-1] / best, 3), "GBps_auto": round(nbytes / (res[-1] * 1e-3) / 1e9, 1),
+                    "TFLOPs_auto": round(6.0 * T * d["K"] * d["H"] * d["I"] / (res[-1] * 1e-3) / 1e12, 2)})
+    return out
 
 
 def algorithmic_bytes(p):
@@ -131,6 +234,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the gated-act and skewed sweeps")
+    ap.add_argument("--profile", action="store_true", help="prefill + stages + stream kernel only")
+    ap.add_argument("--traffic-kib", default=None,
+                    help="gemm1_fetch,gemm1_write,stream_fetch,stream_write (KiB per dispatch, rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
@@ -179,6 +286,21 @@ def main():
                 "per_launch": f"4*R*H*I = {g1_flop:.4g} FLOP (R=T*K={pre.T * pre.K})",
                 "avg_launch_ms": round(pst["gemm1_ms"], 4)}
 
+    if args.traffic_kib:
+        g1f, g1w, sf, sw = (float(v) for v in args.traffic_kib.split(","))
+        fetch_scale = (STREAM_BYTES / 1024.0) / sf
+        write_scale = (STREAM_BYTES / 1024.0) / sw
+        roofline["traffic"] = round(1024.0 * (g1f * fetch_scale + g1w * write_scale))
+        roofline["traffic_note"] = (f"GEMM1 HBM bytes per launch: FETCH_SIZE {g1f:.0f} KiB x {fetch_scale:.4f} + "
+                                    f"WRITE_SIZE {g1w:.0f} KiB x {write_scale:.4f} (scales: 2 GiB stream kernel's "
+                                    f"known bytes / its counter reading)")
+    if args.profile:
+        log("stream kernel (counter calibration)")
+        gbs = stream_bandwidth_gbs()
+        print(json.dumps({"profile": True, "prefill_ms": round(ms, 4), "stages_ms": pst,
+                          "stream_GBps": round(gbs, 1), "roofline": roofline}), flush=True)
+        return
+
     # ---------------- decode
     dec = problem(64, synth.CFG_LARGE, weights)
     wsd = fm.alloc_workspace(dec.T, dec.H, dec.I, dec.E, dec.K, "cuda")
@@ -208,6 +330,13 @@ def main():
         "stages_ms": pst,
         "decode": decode,
     }
+    if not args.no_extras:
+        log("stream bandwidth reference")
+        result["stream_GBps"] = round(stream_bandwidth_gbs(), 1)
+        log("gated activation + MXFP8 sweep")
+        result["gated_act"] = gated_act_bench()
+        log("skewed-routing sweep")
+        result["skewed"] = skewed_bench()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = cpu_baseline(pre)

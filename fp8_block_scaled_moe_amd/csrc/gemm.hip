@@ -96,6 +96,15 @@ __device__ __forceinline__ v8i weight_frag(const uint8_t* rowp, int kb) {
 }
 
 // Tile coordinates of workgroup blockIdx.x; false if it has no tile.
+//
+// Tiles are numbered expert-major with the M tile innermost: expert e (rows
+// [padded[e], padded[e+1]), a whole number of M tiles since segments are
+// aligned to a multiple of TM) owns tile numbers [NT*ms, NT*me) with
+// ms = padded[e]/TM, me = padded[e+1]/TM, and its tile ms*NT + j is
+// (M tile ms + j % (me-ms), N tile j / (me-ms)).  Each XCD takes a contiguous
+// range of tile numbers (workgroups are dealt to the 8 XCDs round-robin), so
+// the M tiles that share one expert's weight tile start together on one XCD
+// and read that weight tile through its L2 in step: the weights leave HBM once.
 struct TileCoord { int mt, nt, e, p0; };
 
 template <int TM>
@@ -108,20 +117,25 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
   const int slot = b / kNumXcd;
   const int L = (b % kNumXcd) * per_xcd + slot;
   if (slot >= per_xcd || L >= tiles) return false;
-  tc.mt = L / NT;
-  tc.nt = L - tc.mt * NT;
-  tc.p0 = tc.mt * TM;
-  if (sorted_src[tc.p0] < 0) return false;  // segment padding only: nothing to compute
-  // expert owning row p0 = (number of e in [0, E) with padded[e] <= p0) - 1:
-  // padded is non-decreasing, so those e form a prefix.  One round of
+  // Expert ranges start at multiples of NT, so the expert owning tile number L
+  // owns row (L / NT) * TM: e = (number of e' in [0, E) with padded[e'] <= that
+  // row) - 1 (padded is non-decreasing, those e' form a prefix).  One round of
   // coalesced loads and a wave sum instead of a chain of dependent loads.
+  const int prow = (L / NT) * TM;
   const int lane = threadIdx.x & 63;
   int cnt = 0;
-  for (int e = lane; e < E; e += 64) cnt += padded[e] <= tc.p0 ? 1 : 0;
+  for (int e = lane; e < E; e += 64) cnt += padded[e] <= prow ? 1 : 0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-  tc.e = __builtin_amdgcn_readfirstlane(cnt - 1);
-  return true;
+  const int e = __builtin_amdgcn_readfirstlane(cnt - 1);
+  const int ms = padded[e] / TM;
+  const int nm = padded[e + 1] / TM - ms;   // >= 1: the expert owns tile L
+  const int j = L - NT * ms;
+  tc.nt = j / nm;
+  tc.mt = ms + (j - tc.nt * nm);
+  tc.p0 = tc.mt * TM;
+  tc.e = e;
+  return sorted_src[tc.p0] >= 0;  // false: segment padding only, nothing to compute
 }
 
 // Per-tile description of the operands the main loop streams.
