@@ -196,7 +196,7 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
   hipError_t err = launch_route_permute(topk_ids, (int)R, E, align, (int)cap, counts, m_indptr, padded,
                                         sorted_src, src_to_sorted, s);
   if (err != hipSuccess) return hip_fail(err, "route_permute launch");
-  GroupedRows g{padded, sorted_src, cap, E, K};
+  GroupedRows g{padded, sorted_src, cap, E, K, R, device_num_cu()};
   err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
                      g, H, I, q, q_scale, tm1, s);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
@@ -223,7 +223,7 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13,
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
   while (align % tm) tm >>= 1;
-  GroupedRows g{padded_indptr, sorted_src, cap, E, K};
+  GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
                                 w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
@@ -246,7 +246,7 @@ int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, cons
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
   while (align % tm) tm >>= 1;
-  GroupedRows g{padded_indptr, sorted_src, cap, E, K};
+  GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = launch_gemm2(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2),
                                 w2_scale, topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm, 256,
                                 (hipStream_t)stream);

@@ -8,6 +8,7 @@ namespace fp8moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr float kE4m3Max = 448.0f;
@@ -49,6 +50,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g * u / (1 + exp(-g)) on the transcendental units:
+// exp(-g) = 2^(-g log2 e) with v_exp_f32 and the reciprocal with v_rcp_f32
+// (1 ulp each).  For |g| <= 88 the result is within (2|g| + 8) * 2^-24
+// relative of the correctly rounded value (the fp32 product g log2 e carries
+// |g| 2^-23 into the exponent); for g > 88 the exponential underflows and the
+// result is g * u to three roundings; for g < -88 it overflows and the result
+// is a signed zero.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float ex = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);  // exp(-g)
+  return g * __builtin_amdgcn_rcpf(1.0f + ex) * u;
+}
 
 }  // namespace fp8moe

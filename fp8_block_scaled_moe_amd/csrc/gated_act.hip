@@ -62,11 +62,6 @@ __device__ __forceinline__ bool needs_exact(float amax) {
   return fabsf(m - 0.875f) <= 0x1p-15f;
 }
 
-// silu(g) * u on the transcendental units (error bound in the header).
-__device__ __forceinline__ float swiglu_fast(float g, float u) {
-  const float ex = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);  // exp(-g)
-  return g * __builtin_amdgcn_rcpf(1.0f + ex) * u;
-}
 
 // Group g (8 outputs) of the flat output: codes at out[8g, 8g+8), its block's
 // scale byte at scale[g / 4] (N % 32 == 0 keeps 4 groups per block and the
@@ -88,7 +83,7 @@ __device__ __forceinline__ void quant_group(const u32x4& graw, const u32x4& uraw
   float m = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    act[k] = swiglu_fast(gv[k], uv[k]);
+    act[k] = silu_mul(gv[k], uv[k]);
     m = fmaxf(m, fabsf(act[k]));
   }
   m = fmaxf(m, __shfl_xor(m, 1, 4));

@@ -17,6 +17,8 @@ struct GroupedRows {
   const int32_t* sorted_src;     // [cap]
   int64_t cap;                   // rows in the padded row space
   int E, K;                      // experts, top-k (token = src / K)
+  int64_t rows;                  // routed rows T*K (sizes the N-tile runs)
+  int num_cu;                    // compute units of the device
 };
 
 size_t route_lds_bytes(int E);
@@ -24,8 +26,8 @@ hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int
                                 int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
                                 int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream);
 
-// Dynamic LDS of a grouped-GEMM launch with tile_m rows and KT K steps.
-size_t gemm_lds_bytes(int tile_m, int KT);
+// Dynamic LDS of a grouped-GEMM launch with tile_m rows, KT K steps and runs of NB N tiles.
+size_t gemm_lds_bytes(int tile_m, int KT, int NB);
 
 // GEMM1 + SwiGLU + 1x128 requant.  tile_m in {16, 32, 64, 128}.
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
