@@ -26,13 +26,14 @@ The line also carries:
   cpu_baseline  the CPU oracle timed on a bounded sample of prefill tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                      [--no-extras] [--profile] [--traffic-kib F,W]
+                      [--no-extras] [--profile {prefill,decode,gated}] [--traffic-kib F,W,SF,SW]
 
---profile runs only the prefill layer, its stages and the 2 GiB stream kernel
-(for rocprofv3 passes).  --traffic-kib takes GEMM1's FETCH_SIZE and WRITE_SIZE
-per dispatch and the stream kernel's (KiB, as rocprofv3 --pmc reports them:
-"gemm1_fetch,gemm1_write,stream_fetch,stream_write") and fills roofline.traffic
-with GEMM1's HBM bytes scaled by the stream kernel's known-size calibration.
+--profile runs one workload only, for rocprofv3 passes: prefill (the layer,
+its stages and the 2 GiB stream kernel), decode (prefill, then the decode
+layer) or gated (the gated-act sweep).  --traffic-kib takes GEMM1's
+FETCH_SIZE and WRITE_SIZE per dispatch and the stream kernel's (KiB, as
+rocprofv3 --pmc reports them) and fills roofline.traffic from them instead of
+the readings recorded in TRAFFIC_COUNTERS.
 """
 
 import argparse
@@ -51,6 +52,38 @@ import fp8_block_scaled_moe_amd as fm  # noqa: E402
 import synth  # noqa: E402
 
 METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roofline"
+
+# HBM counters of the dominant kernel (GEMM1 at T=8192) and of the 2 GiB stream
+# kernel, KiB per dispatch, from two rocprofv3 --pmc passes of
+#   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --profile prefill --steps 2 --warmup 1
+# taken on the GEMM sources whose SHA-256 is recorded; reported as
+# roofline.traffic only while those sources are unchanged.
+TRAFFIC_COUNTERS = {
+    "gemm_sources_sha256": "337a058de330dadc03e469b627f19d52fac256f06c2f1a79a151aa3d66e8754e",
+    "gemm1_fetch_kib": 5557923, "gemm1_write_kib": 198560,
+    "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
+}
+GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm.hip", "fp8_block_scaled_moe_amd/csrc/device_common.h",
+                "fp8_block_scaled_moe_amd/csrc/launch.h")
+
+
+def gemm_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from(g1f, g1w, sf, sw):
+    """GEMM1 HBM bytes per launch: each counter scaled by the stream kernel's known bytes / its reading."""
+    fetch_scale = (STREAM_BYTES / 1024.0) / sf
+    write_scale = (STREAM_BYTES / 1024.0) / sw
+    traffic = round(1024.0 * (g1f * fetch_scale + g1w * write_scale))
+    note = (f"GEMM1 HBM bytes per launch: FETCH_SIZE {g1f:.0f} KiB x {fetch_scale:.4f} + WRITE_SIZE {g1w:.0f} KiB x "
+            f"{write_scale:.4f} (scales: the 2 GiB stream kernel's known bytes / its counter readings)")
+    return traffic, note
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
@@ -260,7 +293,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the gated-act and skewed sweeps")
-    ap.add_argument("--profile", action="store_true", help="prefill + stages + stream kernel only")
+    ap.add_argument("--profile", choices=("prefill", "decode", "gated"), default=None,
+                    help="one workload only, for rocprofv3 passes: prefill (+ stages, stream kernel), "
+                         "decode (+ stages) or gated (the gated-act sweep)")
     ap.add_argument("--traffic-kib", default=None,
                     help="gemm1_fetch,gemm1_write,stream_fetch,stream_write (KiB per dispatch, rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -269,6 +304,9 @@ def main():
         sys.exit(2)
 
     torch.cuda.init()
+    if args.profile == "gated":
+        print(json.dumps({"profile": "gated", "gated_act": gated_act_bench(iters=5)}), flush=True)
+        return
     d = synth.LARGE_DIMS
     log("generating 256-expert fp8 weights on the device")
     w13 = synth.expert_weight_set(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
@@ -311,18 +349,20 @@ def main():
                 "per_launch": f"4*R*H*I = {g1_flop:.4g} FLOP (R=T*K={pre.T * pre.K})",
                 "avg_launch_ms": round(pst["gemm1_ms"], 4)}
 
+    tc = TRAFFIC_COUNTERS
     if args.traffic_kib:
-        g1f, g1w, sf, sw = (float(v) for v in args.traffic_kib.split(","))
-        fetch_scale = (STREAM_BYTES / 1024.0) / sf
-        write_scale = (STREAM_BYTES / 1024.0) / sw
-        roofline["traffic"] = round(1024.0 * (g1f * fetch_scale + g1w * write_scale))
-        roofline["traffic_note"] = (f"GEMM1 HBM bytes per launch: FETCH_SIZE {g1f:.0f} KiB x {fetch_scale:.4f} + "
-                                    f"WRITE_SIZE {g1w:.0f} KiB x {write_scale:.4f} (scales: 2 GiB stream kernel's "
-                                    f"known bytes / its counter reading)")
-    if args.profile:
+        roofline["traffic"], roofline["traffic_note"] = traffic_from(*(float(v) for v in args.traffic_kib.split(",")))
+    elif tc["gemm1_fetch_kib"] is not None and tc["gemm_sources_sha256"] == gemm_sources_sha256():
+        roofline["traffic"], roofline["traffic_note"] = traffic_from(
+            tc["gemm1_fetch_kib"], tc["gemm1_write_kib"], tc["stream_fetch_kib"], tc["stream_write_kib"])
+    else:
+        roofline["traffic_note"] = "no counters recorded for the current GEMM sources"
+    roofline["algorithmic_bytes"] = int(pre.E * 2 * pre.I * pre.H + pre.T * pre.H + 4 * pre.T * (pre.H // 128)
+                                        + pre.T * pre.K * pre.I + 4 * pre.T * pre.K * (pre.I // 128))
+    if args.profile == "prefill":
         log("stream kernel (counter calibration)")
         gbs = stream_bandwidth_gbs()
-        print(json.dumps({"profile": True, "prefill_ms": round(ms, 4), "stages_ms": pst,
+        print(json.dumps({"profile": "prefill", "prefill_ms": round(ms, 4), "stages_ms": pst,
                           "stream_GBps": round(gbs, 1), "roofline": roofline}), flush=True)
         return
 
@@ -340,6 +380,9 @@ def main():
     decode = {"us_per_layer": round(dms * 1e3, 2), "GBps": round(dgbs, 1), "frac_hbm": round(dgbs / PEAK_HBM_GBS, 4),
               "algorithmic_bytes": dbytes, "active_experts": int(dactive), "stages_ms": dst,
               "workload": "decode T=64 H=7168 I=2048 E=256 top-8"}
+    if args.profile == "decode":
+        print(json.dumps({"profile": "decode", "decode": decode}), flush=True)
+        return
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
