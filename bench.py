@@ -92,12 +92,24 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def problem(T, cfg, weights):
+def problem(T, cfg, weights, packed=None):
+    """A problem on the device; packed = (w13, w2) in the MFMA-tiled layout, kept beside the row-major ones."""
     d = synth.LARGE_DIMS
     x_q, x_s, ids, w = synth.moe_tokens(T, d["H"], d["E"], d["K"], cfg)
     w13_q, w13_s, w2_q, w2_s = weights
-    return synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), w13_q, w13_s, w2_q, w2_s,
-                           ids.cuda(), w.cuda())
+    p = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), w13_q, w13_s, w2_q, w2_s,
+                        ids.cuda(), w.cuda())
+    p.w13_p, p.w2_p = packed if packed is not None else (None, None)
+    return p
+
+
+def fused(p, out, ws, packed=True, tile_m=-1):
+    """One layer call: packed weights (the production layout) or the row-major ones."""
+    if packed:
+        return fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_p, p.w13_s, p.w2_p, p.w2_s, p.topk_ids, p.topk_weights,
+                                out=out, workspace=ws, tile_m=tile_m, weight_layout=fm.WEIGHTS_MFMA_TILED)
+    return fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids, p.topk_weights,
+                            out=out, workspace=ws, tile_m=tile_m)
 
 
 def event_time_ms(fn, steps, warmup):
@@ -201,18 +213,19 @@ def skewed_bench(iters=10):
     d = synth.SKEWED_DIMS
     w13 = synth.expert_weight_set(d["E"], 2 * d["I"], d["H"], synth.CFG_SKEWED, synth.TAG_W13, "cuda")
     w2 = synth.expert_weight_set(d["E"], d["H"], d["I"], synth.CFG_SKEWED, synth.TAG_W2, "cuda")
+    packed = (fm.pack_weights(w13[0]), fm.pack_weights(w2[0]))
     out = []
     for T in synth.SKEWED_TS:
         x_q, x_s, ids, w = synth.moe_tokens(T, d["H"], d["E"], d["K"], synth.CFG_SKEWED, extra=(T,),
                                             zipf_s=synth.ZIPF_S)
         p = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), *w13, *w2, ids.cuda(),
                             w.cuda())
+        p.w13_p, p.w2_p = packed
         ws = fm.alloc_workspace(T, d["H"], d["I"], d["E"], d["K"], "cuda")
         o = torch.empty((T, d["H"]), dtype=torch.bfloat16, device="cuda")
         res = {}
         for tm in (-1, 16, 32, 64, 128):
-            fn = lambda: fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids,
-                                          p.topk_weights, out=o, workspace=ws, tile_m=tm)
+            fn = lambda: fused(p, o, ws, tile_m=tm)
             fn()
             res[tm] = cold_time_ms(fn, iters)
         nbytes, active = algorithmic_bytes(p)
@@ -242,21 +255,22 @@ def layer_flops(p):
 
 
 def stage_times(p, steps, warmup):
-    """Average time of each stage launched on its own (same kernels and tiles as the fused call)."""
+    """Average time of each stage launched on its own (same kernels, tiles and weight layout as the fused call)."""
     T, H, I, E, K = p.T, p.H, p.I, p.E, p.K
     R = T * K
     tm1, _ = fm.select_tile(R, I, H, E, 256, True)
     tm2, _ = fm.select_tile(R, H, I, E, 256, False)
     align = max(tm1, tm2)
+    L = fm.WEIGHTS_MFMA_TILED
     route = fm.route_permute(p.topk_ids, E, align)
-    q, qs = fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_q, p.w13_s, route, T, K, align, tile_m=tm1)
-    Y = fm.gemm2_weighted(q, qs, p.w2_q, p.w2_s, route, p.topk_weights, T, K, align, tile_m=tm2)
+    q, qs = fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_p, p.w13_s, route, T, K, align, tile_m=tm1, weight_layout=L)
+    Y = fm.gemm2_weighted(q, qs, p.w2_p, p.w2_s, route, p.topk_weights, T, K, align, tile_m=tm2, weight_layout=L)
     out = {
         "route_ms": event_time_ms(lambda: fm.route_permute(p.topk_ids, E, align), steps, warmup),
-        "gemm1_ms": event_time_ms(lambda: fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_q, p.w13_s, route, T, K, align,
-                                                                tile_m=tm1), steps, warmup),
-        "gemm2_ms": event_time_ms(lambda: fm.gemm2_weighted(q, qs, p.w2_q, p.w2_s, route, p.topk_weights, T, K,
-                                                            align, tile_m=tm2), steps, warmup),
+        "gemm1_ms": event_time_ms(lambda: fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_p, p.w13_s, route, T, K, align,
+                                                                tile_m=tm1, weight_layout=L), steps, warmup),
+        "gemm2_ms": event_time_ms(lambda: fm.gemm2_weighted(q, qs, p.w2_p, p.w2_s, route, p.topk_weights, T, K,
+                                                            align, tile_m=tm2, weight_layout=L), steps, warmup),
         "combine_ms": event_time_ms(lambda: fm.combine(Y, p.topk_ids, E), steps, warmup),
         "tile_m_gemm1": tm1, "tile_m_gemm2": tm2,
     }
@@ -312,13 +326,19 @@ def main():
     w13 = synth.expert_weight_set(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
     w2 = synth.expert_weight_set(d["E"], d["H"], d["I"], synth.CFG_LARGE, synth.TAG_W2, "cuda")
     weights = (*w13, *w2)
+    # the production weight layout: packed once per weight set (a load-time transform, outside the step)
+    torch.cuda.synchronize()
+    tp = time.perf_counter()
+    packed = (fm.pack_weights(w13[0]), fm.pack_weights(w2[0]))
+    torch.cuda.synchronize()
+    pack_ms = (time.perf_counter() - tp) * 1e3
+    log(f"packed 11.3 GB of expert weights in {pack_ms:.1f} ms")
 
     # ---------------- prefill (headline)
-    pre = problem(8192, synth.CFG_PREFILL, weights)
+    pre = problem(8192, synth.CFG_PREFILL, weights, packed)
     ws = fm.alloc_workspace(pre.T, pre.H, pre.I, pre.E, pre.K, "cuda")
     out = torch.empty((pre.T, pre.H), dtype=torch.bfloat16, device="cuda")
-    step = lambda: fm.moe_fused_fp8(pre.x_q, pre.x_s, pre.w13_q, pre.w13_s, pre.w2_q, pre.w2_s, pre.topk_ids,
-                                    pre.topk_weights, out=out, workspace=ws)
+    step = lambda: fused(pre, out, ws)
     log(f"prefill: warmup {args.warmup}, timing {args.steps} steps")
     for _ in range(args.warmup):
         step()
@@ -339,13 +359,15 @@ def main():
     log(f"prefill {ms * 1e3:.1f} us/layer, {tflops:.1f} TFLOP/s (wall {wall:.2f}s)")
     pst = stage_times(pre, max(3, args.steps // 2), 1)
     log("prefill stages", pst)
+    ms_rm = event_time_ms(lambda: fused(pre, out, ws, packed=False), max(3, args.steps // 2), 1)
+    log(f"prefill with row-major weights {ms_rm * 1e3:.1f} us/layer")
 
     # dominant kernel: GEMM1 (+SwiGLU+requant) -- 4*R*H*I algorithmic FLOP per launch
     g1_flop = 4.0 * pre.T * pre.K * pre.H * pre.I
     g1_tflops = g1_flop / (pst["gemm1_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(g1_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g1_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                "kernel": f"gemm1_swiglu_quant_kernel<{pst['tile_m_gemm1']}>",
+                "kernel": f"gemm1_swiglu_quant_kernel<{pst['tile_m_gemm1']}, true> (MFMA-tiled weights)",
                 "per_launch": f"4*R*H*I = {g1_flop:.4g} FLOP (R=T*K={pre.T * pre.K})",
                 "avg_launch_ms": round(pst["gemm1_ms"], 4)}
 
@@ -367,11 +389,10 @@ def main():
         return
 
     # ---------------- decode
-    dec = problem(64, synth.CFG_LARGE, weights)
+    dec = problem(64, synth.CFG_LARGE, weights, packed)
     wsd = fm.alloc_workspace(dec.T, dec.H, dec.I, dec.E, dec.K, "cuda")
     outd = torch.empty((dec.T, dec.H), dtype=torch.bfloat16, device="cuda")
-    dstep = lambda: fm.moe_fused_fp8(dec.x_q, dec.x_s, dec.w13_q, dec.w13_s, dec.w2_q, dec.w2_s, dec.topk_ids,
-                                     dec.topk_weights, out=outd, workspace=wsd)
+    dstep = lambda: fused(dec, outd, wsd)
     dms = event_time_ms(dstep, max(args.steps, 10), args.warmup)
     dbytes, dactive = algorithmic_bytes(dec)
     dgbs = dbytes / (dms * 1e-3) / 1e9
@@ -390,8 +411,11 @@ def main():
         "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
         "config": {"workload": "prefill T=8192 H=7168 I=2048 E=256 top-8, fp8 e4m3 W8A8 (1x128 act, 128x128 weight "
                                "scales), bf16 out", "T": pre.T, "H": pre.H, "I": pre.I, "E": pre.E, "K": pre.K,
-                   "tile_m_gemm1": pst["tile_m_gemm1"], "tile_m_gemm2": pst["tile_m_gemm2"]},
+                   "tile_m_gemm1": pst["tile_m_gemm1"], "tile_m_gemm2": pst["tile_m_gemm2"],
+                   "weights": "MFMA-tiled layout (moe_pack_weights, once per weight set, outside the step)"},
         "us_per_layer": round(ms * 1e3, 2),
+        "us_per_layer_row_major_weights": round(ms_rm * 1e3, 2),
+        "pack_weights_ms": round(pack_ms, 2),
         "frac_mfma_layer": round(tflops / PEAK_FP8_TFLOPS, 4),
         "prefill_GBps": round(pre_bytes / (ms * 1e-3) / 1e9, 1),
         "roofline": roofline,

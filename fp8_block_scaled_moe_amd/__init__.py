@@ -9,5 +9,5 @@ from ._lib import lib, Fp8MoeError, LIB_PATH  # noqa: F401
 from .ops import (  # noqa: F401
     route_capacity, route_permute, fused_workspace_size, alloc_workspace, moe_fused_fp8,
     gemm1_swiglu_quant, gemm2_weighted, combine, gated_act_fp8_quant, select_tile,
-    select_tile_classes,
+    select_tile_classes, pack_weights, WEIGHTS_ROW_MAJOR, WEIGHTS_MFMA_TILED,
 )

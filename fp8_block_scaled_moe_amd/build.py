@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8moe.so")
 
-SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm.hip", "combine.hip", "gated_act.hip"]
+SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm.hip", "combine.hip", "gated_act.hip", "pack.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

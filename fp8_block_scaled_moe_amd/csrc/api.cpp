@@ -41,6 +41,7 @@ int hip_fail(hipError_t err, const char* what) {
 
 bool valid_tile_m(int t) { return t == 16 || t == 32 || t == 64 || t == 128; }
 bool valid_align(int a) { return a == 16 || a == 32 || a == 64 || a == 128; }
+bool valid_layout(int l) { return l == FP8MOE_WEIGHTS_ROW_MAJOR || l == FP8MOE_WEIGHTS_MFMA_TILED; }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 constexpr size_t kAlignWs = 256;
@@ -161,9 +162,11 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
                   const void* w2, const float* w2_scale, const int32_t* topk_ids,
                   const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                   void* out, void* workspace, size_t workspace_bytes, int32_t tile_m, int32_t tile_n,
-                  void* stream) {
+                  int32_t weight_layout, void* stream) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
+  const bool packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
   if (tile_m != -1 && !valid_tile_m(tile_m))
     return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
   if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
@@ -198,10 +201,10 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
   if (err != hipSuccess) return hip_fail(err, "route_permute launch");
   GroupedRows g{padded, sorted_src, cap, E, K, R, device_num_cu()};
   err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
-                     g, H, I, q, q_scale, tm1, s);
+                     g, H, I, q, q_scale, tm1, packed, s);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
   err = launch_gemm2(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2,
-                     256, s);
+                     256, packed, s);
   if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
   err = launch_combine(Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
@@ -211,9 +214,10 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
 int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
                            const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
                            int32_t I, int32_t E, int32_t K, int32_t align, void* q, float* q_scale,
-                           int64_t cap, int32_t tile_m, void* stream) {
+                           int64_t cap, int32_t tile_m, int32_t weight_layout, void* stream) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   if (tile_m != -1 && (!valid_tile_m(tile_m) || align % tile_m))
     return fail(FP8MOE_ERR_TILE, "tile_m %d must be in {16,32,64,128} and divide align %d", tile_m, align);
@@ -225,7 +229,8 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13,
   while (align % tm) tm >>= 1;
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
-                                w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm, (hipStream_t)stream);
+                                w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
+                                weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
   return ok();
 }
@@ -233,9 +238,10 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13,
 int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, const float* w2_scale,
                        const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
                        int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y,
-                       int64_t cap, int32_t tile_m, int32_t tile_n, void* stream) {
+                       int64_t cap, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   if (tile_m != -1 && (!valid_tile_m(tile_m) || align % tile_m))
     return fail(FP8MOE_ERR_TILE, "tile_m %d must be in {16,32,64,128} and divide align %d", tile_m, align);
@@ -249,8 +255,21 @@ int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, cons
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = launch_gemm2(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2),
                                 w2_scale, topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm, 256,
-                                (hipStream_t)stream);
+                                weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
+  return ok();
+}
+
+int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {
+  if (E < 1 || N <= 0 || K <= 0 || N % 16 || K % 128)
+    return fail(FP8MOE_ERR_SHAPE, "pack needs E >= 1, N %% 16 == 0, K %% 128 == 0 (E=%lld N=%d K=%d)",
+                (long long)E, N, K);
+  if (!in || !out) return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out, n = (uintptr_t)(E * (int64_t)N * K);
+  if (a < b + n && b < a + n) return fail(FP8MOE_ERR_SHAPE, "pack in and out overlap");
+  hipError_t err = launch_pack_weights(static_cast<const uint8_t*>(in), E, N, K, static_cast<uint8_t*>(out),
+                                       (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "pack_weights launch");
   return ok();
 }
 

@@ -86,10 +86,14 @@ __device__ __forceinline__ v8i join(const v4i& lo, const v4i& hi) {
   return o;
 }
 
-// Weight operand: rowp = start of the lane's weight row + 16*g.
-__device__ __forceinline__ v8i weight_frag(const uint8_t* rowp, int kb) {
-  const uint8_t* p = rowp + (size_t)kb * kKB;
-  return join(*reinterpret_cast<const v4i*>(p), *reinterpret_cast<const v4i*>(p + 64));
+// Weight operand of K step kb.  Row-major weights: wp = the lane's weight row
+// + 16*g, two 16-byte loads 64 bytes apart (a wave's load touches 16 rows).
+// MFMA-tiled weights: wp = the 16-row band + 16*lane, two 1 KB-contiguous
+// wave loads per 2 KB block (the layout of pack.hip).
+template <bool PACKED>
+__device__ __forceinline__ v8i weight_frag(const uint8_t* wp, int kb) {
+  const uint8_t* p = wp + (size_t)kb * (PACKED ? 2048 : kKB);
+  return join(*reinterpret_cast<const v4i*>(p), *reinterpret_cast<const v4i*>(p + (PACKED ? 1024 : 64)));
 }
 
 // Work of workgroup blockIdx.x: one M tile and a run of up to NB consecutive
@@ -235,9 +239,9 @@ struct Lds {
 // of step j + 4 are fetched at step j whatever N tile they belong to, so the
 // pipeline does not drain between the N tiles of a run.
 //
-// wrow(n, w) gives the lane's weight row pointer (+16*g) of sub-tile w in N
-// tile n at K step 0.
-template <int TM, bool GATED, typename WRow, typename Epi>
+// wrow(n, w) gives the lane's weight pointer of sub-tile w in N tile n at K
+// step 0 (weight_frag's wp).
+template <int TM, bool GATED, bool PACKED, typename WRow, typename Epi>
 __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const (&a_src)[Cfg<TM>::A_PER_THREAD],
                                             int sb_sel, int KT, int nn, int tid, int lane,
                                             v4f (&acc)[Cfg<TM>::TS][2], WRow wrow, Epi epi) {
@@ -265,7 +269,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   const uint8_t* wp[2] = {wrow(0, 0), wrow(0, 1)};
   auto load_w = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag(wp[w], kw);
+    for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wp[w], kw);
     if (++kw == KT) {
       kw = 0;
       if (++nw < nn) {
@@ -423,7 +427,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
 
 // ------------------------------------------------------------------------------------------
 // GEMM1 + SwiGLU + 1x128 FP8 requantisation over a run of N tiles of 128 I columns.
-template <int TM>
+template <int TM, bool PACKED>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
     const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
     const float* __restrict__ w13_scale, const int32_t* __restrict__ padded,
@@ -459,8 +463,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
   const float* sexp = w13_scale + (size_t)tc.e * (2 * IB) * HB;
   auto wrow = [&](int n, int w) -> const uint8_t* {
-    const int c = 128 * (nt0 + n) + 16 * wave + l16;
-    return wexp + (size_t)(w ? I + c : c) * H + 16 * g;
+    const int c = 128 * (nt0 + n) + 16 * wave;   // first row of the 16-row band
+    if constexpr (PACKED) return wexp + (size_t)(w ? I + c : c) * H + 16 * lane;
+    else return wexp + (size_t)((w ? I + c : c) + l16) * H + 16 * g;
   };
   stage_weight_scales(SBs, KT, nn, [&](int n, int which) -> const float* {
     return sexp + (size_t)(which ? IB + nt0 + n : nt0 + n) * HB;
@@ -511,12 +516,12 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, true>(smem, a_src, 0, KT, nn, tid, lane, acc, wrow, epi);
+  ws_mainloop<TM, true, PACKED>(smem, a_src, 0, KT, nn, tid, lane, acc, wrow, epi);
 }
 
 // ------------------------------------------------------------------------------------------
 // GEMM2 with the top-k weight epilogue, over a run of N tiles of 256 H columns.
-template <int TM>
+template <int TM, bool PACKED>
 __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ w2,
     const float* __restrict__ w2_scale, const float* __restrict__ topk_weights,
@@ -551,8 +556,10 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   // its two operands 16 columns each; rows past H read a valid row, outputs masked
   const uint8_t* wexp = w2 + (size_t)tc.e * H * (size_t)I;
   auto wrow = [&](int n, int w) -> const uint8_t* {
-    const int row = min(kTN * (nt0 + n) + 32 * wave + 16 * w + l16, H - 1);
-    return wexp + (size_t)row * I + 16 * g;
+    // bands past H (the last N tile when H % 256 == 128) read the last band
+    const int band = min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16);
+    if constexpr (PACKED) return wexp + (size_t)band * I + 16 * lane;
+    else return wexp + (size_t)(band + l16) * I + 16 * g;
   };
   // N tile n spans scale blocks 2(nt0+n) and 2(nt0+n)+1 (the second clamped
   // at the last block; only columns < H are stored); waves 4..7 use the second
@@ -596,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, false>(smem, a_src, wave >> 2, KT, nn, tid, lane, acc, wrow, epi);
+  ws_mainloop<TM, false, PACKED>(smem, a_src, wave >> 2, KT, nn, tid, lane, acc, wrow, epi);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -656,12 +663,14 @@ static hipError_t allow_lds(Kern k) {
 
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
                         const float* w13_scale, const GroupedRows& g, int H, int I,
-                        uint8_t* q, float* q_scale, int tile_m, hipStream_t stream) {
+                        uint8_t* q, float* q_scale, int tile_m, bool packed, hipStream_t stream) {
   static const hipError_t attr = [] {
-    hipError_t e = allow_lds(gemm1_swiglu_quant_kernel<16>);
-    if (e == hipSuccess) e = allow_lds(gemm1_swiglu_quant_kernel<32>);
-    if (e == hipSuccess) e = allow_lds(gemm1_swiglu_quant_kernel<64>);
-    if (e == hipSuccess) e = allow_lds(gemm1_swiglu_quant_kernel<128>);
+    hipError_t e = hipSuccess;
+    for (auto k : {gemm1_swiglu_quant_kernel<16, false>, gemm1_swiglu_quant_kernel<32, false>,
+                   gemm1_swiglu_quant_kernel<64, false>, gemm1_swiglu_quant_kernel<128, false>,
+                   gemm1_swiglu_quant_kernel<16, true>, gemm1_swiglu_quant_kernel<32, true>,
+                   gemm1_swiglu_quant_kernel<64, true>, gemm1_swiglu_quant_kernel<128, true>})
+      if (e == hipSuccess) e = allow_lds(k);
     return e;
   }();
   if (attr != hipSuccess) return attr;
@@ -669,9 +678,13 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
   const size_t lds = gemm_lds_bytes(tile_m, H / kKB, NB);
   if (lds > kMaxGemmLds) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g.cap, tile_m, NG)), block(kThreads);
-#define FP8MOE_G1(TMV)                                                                          \
-  hipLaunchKernelGGL(gemm1_swiglu_quant_kernel<TMV>, grid, block, lds, stream, x, x_scale, w13, \
-                     w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale)
+#define FP8MOE_G1(TMV)                                                                                 \
+  if (packed)                                                                                          \
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, true>), grid, block, lds, stream, x, x_scale, w13, \
+                       w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale);       \
+  else                                                                                                 \
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, false>), grid, block, lds, stream, x, x_scale, w13, \
+                       w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale)
   switch (tile_m) {
     case 16: FP8MOE_G1(16); break;
     case 32: FP8MOE_G1(32); break;
@@ -685,13 +698,15 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
 
 hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w2,
                         const float* w2_scale, const float* topk_weights, const GroupedRows& g,
-                        int H, int I, uint16_t* Y, int tile_m, int tile_n, hipStream_t stream) {
+                        int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream) {
   if (tile_n != kTN) return hipErrorInvalidValue;
   static const hipError_t attr = [] {
-    hipError_t e = allow_lds(gemm2_weighted_kernel<16>);
-    if (e == hipSuccess) e = allow_lds(gemm2_weighted_kernel<32>);
-    if (e == hipSuccess) e = allow_lds(gemm2_weighted_kernel<64>);
-    if (e == hipSuccess) e = allow_lds(gemm2_weighted_kernel<128>);
+    hipError_t e = hipSuccess;
+    for (auto k : {gemm2_weighted_kernel<16, false>, gemm2_weighted_kernel<32, false>,
+                   gemm2_weighted_kernel<64, false>, gemm2_weighted_kernel<128, false>,
+                   gemm2_weighted_kernel<16, true>, gemm2_weighted_kernel<32, true>,
+                   gemm2_weighted_kernel<64, true>, gemm2_weighted_kernel<128, true>})
+      if (e == hipSuccess) e = allow_lds(k);
     return e;
   }();
   if (attr != hipSuccess) return attr;
@@ -699,9 +714,13 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
   const size_t lds = gemm_lds_bytes(tile_m, I / kKB, NB);
   if (lds > kMaxGemmLds) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g.cap, tile_m, NG)), block(kThreads);
-#define FP8MOE_G2(TMV)                                                                                  \
-  hipLaunchKernelGGL(gemm2_weighted_kernel<TMV>, grid, block, lds, stream, q, q_scale, w2, w2_scale, \
-                     topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y)
+#define FP8MOE_G2(TMV)                                                                                    \
+  if (packed)                                                                                             \
+    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, true>), grid, block, lds, stream, q, q_scale, w2, w2_scale, \
+                       topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y);                    \
+  else                                                                                                    \
+    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, false>), grid, block, lds, stream, q, q_scale, w2,       \
+                       w2_scale, topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y)
   switch (tile_m) {
     case 16: FP8MOE_G2(16); break;
     case 32: FP8MOE_G2(32); break;

@@ -29,15 +29,19 @@ hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int
 // Dynamic LDS of a grouped-GEMM launch with tile_m rows, KT K steps and runs of NB N tiles.
 size_t gemm_lds_bytes(int tile_m, int KT, int NB);
 
-// GEMM1 + SwiGLU + 1x128 requant.  tile_m in {16, 32, 64, 128}.
+// GEMM1 + SwiGLU + 1x128 requant.  tile_m in {16, 32, 64, 128}; packed: w13
+// in the MFMA-tiled layout of launch_pack_weights, else row-major.
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
                         const float* w13_scale, const GroupedRows& g, int H, int I,
-                        uint8_t* q, float* q_scale, int tile_m, hipStream_t stream);
+                        uint8_t* q, float* q_scale, int tile_m, bool packed, hipStream_t stream);
 
 // GEMM2 with the top-k weight epilogue, Y indexed by source row.  tile_m in {16, 32, 64, 128}.
 hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w2,
                         const float* w2_scale, const float* topk_weights, const GroupedRows& g,
-                        int H, int I, uint16_t* Y, int tile_m, int tile_n, hipStream_t stream);
+                        int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream);
+
+// Row-major e4m3 [E][N][K] -> MFMA-tiled layout (N % 16 == 0, K % 128 == 0).
+hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* Y, const int32_t* topk_ids, int T, int H, int E, int K,
                           uint16_t* out, hipStream_t stream);

@@ -77,9 +77,28 @@ def alloc_workspace(T, H, I, E, K, device):
     return torch.empty(fused_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
 
 
+WEIGHTS_ROW_MAJOR, WEIGHTS_MFMA_TILED = 0, 1
+
+
+def pack_weights(w, out=None):
+    """Expert weights e4m3 [E, N, K] row-major -> the MFMA-tiled layout (same shape and byte
+    count, bytes permuted; see moe_pack_weights in include/fp8moe.h)."""
+    w = _u8(w)
+    _need(w, torch.uint8, "w", 3)
+    E, N, K = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _need(out, torch.uint8, "out", 3)
+    if tuple(out.shape) != (E, N, K):
+        raise ValueError("out must have the shape of w")
+    check(lib().moe_pack_weights(_p(w), E, N, K, _p(out), _stream(w.device)))
+    return out
+
+
 def moe_fused_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
-                  out=None, workspace=None, tile_m=-1, tile_n=-1):
-    """Fused W8A8 FP8 block-scaled MoE layer.  Returns bf16 [T, H]."""
+                  out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
+    """Fused W8A8 FP8 block-scaled MoE layer.  Returns bf16 [T, H].  weight_layout 1: w13 and w2
+    packed by pack_weights (same shapes)."""
     x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
     _need(x, torch.uint8, "x", 2)
     _need(x_scale, torch.float32, "x_scale", 2)
@@ -108,11 +127,13 @@ def moe_fused_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weigh
         workspace = alloc_workspace(T, H, I, E, K, dev)
     check(lib().moe_fused_fp8(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
                               _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
-                              workspace.numel() * workspace.element_size(), tile_m, tile_n, _stream(dev)))
+                              workspace.numel() * workspace.element_size(), tile_m, tile_n, weight_layout,
+                              _stream(dev)))
     return out
 
 
-def gemm1_swiglu_quant(x, x_scale, w13, w13_scale, route, T, K, align, tile_m=-1):
+def gemm1_swiglu_quant(x, x_scale, w13, w13_scale, route, T, K, align, tile_m=-1,
+                       weight_layout=WEIGHTS_ROW_MAJOR):
     """GEMM1 + SwiGLU + requant stage over a routing result.  Returns (q uint8 [cap, I], q_scale [cap, I/128])."""
     x, w13 = _u8(x), _u8(w13)
     E, I2, H = w13.shape
@@ -123,11 +144,12 @@ def gemm1_swiglu_quant(x, x_scale, w13, w13_scale, route, T, K, align, tile_m=-1
     qs = torch.zeros((cap, I // 128), dtype=torch.float32, device=dev)
     check(lib().moe_gemm1_swiglu_quant(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(route["padded_indptr"]),
                                        _p(route["sorted_src"]), T, H, I, E, K, align, _p(q), _p(qs), cap, tile_m,
-                                       _stream(dev)))
+                                       weight_layout, _stream(dev)))
     return q, qs
 
 
-def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1):
+def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
+                   weight_layout=WEIGHTS_ROW_MAJOR):
     """GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H] (rows of dropped slots are zero here)."""
     w2 = _u8(w2)
     E, H, I = w2.shape
@@ -136,7 +158,7 @@ def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, t
     Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev)
     check(lib().moe_gemm2_weighted(_p(q), _p(q_scale), _p(w2), _p(w2_scale), _p(route["padded_indptr"]),
                                    _p(route["sorted_src"]), _p(topk_weights), T, H, I, E, K, align, _p(Y), cap,
-                                   tile_m, tile_n, _stream(dev)))
+                                   tile_m, tile_n, weight_layout, _stream(dev)))
     return Y
 
 

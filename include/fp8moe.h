@@ -57,6 +57,10 @@ extern "C" {
 #define FP8MOE_MAX_EXPERTS   1024
 #define FP8MOE_MAX_DIM      16384  /* largest H and I */
 
+/* Expert-weight layouts accepted by the GEMMs (weight_layout arguments). */
+#define FP8MOE_WEIGHTS_ROW_MAJOR  0   /* [E, N, K] row-major, K contiguous         */
+#define FP8MOE_WEIGHTS_MFMA_TILED 1   /* moe_pack_weights' layout, same byte count */
+
 /* Text for a status code (static storage). */
 const char* moe_status_string(int status);
 /* Message of the last failure on the calling thread ("" if none). */
@@ -115,6 +119,9 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *            MFMA side); applies to both GEMMs when given
  *   tile_n   -1 (auto) or 256: GEMM2 output columns per tile (GEMM1 always
  *            covers 128 columns of I, one requantisation block, per tile)
+ *   weight_layout  FP8MOE_WEIGHTS_ROW_MAJOR (w13, w2 as above) or
+ *            FP8MOE_WEIGHTS_MFMA_TILED (both packed by moe_pack_weights; the
+ *            scales keep their layout); results are bit-identical
  * Requires H % 128 == 0, I % 128 == 0, H, I <= FP8MOE_MAX_DIM,
  * 1 <= K <= E <= FP8MOE_MAX_EXPERTS.
  * T == 0 returns FP8MOE_OK and launches nothing.  Deterministic: no atomics
@@ -128,7 +135,7 @@ int moe_fused_fp8(const void* x, const float* x_scale,
                   const int32_t* topk_ids, const float* topk_weights,
                   int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                   void* out, void* workspace, size_t workspace_bytes,
-                  int32_t tile_m, int32_t tile_n, void* stream);
+                  int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream);
 
 /* ---------------------------------------------------------------- stages of the fused layer
  * The three compute stages moe_fused_fp8 runs after routing, exposed so each
@@ -159,15 +166,30 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale,
                            const int32_t* padded_indptr, const int32_t* sorted_src,
                            int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
                            void* q, float* q_scale, int64_t cap,
-                           int32_t tile_m, void* stream);
+                           int32_t tile_m, int32_t weight_layout, void* stream);
 int moe_gemm2_weighted(const void* q, const float* q_scale,
                        const void* w2, const float* w2_scale,
                        const int32_t* padded_indptr, const int32_t* sorted_src,
                        const float* topk_weights,
                        int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
-                       void* Y, int64_t cap, int32_t tile_m, int32_t tile_n, void* stream);
+                       void* Y, int64_t cap, int32_t tile_m, int32_t tile_n,
+                       int32_t weight_layout, void* stream);
 int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E,
                 int32_t K, void* out, void* stream);
+
+/* ---------------------------------------------------------------- weight packing
+ * moe_pack_weights: expert weights e4m3 [E, N, K] row-major (w13 with N = 2I,
+ * K = H, or w2 with N = H, K = I) -> FP8MOE_WEIGHTS_MFMA_TILED, the layout
+ * the GEMMs read with one contiguous 1 KB load per wave and instruction:
+ *   out[e][b][kb][h][l][0..15] = in[e][16b + l%16][128kb + 64h + 16(l/16) + 0..15]
+ * for 16-row band b, 128-wide K block kb, half h in {0, 1}, lane l in [0, 64).
+ * A byte permutation of the same size, done once per weight set (the path's
+ * own data layout choice: the pages' kernels read row-major weights).
+ * Requires E >= 1, N % 16 == 0, K % 128 == 0, in and out non-NULL and not
+ * overlapping (FP8MOE_ERR_SHAPE otherwise); out is caller-owned device memory
+ * of E*N*K bytes.  Asynchronous on `stream`.
+ */
+int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out, void* stream);
 
 /* ---------------------------------------------------------------- gated activation + MXFP8
  * SwiGLU + MXFP8 quantisation (PR 8023 page, title and section 1):

@@ -64,8 +64,9 @@ def test_route_permute_validation():
     assert "top-k" in lib().moe_last_error().decode() or lib().moe_last_error().decode()
 
 
-def _fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE):
-    return lib().moe_fused_fp8(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn, NULL)
+def _fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE, layout=0):
+    return lib().moe_fused_fp8(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn, layout,
+                               NULL)
 
 
 def test_fused_validation():
@@ -79,6 +80,8 @@ def test_fused_validation():
     assert _fused(E=1025, K=2) == E_LIMIT
     assert _fused(tm=48) == E_TILE
     assert _fused(tn=128) == E_TILE
+    assert _fused(layout=2) == E_SHAPE
+    assert _fused(layout=-1) == E_SHAPE
     assert _fused(ptr=NULL) == E_NULL
     assert _fused(out=NULL) == E_NULL
     assert _fused(ws=NULL) == E_WS
@@ -103,19 +106,33 @@ def test_workspace_size():
 def test_stage_validation():
     L = lib()
     g1 = lambda **k: L.moe_gemm1_swiglu_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("T", 16), 256, 128, 4, 2,
-                                              k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1), NULL)
+                                              k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1),
+                                              k.get("layout", 0), NULL)
     assert g1(align=24) == E_ALIGN
     assert g1(align=16, tm=32) == E_TILE          # tile must divide align
     assert g1(cap=-1) == E_SHAPE
     assert g1(T=0) == OK
+    assert g1(layout=3) == E_SHAPE
     g2 = lambda **k: L.moe_gemm2_weighted(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 256, 128, 4, 2,
-                                          k.get("align", 16), FAKE, 100, k.get("tm", -1), k.get("tn", -1), NULL)
+                                          k.get("align", 16), FAKE, 100, k.get("tm", -1), k.get("tn", -1),
+                                          k.get("layout", 0), NULL)
     assert g2(tn=64) == E_TILE
     assert g2(align=32, tm=64) == E_TILE
+    assert g2(layout=2) == E_SHAPE
     assert L.moe_combine(FAKE, FAKE, 4, 100, 4, 2, FAKE, NULL) == E_ALIGN
     assert L.moe_combine(FAKE, FAKE, 4, 128, 4, 9, FAKE, NULL) == E_TOPK
     assert L.moe_combine(NULL, FAKE, 4, 128, 4, 2, FAKE, NULL) == E_NULL
     assert L.moe_combine(NULL, NULL, 0, 128, 4, 2, NULL, NULL) == OK
+
+
+def test_pack_weights_validation():
+    f = lib().moe_pack_weights
+    assert f(FAKE, 0, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE
+    assert f(FAKE, 2, 24, 128, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE      # N % 16
+    assert f(FAKE, 2, 32, 64, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE       # K % 128
+    assert f(NULL, 2, 32, 128, FAKE, NULL) == E_NULL
+    assert f(FAKE, 2, 32, 128, FAKE, NULL) == E_SHAPE                          # in == out
+    assert "overlap" in lib().moe_last_error().decode()
 
 
 def test_gated_act_validation():
