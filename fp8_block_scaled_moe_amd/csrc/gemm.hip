@@ -264,18 +264,24 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   v8i wr[D][2];   // weight ring: slot s holds step j with j % D == s
   v4i ra[2][AP];  // token rows staged in registers, indexed by step parity
 
-  // producer of weights: step jw = (nw, kw), row pointers of N tile nw
+  // Producers never skip a load: past the run's last step the weight
+  // producer re-reads that step (a cache hit into a ring slot no step uses)
+  // and the token producer wraps within the M tile's K steps, so every step
+  // issues the same loads and the compiler's waits stay counted to the end.
+  //
+  // producer of weights: step (nw, kw), row pointers of N tile nw
   int nw = 0, kw = 0;
   const uint8_t* wp[2] = {wrow(0, 0), wrow(0, 1)};
   auto load_w = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wp[w], kw);
-    if (++kw == KT) {
+    if (kw + 1 < KT) {
+      ++kw;
+    } else if (nw + 1 < nn) {
       kw = 0;
-      if (++nw < nn) {
-        wp[0] = wrow(nw, 0);
-        wp[1] = wrow(nw, 1);
-      }
+      ++nw;
+      wp[0] = wrow(nw, 0);
+      wp[1] = wrow(nw, 1);
     }
   };
   // producer of token rows: K step ka (the rows are the same in every N tile).
@@ -321,12 +327,12 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   uint32_t bc = 0, bn = C::A_BYTES, bs = 2 * C::A_BYTES;   // buffers of steps j, j+1, j+2
 
   // one step j = (N tile n, K step k) with ring slot s = j % D and register
-  // parity s & 1 = j & 1; (nx, kx) is step j+1
-  auto step = [&](int s, int k, int nx, int kx, bool st2, bool ld4, bool more_w, bool next)
-      __attribute__((always_inline)) {
+  // parity s & 1 = j & 1; (nx, kx) is step j+1 (past the run's end it names
+  // LDS no step reads: the prefetch is harmless)
+  auto step = [&](int s, int k, int nx, int kx) __attribute__((always_inline)) {
     const int par = s & 1;
-    if (st2) store_a(par, bs);          // rows of step j+2 -> buffer (j+2) % 3
-    if (ld4) load_a(par);               // that register set is free again: fetch step j+4
+    store_a(par, bs);          // rows of step j+2 -> buffer (j+2) % 3
+    load_a(par);               // that register set is free again: fetch step j+4
     // software pipeline over the token sub-tiles: operands are read two
     // sub-tiles ahead, and the fold of sub-tile ts waits until the MFMAs of
     // ts+1 are issued, so neither LDS latency nor MFMA latency is exposed
@@ -350,8 +356,8 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
       asm volatile("" : "+v"(acc[ts][0]));
       asm volatile("" : "+v"(acc[ts][1]));
     }
-    if (more_w) load_w(s);
-    if (next) prefetch(bn, nx, kx);
+    load_w(s);
+    prefetch(bn, nx, kx);
     step_barrier();
     (void)k;
     const uint32_t t = bc;
@@ -372,31 +378,30 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   // looks the same whether entered from here or from the back edge, and the
   // compiler's counted waits need not drain it.
 #pragma unroll
-  for (int s = 0; s < D - 2; ++s)
-    if (s < S) load_w(s);
+  for (int s = 0; s < D - 2; ++s) load_w(s);
   load_a(0);
-  if (S > 1) load_a(1);
+  load_a(1);
   store_a(0, 0);
-  if (S > 1) store_a(1, C::A_BYTES);
-  if (S > 2) load_a(0);
-  if (D - 2 < S) load_w(D - 2);
-  if (S > 3) load_a(1);
-  if (D - 1 < S) load_w(D - 1);
+  store_a(1, C::A_BYTES);
+  load_a(0);
+  load_w(D - 2);
+  load_a(1);
+  load_w(D - 1);
   __syncthreads();
   prefetch(0, 0, 0);
 
   // Rounds of D steps.  A run of several N tiles needs KT % D == 0 (the host
   // only forms such runs then), so N tiles end on round boundaries and the
-  // ring slot of each step is static.
-  constexpr int kFull = D + 4 > 2 * D ? D + 4 : 2 * D;   // steps a full round looks ahead
+  // ring slot of each step is static.  Only a run of one N tile with
+  // KT % D != 0 ends in a partial round.
   int j = 0, n = 0, kb = 0;
-  // steady state: every step stores, loads and refills, no guards
-  while (j + kFull <= S) {
+  const int full = S - S % D;
+  while (j < full) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int k = kb + s;
       const bool end = k + 1 == KT;
-      step(s, k, end ? n + 1 : n, end ? 0 : k + 1, true, true, true, true);
+      step(s, k, end ? n + 1 : n, end ? 0 : k + 1);
     }
     j += D;
     kb += D;
@@ -406,22 +411,13 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
       ++n;
     }
   }
-  // last rounds
-  while (j < S) {
+  if (j < S) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      const int k = kb + s, jj = j + s;
-      const bool end = k + 1 == KT;
-      if (k < KT && jj < S) step(s, k, end ? n + 1 : n, end ? 0 : k + 1, jj + 2 < S, jj + 4 < S, jj + D < S, jj + 1 < S);
+      const int k = kb + s;
+      if (k < KT) step(s, k, k + 1 == KT ? 1 : 0, k + 1 == KT ? 0 : k + 1);
     }
-    j += D;
-    kb += D;
-    if (kb >= KT) {
-      finish_tile(n);
-      j += KT - kb;   // a partial last round (KT % D != 0 only with one N tile)
-      kb = 0;
-      ++n;
-    }
+    finish_tile(0);
   }
 }
 
@@ -607,13 +603,21 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// N tiles per workgroup: enough workgroups for about 8 per CU (load balance),
-// then spread evenly over the runs of an M tile.
-static int run_length(const GroupedRows& g, int tm, int NT) {
+// N tiles per workgroup: about 8 workgroups per CU (load balance); for a
+// short K (<= 16 steps per N tile, GEMM2's case) at least a quarter of the N
+// tiles, since each workgroup's prologue is then a large share of its work
+// (measured on GEMM2 at T=64 and T=8192: a quarter was fastest at both);
+// never so long that fewer than 2 workgroups per CU remain.  Then spread
+// evenly over the runs of an M tile.
+static int run_length(const GroupedRows& g, int tm, int NT, int KT) {
+  const int64_t cu = g.num_cu > 0 ? g.num_cu : 256;
   const int64_t mt_cap = g.cap / tm;
   int64_t mt_est = g.rows / tm + (g.E < g.rows ? g.E : g.rows) / 2 + 1;
   if (mt_est > mt_cap) mt_est = mt_cap;
-  int64_t nb = mt_est * NT / (8 * (int64_t)(g.num_cu > 0 ? g.num_cu : 256));
+  int64_t nb = mt_est * NT / (8 * cu);
+  if (KT <= 16 && nb < NT / 4) nb = NT / 4;
+  const int64_t nb_par = mt_est * NT / (2 * cu);
+  if (nb > nb_par) nb = nb_par;
   if (nb < 1) nb = 1;
   if (nb > NT) nb = NT;
   const int64_t ng = (NT + nb - 1) / nb;
@@ -635,7 +639,7 @@ static int ring_depth(int tm) {
 // per workgroup unless the K steps fill whole rounds of the weight ring
 static int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
   if (KT % ring_depth(tm) != 0) return 1;
-  int nb = run_length(g, tm, NT);
+  int nb = run_length(g, tm, NT, KT);
   while (nb > 1 && gemm_lds_bytes(tm, KT, nb) > kMaxGemmLds) nb = (nb + 1) / 2;
   const int ng = (NT + nb - 1) / nb;
   return (NT + ng - 1) / ng;
