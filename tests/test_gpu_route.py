@@ -32,6 +32,12 @@ def _ids_cases():
     cases.append(("E1024", rng.integers(0, 1024, size=(3000, 8)).astype(np.int32), 1024, 128))
     cases.append(("empty", np.zeros((0, 8), np.int32), 32, 16))
     cases.append(("ragged-chunk", rng.integers(0, 7, size=(1025, 1)).astype(np.int32), 7, 16))
+    # more than 4096 rows: the chunked multi-workgroup path
+    cases.append(("chunked-dropped", rng.integers(-5, 300, size=(1000, 9)).astype(np.int32), 256, 64))
+    cases.append(("chunked-ragged", rng.integers(0, 33, size=(4097, 1)).astype(np.int32), 33, 16))
+    cases.append(("chunked-all-same", np.full((1200, 8), 3, np.int32), 16, 128))
+    cases.append(("chunked-E1", np.zeros((5000, 1), np.int32), 1, 32))
+    cases.append(("chunked-E1024-ragged", rng.integers(0, 1024, size=(4099, 1)).astype(np.int32), 1024, 16))
     return cases
 
 
