@@ -9,42 +9,62 @@
 
 namespace fp8moe {
 
+typedef uint32_t u32x4c __attribute__((ext_vector_type(4)));
+constexpr int kMaxCombineK = 16;   // slots gathered with all loads in flight; larger K loops
+
+// Block (t, y): token t (grid x, which is not limited to 65536), 16-byte
+// column chunks 256*y + threadIdx.x.  All of
+// the token's K loads are issued before any sum (a dropped slot loads its own
+// row, which exists, and adds zero), so K x 16 bytes per thread are in
+// flight; Y is read once and out written once, both non-temporally.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Y,
                                                       const int32_t* __restrict__ ids, int T, int H,
                                                       int E, int K, uint16_t* __restrict__ out) {
   const int chunks = H / 8;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)T * chunks) return;
-  const int t = (int)(gid / chunks);
-  const int c = (int)(gid - (int64_t)t * chunks);
+  const int t = blockIdx.x;
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const uint16_t* yt = Y + (size_t)t * K * H + (size_t)c * 8;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const int e = ids[(size_t)t * K + j];
-    if ((unsigned)e >= (unsigned)E) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(Y + ((size_t)t * K + j) * H + (size_t)c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int j0 = 0; j0 < K; j0 += kMaxCombineK) {
+    const int n = K - j0 < kMaxCombineK ? K - j0 : kMaxCombineK;
+    u32x4c v[kMaxCombineK];
+    float keep[kMaxCombineK];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[2 * k] += bf16_to_f32((uint16_t)(w[k] & 0xffffu));
-      acc[2 * k + 1] += bf16_to_f32((uint16_t)(w[k] >> 16));
+    for (int j = 0; j < kMaxCombineK; ++j) {
+      if (j < n) {
+        const int e = ids[(size_t)t * K + j0 + j];
+        keep[j] = (unsigned)e < (unsigned)E ? 1.f : 0.f;
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4c*>(yt + (size_t)(j0 + j) * H));
+      }
+    }
+    // ascending j, as the single-slot loop summed
+#pragma unroll
+    for (int j = 0; j < kMaxCombineK; ++j) {
+      if (j < n && keep[j] != 0.f) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += bf16_to_f32((uint16_t)(v[j][k] & 0xffffu));
+          acc[2 * k + 1] += bf16_to_f32((uint16_t)(v[j][k] >> 16));
+        }
+      }
     }
   }
-  uint4 o;
-  uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+  u32x4c o;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    op[k] = (uint32_t)f32_to_bf16(acc[2 * k]) | ((uint32_t)f32_to_bf16(acc[2 * k + 1]) << 16);
-  *reinterpret_cast<uint4*>(out + (size_t)t * H + (size_t)c * 8) = o;
+    o[k] = (uint32_t)f32_to_bf16(acc[2 * k]) | ((uint32_t)f32_to_bf16(acc[2 * k + 1]) << 16);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4c*>(out + (size_t)t * H + (size_t)c * 8));
 }
 
 hipError_t launch_combine(const uint16_t* Y, const int32_t* topk_ids, int T, int H, int E, int K,
                           uint16_t* out, hipStream_t stream) {
-  const int64_t n = (int64_t)T * (H / 8);
-  if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, Y, topk_ids, T, H, E, K, out);
+  if (T == 0) return hipSuccess;
+  const int chunks = H / 8;
+  const dim3 grid((unsigned)T, (unsigned)((chunks + 255) / 256));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, Y, topk_ids, T, H, E, K, out);
   return hipGetLastError();
 }
 
