@@ -86,14 +86,27 @@ __device__ __forceinline__ v8i join(const v4i& lo, const v4i& hi) {
   return o;
 }
 
-// Weight operand of K step kb.  Row-major weights: wp = the lane's weight row
-// + 16*g, two 16-byte loads 64 bytes apart (a wave's load touches 16 rows).
-// MFMA-tiled weights: wp = the 16-row band + 16*lane, two 1 KB-contiguous
-// wave loads per 2 KB block (the layout of pack.hip).
+// Weights are read with buffer loads over the expert's weight block (at most
+// 2 x 16384 x 16384 bytes, so 32-bit offsets suffice): a per-lane offset that
+// never changes plus a wave-uniform (scalar) offset for the 16-row band and
+// the K step, so a weight load costs no vector address arithmetic.
+// Row-major weights: lane l reads row band + l%16, bytes 16g and 64 + 16g of
+// the K step's 128 (a wave's load touches 16 rows).  MFMA-tiled weights: the
+// band's 2 KB block of the K step, lane l at 16l and 1024 + 16l (two 1 KB
+// contiguous wave loads; the layout of pack.hip).
+constexpr int kWeightRsrcFlags = 0x00020000;   // gfx9-family raw buffer resource word 3
+
 template <bool PACKED>
-__device__ __forceinline__ v8i weight_frag(const uint8_t* wp, int kb) {
-  const uint8_t* p = wp + (size_t)kb * (PACKED ? 2048 : kKB);
-  return join(*reinterpret_cast<const v4i*>(p), *reinterpret_cast<const v4i*>(p + (PACKED ? 1024 : 64)));
+__device__ __forceinline__ int weight_lane_offset(int lane, int kdim) {
+  return PACKED ? 16 * lane : (lane & 15) * kdim + 16 * (lane >> 4);
+}
+
+// soff = the band's scalar offset (band_row * kdim) + K step offset
+template <bool PACKED>
+__device__ __forceinline__ v8i weight_frag(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff) {
+  constexpr int kHalf = PACKED ? 1024 : 64;
+  return join(__builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0),
+              __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + kHalf, soff, 0));
 }
 
 // Work of workgroup blockIdx.x: one M tile and a run of up to NB consecutive
@@ -239,12 +252,13 @@ struct Lds {
 // of step j + 4 are fetched at step j whatever N tile they belong to, so the
 // pipeline does not drain between the N tiles of a run.
 //
-// wrow(n, w) gives the lane's weight pointer of sub-tile w in N tile n at K
-// step 0 (weight_frag's wp).
-template <int TM, bool GATED, bool PACKED, typename WRow, typename Epi>
+// wband(n, w) gives the scalar byte offset of sub-tile w's 16-row band in N
+// tile n (band row * kdim) within the expert's weight block `wrsrc`; kdim is
+// the K extent in bytes (H for GEMM1, I for GEMM2).
+template <int TM, bool GATED, bool PACKED, typename WBand, typename Epi>
 __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const (&a_src)[Cfg<TM>::A_PER_THREAD],
-                                            int sb_sel, int KT, int nn, int tid, int lane,
-                                            v4f (&acc)[Cfg<TM>::TS][2], WRow wrow, Epi epi) {
+                                            __amdgpu_buffer_rsrc_t wrsrc, int kdim, int sb_sel, int KT, int nn,
+                                            int tid, int lane, v4f (&acc)[Cfg<TM>::TS][2], WBand wband, Epi epi) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS, D = C::D, AP = C::A_PER_THREAD;
   const float* SAs = Lds<TM>::token_scales(smem);
@@ -269,19 +283,21 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   // and the token producer wraps within the M tile's K steps, so every step
   // issues the same loads and the compiler's waits stay counted to the end.
   //
-  // producer of weights: step (nw, kw), row pointers of N tile nw
+  // producer of weights: step (nw, kw), band offsets of N tile nw
+  const int wvoff = weight_lane_offset<PACKED>(lane, kdim);
+  constexpr int kKStep = PACKED ? 2048 : kKB;   // bytes between K steps within a band
   int nw = 0, kw = 0;
-  const uint8_t* wp[2] = {wrow(0, 0), wrow(0, 1)};
+  int wb[2] = {wband(0, 0), wband(0, 1)};
   auto load_w = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wp[w], kw);
+    for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wrsrc, wvoff, wb[w] + kw * kKStep);
     if (kw + 1 < KT) {
       ++kw;
     } else if (nw + 1 < nn) {
       kw = 0;
       ++nw;
-      wp[0] = wrow(nw, 0);
-      wp[1] = wrow(nw, 1);
+      wb[0] = wband(nw, 0);
+      wb[1] = wband(nw, 1);
     }
   };
   // producer of token rows: K step ka (the rows are the same in every N tile).
@@ -457,11 +473,12 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   // wave w owns I columns [n0 + 16w, n0 + 16w + 16) of N tile n (n0 = 128 (nt0 + n)):
   // its two operands are those columns' gate rows and up rows
   const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, 2 * I * H, kWeightRsrcFlags);
   const float* sexp = w13_scale + (size_t)tc.e * (2 * IB) * HB;
-  auto wrow = [&](int n, int w) -> const uint8_t* {
+  auto wband = [&](int n, int w) -> int {
     const int c = 128 * (nt0 + n) + 16 * wave;   // first row of the 16-row band
-    if constexpr (PACKED) return wexp + (size_t)(w ? I + c : c) * H + 16 * lane;
-    else return wexp + (size_t)((w ? I + c : c) + l16) * H + 16 * g;
+    return (w ? I + c : c) * H;
   };
   stage_weight_scales(SBs, KT, nn, [&](int n, int which) -> const float* {
     return sexp + (size_t)(which ? IB + nt0 + n : nt0 + n) * HB;
@@ -512,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, true, PACKED>(smem, a_src, 0, KT, nn, tid, lane, acc, wrow, epi);
+  ws_mainloop<TM, true, PACKED>(smem, a_src, wrsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -551,11 +568,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   // wave w owns H columns [n0 + 32w, n0 + 32w + 32) of N tile n (n0 = 256 (nt0 + n)),
   // its two operands 16 columns each; rows past H read a valid row, outputs masked
   const uint8_t* wexp = w2 + (size_t)tc.e * H * (size_t)I;
-  auto wrow = [&](int n, int w) -> const uint8_t* {
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, H * I,
+                                                                         kWeightRsrcFlags);
+  auto wband = [&](int n, int w) -> int {
     // bands past H (the last N tile when H % 256 == 128) read the last band
-    const int band = min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16);
-    if constexpr (PACKED) return wexp + (size_t)band * I + 16 * lane;
-    else return wexp + (size_t)(band + l16) * I + 16 * g;
+    return min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16) * I;
   };
   // N tile n spans scale blocks 2(nt0+n) and 2(nt0+n)+1 (the second clamped
   // at the last block; only columns < H are stored); waves 4..7 use the second
@@ -599,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, false, PACKED>(smem, a_src, wave >> 2, KT, nn, tid, lane, acc, wrow, epi);
+  ws_mainloop<TM, false, PACKED>(smem, a_src, wrsrc, I, wave >> 2, KT, nn, tid, lane, acc, wband, epi);
 }
 
 // ------------------------------------------------------------------------------------------
