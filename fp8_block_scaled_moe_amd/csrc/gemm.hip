@@ -21,8 +21,9 @@
 //   * each wave owns 32 weight rows (two 16-row MFMA operands) and loads them
 //     straight from global memory into a ring of VGPRs D K-steps deep -- no
 //     LDS, no barrier on the weight path, up to D x 4 KB in flight per wave;
-//   * the TM token rows, shared by all 8 waves, rotate through three LDS
-//     buffers (register-staged two steps ahead), one barrier per K step;
+//   * the TM token rows, shared by all 8 waves, go straight from global
+//     memory into four LDS buffers (global_load_lds_dwordx4, no VGPR staging)
+//     three K steps ahead of their use; one barrier per K step;
 //   * the token-row scales of the whole tile are staged in LDS once.
 // The MFMA puts weight rows on its A side and tokens on its B side, so the
 // lane layout of the result is: token = lane % 16, four consecutive weight
@@ -68,11 +69,13 @@ constexpr int kKB = 128;   // K per step (= scale block)
 template <int TM>
 struct Cfg {
   static constexpr int TS = TM / 16;                                 // token sub-tiles
-  static constexpr int D = TM >= 128 ? 4 : (TM >= 64 ? 6 : 8);      // weight ring depth (even)
-  static constexpr int A_BYTES = TM * kKB;
-  static constexpr int A_CHUNKS = TM * 8;                            // 16-byte chunks per K step
-  static constexpr int A_PER_THREAD = (A_CHUNKS + kThreads - 1) / kThreads;
-  static_assert(D % 2 == 0, "the token double buffer follows the parity of the unrolled step");
+  static constexpr int D = 4;                                        // weight ring depth = token buffers
+  static constexpr int A_BYTES = TM * kKB;                           // token rows of one K step
+  // direct-to-LDS loads write 1 KB (64 lanes x 16 bytes) each: NBLK per K
+  // step, A_PER_WAVE issued by each wave (below 8 blocks waves repeat blocks)
+  static constexpr int NBLK = A_BYTES / 1024;
+  static constexpr int A_PER_WAVE = NBLK >= kWaves ? NBLK / kWaves : 1;
+  __host__ __device__ static constexpr int block_of(int wave, int i) { return (wave * A_PER_WAVE + i) % NBLK; }
 };
 
 
@@ -157,13 +160,21 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
 }
 
 // The per-step workgroup barrier, without the memory fence of __syncthreads
-// (which would wait for the next step's operand reads already in flight).
+// (which would wait for all loads in flight, the look-ahead ones included).
 // Sufficient here: every LDS read of a buffer is consumed by an MFMA before
 // the wave reaches the barrier that precedes the buffer's next write, and
-// every LDS write is retired by the writer's own in-order LDS waits a full
-// step before any wave reads it.  The empty asm keeps the compiler from
+// every direct-to-LDS write is retired by the writer's explicit vmcnt wait
+// before the barrier that publishes it.  The empty asm keeps the compiler from
 // moving memory accesses across it; the scheduling barriers keep each step's
 // MFMAs on their side.
+// s_waitcnt vmcnt(N) with the LDS and export counters unconstrained (gfx9
+// encoding: vmcnt low bits 3:0 and high bits 15:14).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
 __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -224,15 +235,16 @@ __device__ __forceinline__ void read_token_scales(const float* p, float (&sa)[TS
   }
 }
 
-// LDS layout: three token buffers [TM][128], the M tile's token scales
-// [KT][TM], the run's weight block scales [NB][KT][2], the epilogue scratch
-// (GEMM1: per-wave row max [8][TM]; GEMM2: source row and top-k weight [2][TM]).
+// Dynamic LDS layout (the four token buffers [TM][128] are static arrays of
+// the main loop): the M tile's token scales [KT][TM], the run's weight block
+// scales [NB][KT][2], the epilogue scratch (GEMM1: per-wave row max [8][TM];
+// GEMM2: source row and top-k weight [2][TM]).
 template <int TM>
 struct Lds {
   __host__ __device__ static constexpr size_t bytes(int KT, int NB) {
-    return 3 * (size_t)Cfg<TM>::A_BYTES + 4 * (size_t)TM * KT + 8 * (size_t)NB * KT + 4 * (size_t)kWaves * TM;
+    return 4 * (size_t)TM * KT + 8 * (size_t)NB * KT + 4 * (size_t)kWaves * TM;
   }
-  __device__ static float* token_scales(uint8_t* smem) { return reinterpret_cast<float*>(smem + 3 * Cfg<TM>::A_BYTES); }
+  __device__ static float* token_scales(uint8_t* smem) { return reinterpret_cast<float*>(smem); }
   __device__ static float* weight_scales(uint8_t* smem, int KT) { return token_scales(smem) + (size_t)TM * KT; }
   __device__ static float* scratch(uint8_t* smem, int KT, int NB) { return weight_scales(smem, KT) + 2 * (size_t)NB * KT; }
 };
@@ -242,25 +254,26 @@ struct Lds {
 // j % KT): acc[ts][w] for the wave's two weight sub-tiles x TS token
 // sub-tiles; epi(n) consumes and the loop clears acc after N tile n's last step.
 //
-// Token rows rotate through three LDS buffers: step j reads buffer j % 3 and
-// fills buffer (j + 2) % 3 with the rows of step j + 2 (fetched into
-// registers two steps earlier).  That buffer was last read in step j - 1, so
-// one barrier per step orders both hazards, and the first two operand
-// fragments (and the scales) of step j + 1 can be read before step j's
-// barrier: the LDS latency at the step boundary overlaps the barrier wait
-// instead of stalling the first MFMAs.  Weights of step j + D and token rows
-// of step j + 4 are fetched at step j whatever N tile they belong to, so the
-// pipeline does not drain between the N tiles of a run.
+// Token rows rotate through four LDS buffers: step j reads buffer j % 4 and
+// starts the direct-to-LDS loads of step j + 3's rows into buffer
+// (j + 3) % 4, last read in step j - 1 (so after step j - 1's barrier).  The
+// loads are published by the barrier that ends step j + 1, after each
+// wave's own vmcnt wait, and the first two operand fragments (and the
+// scales) of step j + 3 are read just before step j + 2's barrier: the LDS
+// latency at the step boundary overlaps the barrier wait instead of stalling
+// the first MFMAs.  Weights of step j + D and token rows of step j + 3 are
+// fetched at step j whatever N tile they belong to, so the pipeline does not
+// drain between the N tiles of a run.
 //
 // wband(n, w) gives the scalar byte offset of sub-tile w's 16-row band in N
 // tile n (band row * kdim) within the expert's weight block `wrsrc`; kdim is
 // the K extent in bytes (H for GEMM1, I for GEMM2).
 template <int TM, bool GATED, bool PACKED, typename WBand, typename Epi>
-__device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const (&a_src)[Cfg<TM>::A_PER_THREAD],
+__device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
                                             __amdgpu_buffer_rsrc_t wrsrc, int kdim, int sb_sel, int KT, int nn,
                                             int tid, int lane, v4f (&acc)[Cfg<TM>::TS][2], WBand wband, Epi epi) {
   using C = Cfg<TM>;
-  constexpr int TS = C::TS, D = C::D, AP = C::A_PER_THREAD;
+  constexpr int TS = C::TS, D = C::D, APW = C::A_PER_WAVE;
   const float* SAs = Lds<TM>::token_scales(smem);
   const float* SBs = Lds<TM>::weight_scales(smem, KT);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -268,22 +281,23 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   // this lane's two 16-byte reads of token sub-tile 0 (sub-tile ts adds 2048 bytes:
   // the swizzle key depends on the row's low four bits only)
   const int r0 = lane & 15, g = lane >> 4;
-  const uint8_t* rd0 = smem + swz(r0, g);
-  const uint8_t* rd1 = smem + swz(r0, g + 4);
-  auto frag = [&](uint32_t buf, int ts) __attribute__((always_inline)) -> v8i {
-    return join(*reinterpret_cast<const v4i*>(rd0 + buf + 2048 * ts),
-                *reinterpret_cast<const v4i*>(rd1 + buf + 2048 * ts));
+  // four token buffers, separate LDS objects so the compiler tracks each one's
+  // direct-to-LDS loads on its own; step j reads buffer j % 4 (= its ring slot)
+  __shared__ __attribute__((aligned(1024))) uint8_t tb0[C::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t tb1[C::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t tb2[C::A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t tb3[C::A_BYTES];
+  auto tbuf = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return i == 0 ? tb0 : (i == 1 ? tb1 : (i == 2 ? tb2 : tb3));
+  };
+  const int o0 = swz(r0, g), o1 = swz(r0, g + 4);
+  auto frag = [&](int bi, int ts) __attribute__((always_inline)) -> v8i {
+    const uint8_t* t = tbuf(bi);
+    return join(*reinterpret_cast<const v4i*>(t + o0 + 2048 * ts), *reinterpret_cast<const v4i*>(t + o1 + 2048 * ts));
   };
 
   v8i wr[D][2];   // weight ring: slot s holds step j with j % D == s
-  v4i ra[2][AP];  // token rows staged in registers, indexed by step parity
 
-  // Producers never skip a load: past the run's last step the weight
-  // producer re-reads that step (a cache hit into a ring slot no step uses)
-  // and the token producer wraps within the M tile's K steps, so every step
-  // issues the same loads and the compiler's waits stay counted to the end.
-  //
-  // producer of weights: step (nw, kw), band offsets of N tile nw
   const int wvoff = weight_lane_offset<PACKED>(lane, kdim);
   constexpr int kKStep = PACKED ? 2048 : kKB;   // bytes between K steps within a band
   int nw = 0, kw = 0;
@@ -300,24 +314,29 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
       wb[1] = wband(nw, 1);
     }
   };
-  // producer of token rows: K step ka (the rows are the same in every N tile).
-  // Every thread loads and stores every time (a thread past the tile's chunk
-  // count repeats chunk cid % A_CHUNKS: same bytes to the same address), so
-  // the number of memory instructions in flight is static and the compiler's
-  // waits can count them instead of draining the queues.
+  // token rows of K step ka -> buffer bi, straight from global memory into
+  // LDS: the wave's load i fills 1 KB block block_of(wave, i) of the buffer,
+  // lane l its 16-byte chunk l, read from a_src[i] (the source already
+  // follows the swizzle).  ka wraps within the tile, so loads past the last
+  // step re-read valid rows and are never used.
+  const int wave = tid >> 6;
   int ka = 0;
-  auto load_a = [&](int par) __attribute__((always_inline)) {
+  auto dma_a = [&](int bi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < AP; ++i) ra[par][i] = *reinterpret_cast<const v4i*>(a_src[i] + (size_t)ka * kKB);
+    for (int i = 0; i < APW; ++i) {
+      uint8_t* dst = tbuf(bi) + C::block_of(wave, i) * 1024;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src[i] + (size_t)ka * kKB),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
     if (++ka == KT) ka = 0;
   };
-  auto store_a = [&](int par, uint32_t buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < AP; ++i) {
-      const int cid = (tid + i * kThreads) % C::A_CHUNKS;
-      *reinterpret_cast<v4i*>(smem + buf + swz(cid >> 3, cid & 7)) = ra[par][i];
-    }
-  };
+  // The direct-to-LDS loads a wave issued one step back (for the step after
+  // next) must have landed before the barrier that hands their buffer to the
+  // other waves.  Vector memory operations complete in issue order for the
+  // counter, and younger than those loads are that step's 4 weight loads and
+  // this step's APW + 4 loads, so the wait is vmcnt(8 + APW).  Every step
+  // issues all of them (the producers never skip), so the count holds.
+  auto publish_wait = [&]() __attribute__((always_inline)) { vmcnt_wait<8 + APW>(); };
 
   // carried across the step boundary: the first two fragments and the scales of the next step
   v8i af[3];
@@ -334,24 +353,18 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
       sb0 = sb1 = b[sb_sel];
     }
   };
-  auto prefetch = [&](uint32_t buf, int n, int k) __attribute__((always_inline)) {
-    af[0] = frag(buf, 0);
-    if (TS > 1) af[1] = frag(buf, 1);
+  auto prefetch = [&](int bi, int n, int k) __attribute__((always_inline)) {
+    af[0] = frag(bi, 0);
+    if (TS > 1) af[1] = frag(bi, 1);
     read_scales(n, k);
   };
 
-  uint32_t bc = 0, bn = C::A_BYTES, bs = 2 * C::A_BYTES;   // buffers of steps j, j+1, j+2
-
-  // one step j = (N tile n, K step k) with ring slot s = j % D and register
-  // parity s & 1 = j & 1; (nx, kx) is step j+1 (past the run's end it names
-  // LDS no step reads: the prefetch is harmless)
-  auto step = [&](int s, int k, int nx, int kx) __attribute__((always_inline)) {
-    const int par = s & 1;
-    store_a(par, bs);          // rows of step j+2 -> buffer (j+2) % 3
-    load_a(par);               // that register set is free again: fetch step j+4
-    // software pipeline over the token sub-tiles: operands are read two
-    // sub-tiles ahead, and the fold of sub-tile ts waits until the MFMAs of
-    // ts+1 are issued, so neither LDS latency nor MFMA latency is exposed
+  static_assert(D == 4, "the token buffers follow the weight ring slot");
+  // one step j = (N tile n, K step k) with ring slot / buffer s = j % 4;
+  // (nx, kx) is step j+1
+  auto step = [&](int s, int nx, int kx) __attribute__((always_inline)) {
+    dma_a((s + 3) & 3);        // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
+    __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
     v4f pr[2][2];
     auto fold = [&](int ts) __attribute__((always_inline)) {
       acc[ts][0] += pr[ts & 1][0] * (sa[ts] * sb0);
@@ -359,27 +372,21 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
     };
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
-      if (ts + 2 < TS) af[(ts + 2) % 3] = frag(bc, ts + 2);
+      if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
       pr[ts & 1][0] = mfma16x16x128_fp8(wr[s][0], af[ts % 3], zero);
       pr[ts & 1][1] = mfma16x16x128_fp8(wr[s][1], af[ts % 3], zero);
       if (ts >= 1) fold(ts - 1);
     }
     fold(TS - 1);
-    // MFMAs and folds are pure register work: pin them to this step, or the
-    // compiler sinks them past later barriers and keeps old ring slots alive
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
       asm volatile("" : "+v"(acc[ts][0]));
       asm volatile("" : "+v"(acc[ts][1]));
     }
     load_w(s);
-    prefetch(bn, nx, kx);
+    prefetch((s + 1) & 3, nx, kx);
+    publish_wait();
     step_barrier();
-    (void)k;
-    const uint32_t t = bc;
-    bc = bn;
-    bn = bs;
-    bs = t;
   };
   auto finish_tile = [&](int n) __attribute__((always_inline)) {
     epi(n, acc);
@@ -387,22 +394,15 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
     for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = zero;
   };
 
-  // prologue: weights of steps 0..D-1; token rows of steps 0, 1 into buffers
-  // 0, 1; registers then hold steps 2 (parity 0) and 3 (parity 1).  The last
-  // loads go out in the loop's own order (rows of step j+4, then weights of
-  // step j+D, per step j), so at the loop head the queue of loads in flight
-  // looks the same whether entered from here or from the back edge, and the
-  // compiler's counted waits need not drain it.
+  // prologue: rows of steps 0..2 into buffers 0..2, weights of steps 0..3;
+  // rows of steps 0 and 1 must have landed before the first barrier (younger
+  // than them: step 2's rows and the 16 weight loads)
+  dma_a(0);
+  dma_a(1);
+  dma_a(2);
 #pragma unroll
-  for (int s = 0; s < D - 2; ++s) load_w(s);
-  load_a(0);
-  load_a(1);
-  store_a(0, 0);
-  store_a(1, C::A_BYTES);
-  load_a(0);
-  load_w(D - 2);
-  load_a(1);
-  load_w(D - 1);
+  for (int s = 0; s < D; ++s) load_w(s);
+  vmcnt_wait<APW + 4 * D>();
   __syncthreads();
   prefetch(0, 0, 0);
 
@@ -417,7 +417,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
     for (int s = 0; s < D; ++s) {
       const int k = kb + s;
       const bool end = k + 1 == KT;
-      step(s, k, end ? n + 1 : n, end ? 0 : k + 1);
+      step(s, end ? n + 1 : n, end ? 0 : k + 1);
     }
     j += D;
     kb += D;
@@ -431,10 +431,12 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int k = kb + s;
-      if (k < KT) step(s, k, k + 1 == KT ? 1 : 0, k + 1 == KT ? 0 : k + 1);
+      if (k < KT) step(s, k + 1 == KT ? 1 : 0, k + 1 == KT ? 0 : k + 1);
     }
     finish_tile(0);
   }
+  // the look-ahead loads into LDS land before the workgroup's LDS is released
+  vmcnt_wait<0>();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -462,13 +464,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   float* SBs = Lds<TM>::weight_scales(smem, KT);
   float* red = Lds<TM>::scratch(smem, KT, NB);
 
-  const uint8_t* a_src[C::A_PER_THREAD];
+  // source of this lane's 16-byte chunk of each direct-to-LDS block: LDS
+  // chunk qc holds row qc / 8, logical chunk (qc % 8) XOR the row's key
+  const uint8_t* a_src[C::A_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < C::A_PER_THREAD; ++i) {
-    const int cid = (tid + i * kThreads) % C::A_CHUNKS;
-    const int src = sorted_src[tc.p0 + (cid >> 3)];
+  for (int i = 0; i < C::A_PER_WAVE; ++i) {
+    const int qc = C::block_of(tid >> 6, i) * 64 + lane;
+    const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
+    const int src = sorted_src[tc.p0 + r];
     const size_t tok = src >= 0 ? (size_t)(src / K) : 0;  // a pad row reads token 0; never stored
-    a_src[i] = x + tok * H + (cid & 7) * 16;
+    a_src[i] = x + tok * H + c * 16;
   }
   // wave w owns I columns [n0 + 16w, n0 + 16w + 16) of N tile n (n0 = 128 (nt0 + n)):
   // its two operands are those columns' gate rows and up rows
@@ -559,11 +564,12 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   float* wrow_w = reinterpret_cast<float*>(srow + TM);
 
   // token rows: q rows p0.. (a pad row holds whatever is there; its outputs are never stored)
-  const uint8_t* a_src[C::A_PER_THREAD];
+  const uint8_t* a_src[C::A_PER_WAVE];   // as in GEMM1
 #pragma unroll
-  for (int i = 0; i < C::A_PER_THREAD; ++i) {
-    const int cid = (tid + i * kThreads) % C::A_CHUNKS;
-    a_src[i] = q + (size_t)(tc.p0 + (cid >> 3)) * I + (cid & 7) * 16;
+  for (int i = 0; i < C::A_PER_WAVE; ++i) {
+    const int qc = C::block_of(tid >> 6, i) * 64 + lane;
+    const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
+    a_src[i] = q + (size_t)(tc.p0 + r) * I + c * 16;
   }
   // wave w owns H columns [n0 + 32w, n0 + 32w + 32) of N tile n (n0 = 256 (nt0 + n)),
   // its two operands 16 columns each; rows past H read a valid row, outputs masked
@@ -642,6 +648,8 @@ static int run_length(const GroupedRows& g, int tm, int NT, int KT) {
 }
 
 size_t gemm_lds_bytes(int tile_m, int KT, int NB);
+// dynamic LDS beside the largest tile's four static token buffers
+constexpr size_t kMaxDynLds = kMaxGemmLds - 4 * (size_t)Cfg<128>::A_BYTES;
 
 static int ring_depth(int tm) {
   switch (tm) {
@@ -657,7 +665,7 @@ static int ring_depth(int tm) {
 static int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
   if (KT % ring_depth(tm) != 0) return 1;
   int nb = run_length(g, tm, NT, KT);
-  while (nb > 1 && gemm_lds_bytes(tm, KT, nb) > kMaxGemmLds) nb = (nb + 1) / 2;
+  while (nb > 1 && gemm_lds_bytes(tm, KT, nb) > kMaxDynLds) nb = (nb + 1) / 2;
   const int ng = (NT + nb - 1) / nb;
   return (NT + ng - 1) / ng;
 }
@@ -679,7 +687,7 @@ size_t gemm_lds_bytes(int tile_m, int KT, int NB) {
 
 template <typename Kern>
 static hipError_t allow_lds(Kern k) {
-  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxGemmLds);
+  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
 }
 
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
@@ -697,7 +705,7 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
   if (attr != hipSuccess) return attr;
   const int NT = I / 128, NB = fit_run(g, tile_m, NT, H / kKB), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes(tile_m, H / kKB, NB);
-  if (lds > kMaxGemmLds) return hipErrorInvalidValue;
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g.cap, tile_m, NG)), block(kThreads);
 #define FP8MOE_G1(TMV)                                                                                 \
   if (packed)                                                                                          \
@@ -733,7 +741,7 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
   if (attr != hipSuccess) return attr;
   const int NT = (H + kTN - 1) / kTN, NB = fit_run(g, tile_m, NT, I / kKB), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes(tile_m, I / kKB, NB);
-  if (lds > kMaxGemmLds) return hipErrorInvalidValue;
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g.cap, tile_m, NG)), block(kThreads);
 #define FP8MOE_G2(TMV)                                                                                    \
   if (packed)                                                                                             \
