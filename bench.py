@@ -255,12 +255,13 @@ def layer_flops(p):
 
 
 def stage_times(p, steps, warmup):
-    """Average time of each stage launched on its own (same kernels, tiles and weight layout as the fused call)."""
+    """Average time of each stage launched on its own (same kernels, tiles, routing alignment and weight
+    layout as the fused call; outputs preallocated, so each timing is the stage's kernels only)."""
     T, H, I, E, K = p.T, p.H, p.I, p.E, p.K
     R = T * K
     tm1, _ = fm.select_tile(R, I, H, E, 256, True)
     tm2, _ = fm.select_tile(R, H, I, E, 256, False)
-    align = max(tm1, tm2)
+    align = 16
     L = fm.WEIGHTS_MFMA_TILED
     route = fm.route_permute(p.topk_ids, E, align)
     q, qs = fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_p, p.w13_s, route, T, K, align, tile_m=tm1, weight_layout=L)
@@ -268,9 +269,10 @@ def stage_times(p, steps, warmup):
     out = {
         "route_ms": event_time_ms(lambda: fm.route_permute(p.topk_ids, E, align), steps, warmup),
         "gemm1_ms": event_time_ms(lambda: fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_p, p.w13_s, route, T, K, align,
-                                                                tile_m=tm1, weight_layout=L), steps, warmup),
+                                                                tile_m=tm1, weight_layout=L, q=q, q_scale=qs),
+                                  steps, warmup),
         "gemm2_ms": event_time_ms(lambda: fm.gemm2_weighted(q, qs, p.w2_p, p.w2_s, route, p.topk_weights, T, K,
-                                                            align, tile_m=tm2, weight_layout=L), steps, warmup),
+                                                            align, tile_m=tm2, weight_layout=L, Y=Y), steps, warmup),
         "combine_ms": event_time_ms(lambda: fm.combine(Y, p.topk_ids, E), steps, warmup),
         "tile_m_gemm1": tm1, "tile_m_gemm2": tm2,
     }

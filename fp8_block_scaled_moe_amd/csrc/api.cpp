@@ -182,7 +182,9 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
   const int64_t R = T * K;
   const int tm1 = pick_tile_m(tile_m, R, I, H, E, true);
   const int tm2 = pick_tile_m(tile_m, R, H, I, E, false);
-  const int align = tm1 > tm2 ? tm1 : tm2;
+  // segments padded to 16 rows only: the GEMMs cover each expert with tiles
+  // of up to tm rows and one shorter last tile
+  const int align = 16;
   const int64_t cap = R + (int64_t)E * (align - 1);
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -219,14 +221,13 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13,
   if (st) return st;
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
-  if (tile_m != -1 && (!valid_tile_m(tile_m) || align % tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d must be in {16,32,64,128} and divide align %d", tile_m, align);
+  if (tile_m != -1 && !valid_tile_m(tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
   if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
   if (T == 0 || cap == 0) return ok();
   if (!x || !x_scale || !w13 || !w13_scale || !padded_indptr || !sorted_src || !q || !q_scale)
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
-  while (align % tm) tm >>= 1;
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
                                 w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
@@ -243,15 +244,14 @@ int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, cons
   if (st) return st;
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
-  if (tile_m != -1 && (!valid_tile_m(tile_m) || align % tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d must be in {16,32,64,128} and divide align %d", tile_m, align);
+  if (tile_m != -1 && !valid_tile_m(tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
   if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
   if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
   if (T == 0 || cap == 0) return ok();
   if (!q || !q_scale || !w2 || !w2_scale || !padded_indptr || !sorted_src || !topk_weights || !Y)
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
-  while (align % tm) tm >>= 1;
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = launch_gemm2(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2),
                                 w2_scale, topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm, 256,

@@ -126,38 +126,73 @@ __device__ __forceinline__ v8i weight_frag(__amdgpu_buffer_rsrc_t rsrc, int voff
 // the 8 XCDs round-robin), so the M tiles that share one expert's weight
 // tiles start together on one XCD and stream them through its L2 in step:
 // the weights leave HBM once.
-struct TileCoord { int mt, run, e, p0; };
+// Tile h of expert e covers rows [p0, p0 + h) of its padded segment: the
+// segment is cut into tiles of TMAX rows from its start, so only its last
+// tile can be shorter (a multiple of the route alignment, >= 16 rows).
+struct TileCoord { int mt, run, e, p0, h; };
 
-template <int TM>
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int TMAX>
+__device__ __forceinline__ int expert_tiles(const int32_t* __restrict__ padded, int e) {
+  return (padded[e + 1] - padded[e] + TMAX - 1) / TMAX;
+}
+
+// Work item L of this workgroup -> (expert, N run, M tile).  Items are
+// ordered expert-major, then N run, then M tile, so expert e's items start at
+// NG * (tiles of experts before e).  Both passes over the experts are a
+// wave-wide coalesced load plus shuffles (all waves compute the same values).
+template <int TMAX>
 __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
                                            const int32_t* __restrict__ sorted_src, int E, int NG, TileCoord& tc) {
-  const int total_rows = padded[E];
-  const int items = (total_rows / TM) * NG;
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int e = lane; e < E; e += 64) tot += expert_tiles<TMAX>(padded, e);
+  const int items = __builtin_amdgcn_readfirstlane(wave_sum(tot)) * NG;
   const int per_xcd = (items + kNumXcd - 1) / kNumXcd;
   const int b = blockIdx.x;
   const int slot = b / kNumXcd;
   const int L = (b % kNumXcd) * per_xcd + slot;
   if (slot >= per_xcd || L >= items) return false;
-  // Expert ranges start at multiples of NG, so the expert owning item L owns
-  // row (L / NG) * TM: e = (number of e' in [0, E) with padded[e'] <= that
-  // row) - 1 (padded is non-decreasing, those e' form a prefix).  One round of
-  // coalesced loads and a wave sum instead of a chain of dependent loads.
-  const int prow = (L / NG) * TM;
-  const int lane = threadIdx.x & 63;
-  int cnt = 0;
-  for (int e = lane; e < E; e += 64) cnt += padded[e] <= prow ? 1 : 0;
+  // The expert owning M tile t = L / NG is the number of experts whose tiles
+  // all come before t (their running tile count is <= t; empty experts
+  // included), and the sum of those experts' tiles is its first tile.
+  const int t = L / NG;
+  int cnt = 0, before = 0, base = 0;
+  for (int c = 0; c < E && base <= t; c += 64) {
+    const int e = c + lane;
+    const int nt = e < E ? expert_tiles<TMAX>(padded, e) : 0;
+    int incl = nt;   // inclusive scan of the chunk's tile counts
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-  const int e = __builtin_amdgcn_readfirstlane(cnt - 1);
-  const int ms = padded[e] / TM;
-  const int nm = padded[e + 1] / TM - ms;   // >= 1: the expert owns item L
-  const int j = L - NG * ms;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (e < E && base + incl <= t) {
+      ++cnt;
+      before += nt;
+    }
+    base += __shfl(incl, 63);
+  }
+  const int e = __builtin_amdgcn_readfirstlane(wave_sum(cnt));
+  const int first = __builtin_amdgcn_readfirstlane(wave_sum(before));
+  const int nm = expert_tiles<TMAX>(padded, e);   // >= 1: the expert owns tile t
+  const int j = L - NG * first;
   tc.run = j / nm;
-  tc.mt = ms + (j - tc.run * nm);
-  tc.p0 = tc.mt * TM;
+  tc.mt = j - tc.run * nm;
+  tc.p0 = padded[e] + tc.mt * TMAX;
+  tc.h = min(TMAX, padded[e + 1] - tc.p0);
   tc.e = e;
   return sorted_src[tc.p0] >= 0;  // false: segment padding only, nothing to compute
 }
+
+// The four LDS token buffers of the main loop (static arrays of the kernel,
+// sized for its largest tile and shared by all its tile bodies).
+struct TokenBuffers { uint8_t* b[4]; };
 
 // The per-step workgroup barrier, without the memory fence of __syncthreads
 // (which would wait for all loads in flight, the look-ahead ones included).
@@ -167,20 +202,20 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
 // before the barrier that publishes it.  The empty asm keeps the compiler from
 // moving memory accesses across it; the scheduling barriers keep each step's
 // MFMAs on their side.
-// s_waitcnt vmcnt(N) with the LDS and export counters unconstrained (gfx9
-// encoding: vmcnt low bits 3:0 and high bits 15:14).
-template <int N>
-__device__ __forceinline__ void vmcnt_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
 __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with the LDS and export counters unconstrained (gfx9
+// encoding: vmcnt low bits 3:0 and high bits 15:14).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
 // Position of row 16*ts + l16's scale within a K step's TM floats.  With
@@ -269,7 +304,8 @@ struct Lds {
 // tile n (band row * kdim) within the expert's weight block `wrsrc`; kdim is
 // the K extent in bytes (H for GEMM1, I for GEMM2).
 template <int TM, bool GATED, bool PACKED, typename WBand, typename Epi>
-__device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
+__device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& tb,
+                                            const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
                                             __amdgpu_buffer_rsrc_t wrsrc, int kdim, int sb_sel, int KT, int nn,
                                             int tid, int lane, v4f (&acc)[Cfg<TM>::TS][2], WBand wband, Epi epi) {
   using C = Cfg<TM>;
@@ -281,15 +317,10 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
   // this lane's two 16-byte reads of token sub-tile 0 (sub-tile ts adds 2048 bytes:
   // the swizzle key depends on the row's low four bits only)
   const int r0 = lane & 15, g = lane >> 4;
-  // four token buffers, separate LDS objects so the compiler tracks each one's
-  // direct-to-LDS loads on its own; step j reads buffer j % 4 (= its ring slot)
-  __shared__ __attribute__((aligned(1024))) uint8_t tb0[C::A_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t tb1[C::A_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t tb2[C::A_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t tb3[C::A_BYTES];
-  auto tbuf = [&](int i) __attribute__((always_inline)) -> uint8_t* {
-    return i == 0 ? tb0 : (i == 1 ? tb1 : (i == 2 ? tb2 : tb3));
-  };
+  // step j reads token buffer j % 4 (= its ring slot); the buffers are
+  // separate LDS objects, so the compiler tracks each one's direct-to-LDS
+  // loads on its own
+  auto tbuf = [&](int i) __attribute__((always_inline)) -> uint8_t* { return tb.b[i]; };
   const int o0 = swz(r0, g), o1 = swz(r0, g + 4);
   auto frag = [&](int bi, int ts) __attribute__((always_inline)) -> v8i {
     const uint8_t* t = tbuf(bi);
@@ -440,21 +471,20 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const uint8_t* const 
 }
 
 // ------------------------------------------------------------------------------------------
-// GEMM1 + SwiGLU + 1x128 FP8 requantisation over a run of N tiles of 128 I columns.
+// GEMM1 + SwiGLU + 1x128 FP8 requantisation over a run of N tiles of 128 I
+// columns, for a tile body of TM rows; rows tc.h.. of the body are past the
+// expert's segment and are treated as padding (read token 0, never stored).
 template <int TM, bool PACKED>
-__global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
-    const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
-    const float* __restrict__ w13_scale, const int32_t* __restrict__ padded,
-    const int32_t* __restrict__ sorted_src, int E, int K, int H, int I, int NB, uint8_t* __restrict__ q,
+__device__ __forceinline__ void gemm1_tile(
+    uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ x,
+    const float* __restrict__ x_scale, const uint8_t* __restrict__ w13, const float* __restrict__ w13_scale,
+    const int32_t* __restrict__ sorted_src, int K, int H, int I, int NB, uint8_t* __restrict__ q,
     float* __restrict__ q_scale) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
-  const int NT = I / 128, NG = (NT + NB - 1) / NB;
-  TileCoord tc;
-  if (!tile_coord<TM>(padded, sorted_src, E, NG, tc)) return;
+  const int NT = I / 128;
   const int nt0 = tc.run * NB, nn = min(NB, NT - nt0);
+  const int h = tc.h;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -471,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
     const int qc = C::block_of(tid >> 6, i) * 64 + lane;
     const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
-    const int src = sorted_src[tc.p0 + r];
+    const int src = r < h ? sorted_src[tc.p0 + r] : -1;
     const size_t tok = src >= 0 ? (size_t)(src / K) : 0;  // a pad row reads token 0; never stored
     a_src[i] = x + tok * H + c * 16;
   }
@@ -489,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
     return sexp + (size_t)(which ? IB + nt0 + n : nt0 + n) * HB;
   }, tid);
   stage_token_scales<TM>(SAs, KT, [&](int r) -> const float* {
-    const int src = sorted_src[tc.p0 + r];
+    const int src = r < h ? sorted_src[tc.p0 + r] : -1;
     return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
   }, tid);
 
@@ -516,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
     step_barrier();
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
+      if (16 * ts >= h) break;   // sub-tiles past the segment (h is a multiple of 16)
       const int row = 16 * ts + l16;
       float amax = 0.f;
 #pragma unroll
@@ -534,25 +565,53 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, true, PACKED>(smem, a_src, wrsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
+  ws_mainloop<TM, true, PACKED>(smem, tb, a_src, wrsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
+}
+
+// The token buffers are the kernel's; each workgroup runs the smallest tile
+// body that covers its tile's rows (bodies up to TMAX).
+#define FP8MOE_TOKEN_BUFFERS(TMAX)                                                \
+  __shared__ __attribute__((aligned(1024))) uint8_t tb0[Cfg<TMAX>::A_BYTES];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t tb1[Cfg<TMAX>::A_BYTES];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t tb2[Cfg<TMAX>::A_BYTES];      \
+  __shared__ __attribute__((aligned(1024))) uint8_t tb3[Cfg<TMAX>::A_BYTES];      \
+  const TokenBuffers tb{{tb0, tb1, tb2, tb3}}
+
+template <int TMAX, bool PACKED>
+__global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
+    const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
+    const float* __restrict__ w13_scale, const int32_t* __restrict__ padded,
+    const int32_t* __restrict__ sorted_src, int E, int K, int H, int I, int NB, uint8_t* __restrict__ q,
+    float* __restrict__ q_scale) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NT = I / 128, NG = (NT + NB - 1) / NB;
+  TileCoord tc;
+  if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
+  FP8MOE_TOKEN_BUFFERS(TMAX);
+#define FP8MOE_G1_BODY(TMV) \
+  gemm1_tile<TMV, PACKED>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB, q, q_scale)
+  if constexpr (TMAX >= 128) if (tc.h > 64) { FP8MOE_G1_BODY(128); return; }
+  if constexpr (TMAX >= 64) if (tc.h > 32) { FP8MOE_G1_BODY(64); return; }
+  if constexpr (TMAX >= 32) if (tc.h > 16) { FP8MOE_G1_BODY(32); return; }
+  FP8MOE_G1_BODY(16);
+#undef FP8MOE_G1_BODY
 }
 
 // ------------------------------------------------------------------------------------------
-// GEMM2 with the top-k weight epilogue, over a run of N tiles of 256 H columns.
+// GEMM2 with the top-k weight epilogue, over a run of N tiles of 256 H
+// columns, for a tile body of TM rows; rows tc.h.. of the body are past the
+// expert's segment (they re-read the tile's last row and are never stored).
 template <int TM, bool PACKED>
-__global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ w2,
-    const float* __restrict__ w2_scale, const float* __restrict__ topk_weights,
-    const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src, int E, int H, int I, int NB,
+__device__ __forceinline__ void gemm2_tile(
+    uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ q,
+    const float* __restrict__ q_scale, const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
+    const float* __restrict__ topk_weights, const int32_t* __restrict__ sorted_src, int H, int I, int NB,
     uint16_t* __restrict__ Y) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
-  const int NT = (H + kTN - 1) / kTN, NG = (NT + NB - 1) / NB;
-  TileCoord tc;
-  if (!tile_coord<TM>(padded, sorted_src, E, NG, tc)) return;
+  const int NT = (H + kTN - 1) / kTN;
   const int nt0 = tc.run * NB, nn = min(NB, NT - nt0);
+  const int h = tc.h;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -569,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
     const int qc = C::block_of(tid >> 6, i) * 64 + lane;
     const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
-    a_src[i] = q + (size_t)(tc.p0 + r) * I + c * 16;
+    a_src[i] = q + (size_t)(tc.p0 + min(r, h - 1)) * I + c * 16;
   }
   // wave w owns H columns [n0 + 32w, n0 + 32w + 32) of N tile n (n0 = 256 (nt0 + n)),
   // its two operands 16 columns each; rows past H read a valid row, outputs masked
@@ -589,11 +648,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   }, tid);
   stage_token_scales<TM>(SAs, KT, [&](int r) -> const float* {
     const int p = tc.p0 + r;
-    return sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
+    return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
   }, tid);
   // source row and top-k weight of each tile row, for the epilogues
   for (int r = tid; r < TM; r += kThreads) {
-    const int src = sorted_src[tc.p0 + r];
+    const int src = r < h ? sorted_src[tc.p0 + r] : -1;
     srow[r] = src;
     wrow_w[r] = src >= 0 ? topk_weights[src] : 0.f;
   }
@@ -622,8 +681,29 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, false, PACKED>(smem, a_src, wrsrc, I, wave >> 2, KT, nn, tid, lane, acc, wband, epi);
+  ws_mainloop<TM, false, PACKED>(smem, tb, a_src, wrsrc, I, wave >> 2, KT, nn, tid, lane, acc, wband, epi);
 }
+
+template <int TMAX, bool PACKED>
+__global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ w2,
+    const float* __restrict__ w2_scale, const float* __restrict__ topk_weights,
+    const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src, int E, int H, int I, int NB,
+    uint16_t* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NT = (H + kTN - 1) / kTN, NG = (NT + NB - 1) / NB;
+  TileCoord tc;
+  if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
+  FP8MOE_TOKEN_BUFFERS(TMAX);
+#define FP8MOE_G2_BODY(TMV) \
+  gemm2_tile<TMV, PACKED>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB, Y)
+  if constexpr (TMAX >= 128) if (tc.h > 64) { FP8MOE_G2_BODY(128); return; }
+  if constexpr (TMAX >= 64) if (tc.h > 32) { FP8MOE_G2_BODY(64); return; }
+  if constexpr (TMAX >= 32) if (tc.h > 16) { FP8MOE_G2_BODY(32); return; }
+  FP8MOE_G2_BODY(16);
+#undef FP8MOE_G2_BODY
+}
+#undef FP8MOE_TOKEN_BUFFERS
 
 // ------------------------------------------------------------------------------------------
 // N tiles per workgroup: about 8 workgroups per CU (load balance); for a
@@ -670,8 +750,12 @@ static int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
   return (NT + ng - 1) / ng;
 }
 
-static unsigned grid_for(int64_t cap, int tm, int ng) {
-  const int64_t items = (cap / tm) * ng;
+// Workgroups for every possible tile: each tile holds >= 16 rows, and an
+// expert has at most one tile shorter than tm.  Those past the actual tile
+// count (known on the device only) exit at once.
+static unsigned grid_for(const GroupedRows& g, int tm, int ng) {
+  const int64_t by_rows = g.cap / 16, by_experts = g.cap / tm + g.E;
+  const int64_t items = (by_rows < by_experts ? by_rows : by_experts) * ng;
   const int64_t b = (items + kNumXcd - 1) / kNumXcd * kNumXcd;
   return (unsigned)(b > 0 ? b : kNumXcd);
 }
@@ -706,7 +790,7 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
   const int NT = I / 128, NB = fit_run(g, tile_m, NT, H / kKB), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes(tile_m, H / kKB, NB);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(g.cap, tile_m, NG)), block(kThreads);
+  const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
 #define FP8MOE_G1(TMV)                                                                                 \
   if (packed)                                                                                          \
     hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, true>), grid, block, lds, stream, x, x_scale, w13, \
@@ -742,7 +826,7 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
   const int NT = (H + kTN - 1) / kTN, NB = fit_run(g, tile_m, NT, I / kKB), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes(tile_m, I / kKB, NB);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(g.cap, tile_m, NG)), block(kThreads);
+  const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
 #define FP8MOE_G2(TMV)                                                                                    \
   if (packed)                                                                                             \
     hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, true>), grid, block, lds, stream, q, q_scale, w2, w2_scale, \

@@ -133,15 +133,20 @@ def moe_fused_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weigh
 
 
 def gemm1_swiglu_quant(x, x_scale, w13, w13_scale, route, T, K, align, tile_m=-1,
-                       weight_layout=WEIGHTS_ROW_MAJOR):
-    """GEMM1 + SwiGLU + requant stage over a routing result.  Returns (q uint8 [cap, I], q_scale [cap, I/128])."""
+                       weight_layout=WEIGHTS_ROW_MAJOR, q=None, q_scale=None):
+    """GEMM1 + SwiGLU + requant stage over a routing result.  Returns (q uint8 [cap, I], q_scale [cap, I/128]);
+    q / q_scale given: written in place (rows the stage does not write keep their contents)."""
     x, w13 = _u8(x), _u8(w13)
     E, I2, H = w13.shape
     I = I2 // 2
     cap = route["sorted_src"].numel()
     dev = x.device
-    q = torch.zeros((cap, I), dtype=torch.uint8, device=dev)
-    qs = torch.zeros((cap, I // 128), dtype=torch.float32, device=dev)
+    q = torch.zeros((cap, I), dtype=torch.uint8, device=dev) if q is None else q
+    qs = torch.zeros((cap, I // 128), dtype=torch.float32, device=dev) if q_scale is None else q_scale
+    _need(q, torch.uint8, "q", 2)
+    _need(qs, torch.float32, "q_scale", 2)
+    if tuple(q.shape) != (cap, I) or tuple(qs.shape) != (cap, I // 128):
+        raise ValueError("q / q_scale must be [cap, I] / [cap, I/128]")
     check(lib().moe_gemm1_swiglu_quant(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(route["padded_indptr"]),
                                        _p(route["sorted_src"]), T, H, I, E, K, align, _p(q), _p(qs), cap, tile_m,
                                        weight_layout, _stream(dev)))
@@ -149,13 +154,17 @@ def gemm1_swiglu_quant(x, x_scale, w13, w13_scale, route, T, K, align, tile_m=-1
 
 
 def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
-                   weight_layout=WEIGHTS_ROW_MAJOR):
-    """GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H] (rows of dropped slots are zero here)."""
+                   weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
+    """GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H]; rows of dropped slots are not written
+    (zero when Y is allocated here)."""
     w2 = _u8(w2)
     E, H, I = w2.shape
     cap = route["sorted_src"].numel()
     dev = q.device
-    Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev)
+    Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev) if Y is None else Y
+    _need(Y, torch.bfloat16, "Y", 2)
+    if tuple(Y.shape) != (T * K, H):
+        raise ValueError("Y must be [T*K, H]")
     check(lib().moe_gemm2_weighted(_p(q), _p(q_scale), _p(w2), _p(w2_scale), _p(route["padded_indptr"]),
                                    _p(route["sorted_src"]), _p(topk_weights), T, H, I, E, K, align, _p(Y), cap,
                                    tile_m, tile_n, weight_layout, _stream(dev)))

@@ -114,9 +114,12 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *   workspace / workspace_bytes       device scratch of at least
  *                                     moe_fused_fp8_workspace_size() bytes,
  *                                     256-byte aligned, owned by the caller
- *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128: token rows
- *            per GEMM tile (16 is the swap-AB class: tokens on the 16-wide
- *            MFMA side); applies to both GEMMs when given
+ *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128: the
+ *            largest number of token rows per GEMM tile (16 is the swap-AB
+ *            class: tokens on the 16-wide MFMA side); applies to both GEMMs
+ *            when given.  The routing pads each expert to 16 rows only, and
+ *            an expert's last tile is the smallest of 16/32/64/128 rows that
+ *            holds the rest of its rows
  *   tile_n   -1 (auto) or 256: GEMM2 output columns per tile (GEMM1 always
  *            covers 128 columns of I, one requantisation block, per tile)
  *   weight_layout  FP8MOE_WEIGHTS_ROW_MAJOR (w13, w2 as above) or
@@ -139,8 +142,11 @@ int moe_fused_fp8(const void* x, const float* x_scale,
 
 /* ---------------------------------------------------------------- stages of the fused layer
  * The three compute stages moe_fused_fp8 runs after routing, exposed so each
- * can be checked on its own.  They consume moe_route_permute's outputs (with
- * `align` a multiple of the tile_m used).
+ * can be checked on its own.  They consume moe_route_permute's outputs (any
+ * align).  Each expert's padded segment is cut into tiles of tile_m rows from
+ * its start; the last tile, if shorter, runs as the smallest of 16/32/64/128
+ * rows that holds it, and the rows of that tile past the segment are
+ * computed as padding and never stored.
  *
  * moe_gemm1_swiglu_quant: for every padded row p < padded_indptr[E] of
  *   expert e (padded_indptr[e] <= p < padded_indptr[e+1]) with source row
@@ -154,9 +160,8 @@ int moe_fused_fp8(const void* x, const float* x_scale,
  * moe_gemm2_weighted: for every row p with src = sorted_src[p] >= 0:
  *     Y[src, :] = bf16( topk_weights[src] * (deq(q[p]) . w2[e]^T) ).
  *   Y bf16 [T*K, H]; rows of dropped slots are not written.
- *   `align` is the one the routing was built with; tile_m (-1 auto, else
- *   16/32/64/128) must divide it (auto picks the largest allowed size not
- *   above the cost model's choice).  cap is the length of sorted_src.
+ *   `align` is the one the routing was built with; tile_m is -1 (auto: the
+ *   cost model's choice) or 16/32/64/128.  cap is the length of sorted_src.
  * moe_combine: out[t, :] = bf16( sum over j with 0 <= topk_ids[t, j] < E of
  *   Y[t*K + j, :] ) summed in fp32 in ascending j; zeros for tokens with no
  *   valid slot.

@@ -109,7 +109,7 @@ def test_stage_validation():
                                               k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1),
                                               k.get("layout", 0), NULL)
     assert g1(align=24) == E_ALIGN
-    assert g1(align=16, tm=32) == E_TILE          # tile must divide align
+    assert g1(align=16, tm=48) == E_TILE          # tile heights 16/32/64/128 only
     assert g1(cap=-1) == E_SHAPE
     assert g1(T=0) == OK
     assert g1(layout=3) == E_SHAPE
@@ -117,7 +117,7 @@ def test_stage_validation():
                                           k.get("align", 16), FAKE, 100, k.get("tm", -1), k.get("tn", -1),
                                           k.get("layout", 0), NULL)
     assert g2(tn=64) == E_TILE
-    assert g2(align=32, tm=64) == E_TILE
+    assert g2(align=32, tm=96) == E_TILE
     assert g2(layout=2) == E_SHAPE
     assert L.moe_combine(FAKE, FAKE, 4, 100, 4, 2, FAKE, NULL) == E_ALIGN
     assert L.moe_combine(FAKE, FAKE, 4, 128, 4, 9, FAKE, NULL) == E_TOPK
