@@ -72,9 +72,13 @@ struct Cfg {
   static constexpr int D = 4;                                        // weight ring depth = token buffers
   static constexpr int A_BYTES = TM * kKB;                           // token rows of one K step
   // direct-to-LDS loads write 1 KB (64 lanes x 16 bytes) each: NBLK per K
-  // step, A_PER_WAVE issued by each wave (below 8 blocks waves repeat blocks)
+  // step, A_PER_WAVE issued by each wave (where 8 * A_PER_WAVE > NBLK, waves
+  // repeat blocks, so every wave issues the same number of loads)
   static constexpr int NBLK = A_BYTES / 1024;
-  static constexpr int A_PER_WAVE = NBLK >= kWaves ? NBLK / kWaves : 1;
+  static constexpr int A_PER_WAVE = (NBLK + kWaves - 1) / kWaves;
+  // floats per K step of the token scales in LDS (scale_slot order): whole
+  // 64-float quad groups once TS >= 4
+  static constexpr int TSLOT = TS >= 4 ? (TS + 3) / 4 * 64 : TM;
   __host__ __device__ static constexpr int block_of(int wave, int i) { return (wave * A_PER_WAVE + i) % NBLK; }
 };
 
@@ -126,10 +130,14 @@ __device__ __forceinline__ v8i weight_frag(__amdgpu_buffer_rsrc_t rsrc, int voff
 // the 8 XCDs round-robin), so the M tiles that share one expert's weight
 // tiles start together on one XCD and stream them through its L2 in step:
 // the weights leave HBM once.
-// Tile h of expert e covers rows [p0, p0 + h) of its padded segment: the
-// segment is cut into tiles of TMAX rows from its start, so only its last
-// tile can be shorter (a multiple of the route alignment, >= 16 rows).
-struct TileCoord { int mt, run, e, p0, h; };
+// An expert's padded segment (len rows, a multiple of 16) is cut into
+// n = ceil(len / TMAX) tiles of equal height tm = 16 * ceil(len / (16 n))
+// <= TMAX; tile mt covers rows [p0, p0 + h) with p0 = start + mt * tm and
+// h = min(tm, len - mt * tm) > 0.  Every tile of the expert runs the body of
+// tm rows (rows h.. of the last one are padding), so the tiles that stream
+// the same weights run at the same pace and share them through L2, and at
+// most 15 rows per tile are computed beyond the segment.
+struct TileCoord { int mt, run, e, p0, h, tm; };
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -181,11 +189,13 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
   const int e = __builtin_amdgcn_readfirstlane(wave_sum(cnt));
   const int first = __builtin_amdgcn_readfirstlane(wave_sum(before));
   const int nm = expert_tiles<TMAX>(padded, e);   // >= 1: the expert owns tile t
+  const int len = padded[e + 1] - padded[e];
   const int j = L - NG * first;
   tc.run = j / nm;
   tc.mt = j - tc.run * nm;
-  tc.p0 = padded[e] + tc.mt * TMAX;
-  tc.h = min(TMAX, padded[e + 1] - tc.p0);
+  tc.tm = ((len + nm - 1) / nm + 15) / 16 * 16;
+  tc.p0 = padded[e] + tc.mt * tc.tm;
+  tc.h = min(tc.tm, len - tc.mt * tc.tm);
   tc.e = e;
   return sorted_src[tc.p0] >= 0;  // false: segment padding only, nothing to compute
 }
@@ -228,18 +238,19 @@ __device__ __forceinline__ int scale_slot(int l16, int ts) {
   else return l16 * TS + ts;
 }
 
-// The token scales of the M tile -> LDS as [kb][TM] in scale_slot order.
+// The token scales of the M tile -> LDS as [kb][TSLOT] in scale_slot order.
 // row_scale(r) gives the row's scale vector (nullptr for a pad row).  Each
 // thread keeps one row and walks its K steps, so after the one row lookup
 // its loads are independent.
 template <int TM, typename RowScale>
 __device__ __forceinline__ void stage_token_scales(float* SAs, int KT, RowScale row_scale, int tid) {
-  constexpr int TS = Cfg<TM>::TS;
+  constexpr int TS = Cfg<TM>::TS, TSLOT = Cfg<TM>::TSLOT;
   constexpr int TPR = kThreads / TM;   // threads per row
   const int r = tid / TPR, part = tid % TPR;
+  if (r >= TM) return;
   const float* rs = row_scale(r);
   float* dst = SAs + scale_slot<TS>(r & 15, r >> 4);
-  for (int kb = part; kb < KT; kb += TPR) dst[kb * TM] = rs ? rs[kb] : 0.f;
+  for (int kb = part; kb < KT; kb += TPR) dst[kb * TSLOT] = rs ? rs[kb] : 0.f;
 }
 
 // The two weight block-scale rows of each N tile of the run -> LDS as
@@ -260,9 +271,11 @@ template <int TS>
 __device__ __forceinline__ void read_token_scales(const float* p, float (&sa)[TS]) {
   if constexpr (TS >= 4) {
 #pragma unroll
-    for (int q = 0; q < TS / 4; ++q) {
+    for (int q = 0; q < (TS + 3) / 4; ++q) {
       const v4f v = *reinterpret_cast<const v4f*>(p + 64 * q);
-      sa[4 * q] = v[0]; sa[4 * q + 1] = v[1]; sa[4 * q + 2] = v[2]; sa[4 * q + 3] = v[3];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * q + r < TS) sa[4 * q + r] = v[r];
     }
   } else {
 #pragma unroll
@@ -271,16 +284,18 @@ __device__ __forceinline__ void read_token_scales(const float* p, float (&sa)[TS
 }
 
 // Dynamic LDS layout (the four token buffers [TM][128] are static arrays of
-// the main loop): the M tile's token scales [KT][TM], the run's weight block
+// the main loop): the M tile's token scales [KT][TSLOT], the run's weight block
 // scales [NB][KT][2], the epilogue scratch (GEMM1: per-wave row max [8][TM];
 // GEMM2: source row and top-k weight [2][TM]).
 template <int TM>
 struct Lds {
   __host__ __device__ static constexpr size_t bytes(int KT, int NB) {
-    return 4 * (size_t)TM * KT + 8 * (size_t)NB * KT + 4 * (size_t)kWaves * TM;
+    return 4 * (size_t)Cfg<TM>::TSLOT * KT + 8 * (size_t)NB * KT + 4 * (size_t)kWaves * TM;
   }
   __device__ static float* token_scales(uint8_t* smem) { return reinterpret_cast<float*>(smem); }
-  __device__ static float* weight_scales(uint8_t* smem, int KT) { return token_scales(smem) + (size_t)TM * KT; }
+  __device__ static float* weight_scales(uint8_t* smem, int KT) {
+    return token_scales(smem) + (size_t)Cfg<TM>::TSLOT * KT;
+  }
   __device__ static float* scratch(uint8_t* smem, int KT, int NB) { return weight_scales(smem, KT) + 2 * (size_t)NB * KT; }
 };
 
@@ -374,7 +389,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   float sa[TS];
   float sb0, sb1;
   auto read_scales = [&](int n, int k) __attribute__((always_inline)) {
-    read_token_scales<TS>(SAs + (size_t)k * TM + scale_slot<TS>(r0, 0), sa);
+    read_token_scales<TS>(SAs + (size_t)k * C::TSLOT + scale_slot<TS>(r0, 0), sa);
     const float* b = SBs + 2 * ((size_t)n * KT + k);
     if constexpr (GATED) {
       const v2f v = *reinterpret_cast<const v2f*>(b);
@@ -568,14 +583,27 @@ __device__ __forceinline__ void gemm1_tile(
   ws_mainloop<TM, true, PACKED>(smem, tb, a_src, wrsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
 }
 
-// The token buffers are the kernel's; each workgroup runs the smallest tile
-// body that covers its tile's rows (bodies up to TMAX).
+// The token buffers are the kernel's; each workgroup runs the tile body of
+// its expert's tile height (16, 32, ..., TMAX rows).
 #define FP8MOE_TOKEN_BUFFERS(TMAX)                                                \
   __shared__ __attribute__((aligned(1024))) uint8_t tb0[Cfg<TMAX>::A_BYTES];      \
   __shared__ __attribute__((aligned(1024))) uint8_t tb1[Cfg<TMAX>::A_BYTES];      \
   __shared__ __attribute__((aligned(1024))) uint8_t tb2[Cfg<TMAX>::A_BYTES];      \
   __shared__ __attribute__((aligned(1024))) uint8_t tb3[Cfg<TMAX>::A_BYTES];      \
   const TokenBuffers tb{{tb0, tb1, tb2, tb3}}
+
+// one uniform branch per workgroup on its tile height tc.tm
+#define FP8MOE_BODIES(BODY)                                                        \
+  switch (tc.tm) {                                                                 \
+    case 16: BODY(16); break;                                                      \
+    case 32: if constexpr (TMAX >= 32) { BODY(32); } break;                        \
+    case 48: if constexpr (TMAX >= 48) { BODY(48); } break;                        \
+    case 64: if constexpr (TMAX >= 64) { BODY(64); } break;                        \
+    case 80: if constexpr (TMAX >= 80) { BODY(80); } break;                        \
+    case 96: if constexpr (TMAX >= 96) { BODY(96); } break;                        \
+    case 112: if constexpr (TMAX >= 112) { BODY(112); } break;                     \
+    default: if constexpr (TMAX >= 128) { BODY(128); } break;                      \
+  }
 
 template <int TMAX, bool PACKED>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
@@ -590,10 +618,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   FP8MOE_TOKEN_BUFFERS(TMAX);
 #define FP8MOE_G1_BODY(TMV) \
   gemm1_tile<TMV, PACKED>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB, q, q_scale)
-  if constexpr (TMAX >= 128) if (tc.h > 64) { FP8MOE_G1_BODY(128); return; }
-  if constexpr (TMAX >= 64) if (tc.h > 32) { FP8MOE_G1_BODY(64); return; }
-  if constexpr (TMAX >= 32) if (tc.h > 16) { FP8MOE_G1_BODY(32); return; }
-  FP8MOE_G1_BODY(16);
+  FP8MOE_BODIES(FP8MOE_G1_BODY)
 #undef FP8MOE_G1_BODY
 }
 
@@ -697,13 +722,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   FP8MOE_TOKEN_BUFFERS(TMAX);
 #define FP8MOE_G2_BODY(TMV) \
   gemm2_tile<TMV, PACKED>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB, Y)
-  if constexpr (TMAX >= 128) if (tc.h > 64) { FP8MOE_G2_BODY(128); return; }
-  if constexpr (TMAX >= 64) if (tc.h > 32) { FP8MOE_G2_BODY(64); return; }
-  if constexpr (TMAX >= 32) if (tc.h > 16) { FP8MOE_G2_BODY(32); return; }
-  FP8MOE_G2_BODY(16);
+  FP8MOE_BODIES(FP8MOE_G2_BODY)
 #undef FP8MOE_G2_BODY
 }
 #undef FP8MOE_TOKEN_BUFFERS
+#undef FP8MOE_BODIES
 
 // ------------------------------------------------------------------------------------------
 // N tiles per workgroup: about 8 workgroups per CU (load balance); for a

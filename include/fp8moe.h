@@ -118,8 +118,8 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *            largest number of token rows per GEMM tile (16 is the swap-AB
  *            class: tokens on the 16-wide MFMA side); applies to both GEMMs
  *            when given.  The routing pads each expert to 16 rows only, and
- *            an expert's last tile is the smallest of 16/32/64/128 rows that
- *            holds the rest of its rows
+ *            the GEMMs cut each expert into ceil(rows / tile_m) tiles of
+ *            equal height (a multiple of 16, at most tile_m)
  *   tile_n   -1 (auto) or 256: GEMM2 output columns per tile (GEMM1 always
  *            covers 128 columns of I, one requantisation block, per tile)
  *   weight_layout  FP8MOE_WEIGHTS_ROW_MAJOR (w13, w2 as above) or
@@ -143,10 +143,10 @@ int moe_fused_fp8(const void* x, const float* x_scale,
 /* ---------------------------------------------------------------- stages of the fused layer
  * The three compute stages moe_fused_fp8 runs after routing, exposed so each
  * can be checked on its own.  They consume moe_route_permute's outputs (any
- * align).  Each expert's padded segment is cut into tiles of tile_m rows from
- * its start; the last tile, if shorter, runs as the smallest of 16/32/64/128
- * rows that holds it, and the rows of that tile past the segment are
- * computed as padding and never stored.
+ * align).  Each expert's padded segment of len rows is cut into
+ * n = ceil(len / tile_m) tiles of equal height 16 * ceil(len / (16 n)); rows
+ * of the last tile past the segment are computed as padding and never
+ * stored.
  *
  * moe_gemm1_swiglu_quant: for every padded row p < padded_indptr[E] of
  *   expert e (padded_indptr[e] <= p < padded_indptr[e+1]) with source row

@@ -1,14 +1,15 @@
 """Tile heights of the grouped GEMMs on the GPU.
 
-An expert's padded segment is covered by tiles of tile_m rows from its start;
-its last tile runs as the smallest of 16/32/64/128 rows that holds the rest,
-and rows of that tile past the segment are padding that is never stored.  Each
+An expert's padded segment of len rows is cut into ceil(len / tile_m) tiles
+of equal height (a multiple of 16, at most tile_m); rows of the last tile past
+the segment are padding that is never stored.  Each
 output row's arithmetic (its K order and scale folds) does not depend on the
 tile it sits in, so every (align, tile_m) pair must give bit-identical q rows,
 Y rows and layer outputs, and one of them is checked against the oracle.
 
 Problem: the Zipf-skewed 128-expert configuration at T=512 (experts from a
-handful of rows to several 128-row tiles, so tails of every height occur), with
+handful of rows to several 128-row tiles, so tile heights of 16 to 128 rows
+and short last tiles occur), with
 a few dropped slots; I=768 gives GEMM2 six K steps, which exercises the
 partial round of the four-deep operand ring.
 """
@@ -61,7 +62,7 @@ def _stages(pd, align, tm):
 
 
 def test_tail_heights_are_covered(skewed512):
-    """The problem really has experts whose last 128-row tile is short, of many heights."""
+    """The problem really has experts that span several 128-row tiles with a short remainder."""
     ph, _ = skewed512
     ids = ph.topk_ids.numpy().ravel()
     c = np.bincount(ids[(ids >= 0) & (ids < ph.E)], minlength=ph.E)
