@@ -51,6 +51,9 @@ sys.path.insert(0, ROOT)
 import fp8_block_scaled_moe_amd as fm  # noqa: E402
 import synth  # noqa: E402
 
+# tile height (rows) each GEMM runs the cost model's 128-row class with
+CLASS128_TILE = {"gemm1": 128, "gemm2": 160}
+
 METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roofline"
 
 # HBM counters of the dominant kernel (GEMM1 at T=8192) and of the 2 GiB stream
@@ -224,16 +227,17 @@ def skewed_bench(iters=10):
         ws = fm.alloc_workspace(T, d["H"], d["I"], d["E"], d["K"], "cuda")
         o = torch.empty((T, d["H"]), dtype=torch.bfloat16, device="cuda")
         res = {}
-        for tm in (-1, 16, 32, 64, 128):
+        forced = (16, 32, 64, 128, 160)   # 160: GEMM1 runs 144 (its largest body)
+        for tm in (-1,) + forced:
             fn = lambda: fused(p, o, ws, tile_m=tm)
             fn()
             res[tm] = cold_time_ms(fn, iters)
         nbytes, active = algorithmic_bytes(p)
-        best = min(res[t] for t in (16, 32, 64, 128))
+        best = min(res[t] for t in forced)
         auto_tm = fm.select_tile(T * d["K"], d["I"], d["H"], d["E"], 256, True)[0]
-        out.append({"T": T, "active_experts": int(active), "auto_tile_m_gemm1": auto_tm,
+        out.append({"T": T, "active_experts": int(active), "auto_tile_class_gemm1": auto_tm,
                     "us_auto": round(res[-1] * 1e3, 2),
-                    "us_by_tile_m": {str(t): round(res[t] * 1e3, 2) for t in (16, 32, 64, 128)},
+                    "us_by_tile_m": {str(t): round(res[t] * 1e3, 2) for t in forced},
                     "regret": round(res[-1] / best, 3), "GBps_auto": round(nbytes / (res[-1] * 1e-3) / 1e9, 1),
                     "TFLOPs_auto": round(6.0 * T * d["K"] * d["H"] * d["I"] / (res[-1] * 1e-3) / 1e12, 2)})
     return out
@@ -259,8 +263,12 @@ def stage_times(p, steps, warmup):
     layout as the fused call; outputs preallocated, so each timing is the stage's kernels only)."""
     T, H, I, E, K = p.T, p.H, p.I, p.E, p.K
     R = T * K
-    tm1, _ = fm.select_tile(R, I, H, E, 256, True)
-    tm2, _ = fm.select_tile(R, H, I, E, 256, False)
+    # tile_m -1 as in the fused call: the cost model's class, the 128-row class
+    # running with each GEMM's largest tile body
+    cls1, _ = fm.select_tile(R, I, H, E, 256, True)
+    cls2, _ = fm.select_tile(R, H, I, E, 256, False)
+    eff1, eff2 = (CLASS128_TILE["gemm1"] if cls1 == 128 else cls1), (CLASS128_TILE["gemm2"] if cls2 == 128 else cls2)
+    tm1 = tm2 = -1
     align = 16
     L = fm.WEIGHTS_MFMA_TILED
     route = fm.route_permute(p.topk_ids, E, align)
@@ -274,7 +282,7 @@ def stage_times(p, steps, warmup):
         "gemm2_ms": event_time_ms(lambda: fm.gemm2_weighted(q, qs, p.w2_p, p.w2_s, route, p.topk_weights, T, K,
                                                             align, tile_m=tm2, weight_layout=L, Y=Y), steps, warmup),
         "combine_ms": event_time_ms(lambda: fm.combine(Y, p.topk_ids, E), steps, warmup),
-        "tile_m_gemm1": tm1, "tile_m_gemm2": tm2,
+        "tile_m_gemm1": eff1, "tile_m_gemm2": eff2, "tile_class_gemm1": cls1, "tile_class_gemm2": cls2,
     }
     return out
 

@@ -39,7 +39,7 @@ int hip_fail(hipError_t err, const char* what) {
   return fail(FP8MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
-bool valid_tile_m(int t) { return t == 16 || t == 32 || t == 64 || t == 128; }
+bool valid_tile_m(int t) { return t == 16 || t == 32 || t == 64 || t == 128 || t == 144 || t == 160; }
 bool valid_align(int a) { return a == 16 || a == 32 || a == 64 || a == 128; }
 bool valid_layout(int l) { return l == FP8MOE_WEIGHTS_ROW_MAJOR || l == FP8MOE_WEIGHTS_MFMA_TILED; }
 
@@ -99,9 +99,14 @@ int device_num_cu() {
   return n;
 }
 
+// Largest tile height a GEMM runs with: the requested one (GEMM1 at most
+// 144 rows), else the cost model's class, the 128-row class running with
+// kClass128Tile* rows.
 int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
-  if (requested != -1) return requested;
-  return select_tile_m(R, n, k, E, device_num_cu(), mi355x_classes(gated));
+  const int cap = gated ? kMaxTileGemm1 : kMaxTileGemm2;
+  if (requested != -1) return requested < cap ? requested : cap;
+  const int cls = select_tile_m(R, n, k, E, device_num_cu(), mi355x_classes(gated));
+  return cls == 128 ? (gated ? kClass128TileGemm1 : kClass128TileGemm2) : cls;
 }
 
 }  // namespace
@@ -168,7 +173,7 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   const bool packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
   if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
   if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
   if (T == 0) return ok();
   if (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out)
@@ -222,7 +227,7 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13,
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
   if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
   if (T == 0 || cap == 0) return ok();
   if (!x || !x_scale || !w13 || !w13_scale || !padded_indptr || !sorted_src || !q || !q_scale)
@@ -245,7 +250,7 @@ int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, cons
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
   if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
   if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
   if (T == 0 || cap == 0) return ok();

@@ -602,7 +602,9 @@ __device__ __forceinline__ void gemm1_tile(
     case 80: if constexpr (TMAX >= 80) { BODY(80); } break;                        \
     case 96: if constexpr (TMAX >= 96) { BODY(96); } break;                        \
     case 112: if constexpr (TMAX >= 112) { BODY(112); } break;                     \
-    default: if constexpr (TMAX >= 128) { BODY(128); } break;                      \
+    case 128: if constexpr (TMAX >= 128) { BODY(128); } break;                     \
+    case 144: if constexpr (TMAX >= 144) { BODY(144); } break;                     \
+    default: if constexpr (TMAX >= 160) { BODY(160); } break;                      \
   }
 
 template <int TMAX, bool PACKED>
@@ -751,24 +753,19 @@ static int run_length(const GroupedRows& g, int tm, int NT, int KT) {
 }
 
 size_t gemm_lds_bytes(int tile_m, int KT, int NB);
-// dynamic LDS beside the largest tile's four static token buffers
-constexpr size_t kMaxDynLds = kMaxGemmLds - 4 * (size_t)Cfg<128>::A_BYTES;
+// dynamic LDS beside the four static token buffers of a kernel with tiles of
+// up to tm rows
+static size_t max_dyn_lds(int tm) { return kMaxGemmLds - 4 * (size_t)tm * kKB; }
 
-static int ring_depth(int tm) {
-  switch (tm) {
-    case 16: return Cfg<16>::D;
-    case 32: return Cfg<32>::D;
-    case 64: return Cfg<64>::D;
-    default: return Cfg<128>::D;
-  }
-}
+constexpr int kRing = Cfg<16>::D;   // the weight ring depth of every tile body
+static_assert(Cfg<128>::D == kRing && Cfg<160>::D == kRing, "one ring depth");
 
 // run_length, shortened until the run's weight scales fit in LDS; one N tile
 // per workgroup unless the K steps fill whole rounds of the weight ring
 static int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
-  if (KT % ring_depth(tm) != 0) return 1;
+  if (KT % kRing != 0) return 1;
   int nb = run_length(g, tm, NT, KT);
-  while (nb > 1 && gemm_lds_bytes(tm, KT, nb) > kMaxDynLds) nb = (nb + 1) / 2;
+  while (nb > 1 && gemm_lds_bytes(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
   const int ng = (NT + nb - 1) / nb;
   return (NT + ng - 1) / ng;
 }
@@ -788,13 +785,15 @@ size_t gemm_lds_bytes(int tile_m, int KT, int NB) {
     case 16: return Lds<16>::bytes(KT, NB);
     case 32: return Lds<32>::bytes(KT, NB);
     case 64: return Lds<64>::bytes(KT, NB);
-    default: return Lds<128>::bytes(KT, NB);
+    case 128: return Lds<128>::bytes(KT, NB);
+    case 144: return Lds<144>::bytes(KT, NB);
+    default: return Lds<160>::bytes(KT, NB);
   }
 }
 
-template <typename Kern>
+template <int TMAX, typename Kern>
 static hipError_t allow_lds(Kern k) {
-  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_dyn_lds(TMAX));
 }
 
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
@@ -802,17 +801,18 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
                         uint8_t* q, float* q_scale, int tile_m, bool packed, hipStream_t stream) {
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
-    for (auto k : {gemm1_swiglu_quant_kernel<16, false>, gemm1_swiglu_quant_kernel<32, false>,
-                   gemm1_swiglu_quant_kernel<64, false>, gemm1_swiglu_quant_kernel<128, false>,
-                   gemm1_swiglu_quant_kernel<16, true>, gemm1_swiglu_quant_kernel<32, true>,
-                   gemm1_swiglu_quant_kernel<64, true>, gemm1_swiglu_quant_kernel<128, true>})
-      if (e == hipSuccess) e = allow_lds(k);
+#define FP8MOE_ATTR(TMV)                                                        \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, false>); \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, true>)
+    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144);
+#undef FP8MOE_ATTR
     return e;
   }();
   if (attr != hipSuccess) return attr;
+  if (tile_m > kMaxTileGemm1) return hipErrorInvalidValue;
   const int NT = I / 128, NB = fit_run(g, tile_m, NT, H / kKB), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes(tile_m, H / kKB, NB);
-  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
 #define FP8MOE_G1(TMV)                                                                                 \
   if (packed)                                                                                          \
@@ -826,6 +826,7 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
     case 32: FP8MOE_G1(32); break;
     case 64: FP8MOE_G1(64); break;
     case 128: FP8MOE_G1(128); break;
+    case 144: FP8MOE_G1(144); break;
     default: return hipErrorInvalidValue;
   }
 #undef FP8MOE_G1
@@ -838,17 +839,18 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
   if (tile_n != kTN) return hipErrorInvalidValue;
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
-    for (auto k : {gemm2_weighted_kernel<16, false>, gemm2_weighted_kernel<32, false>,
-                   gemm2_weighted_kernel<64, false>, gemm2_weighted_kernel<128, false>,
-                   gemm2_weighted_kernel<16, true>, gemm2_weighted_kernel<32, true>,
-                   gemm2_weighted_kernel<64, true>, gemm2_weighted_kernel<128, true>})
-      if (e == hipSuccess) e = allow_lds(k);
+#define FP8MOE_ATTR(TMV)                                                    \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, false>); \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, true>)
+    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144); FP8MOE_ATTR(160);
+#undef FP8MOE_ATTR
     return e;
   }();
   if (attr != hipSuccess) return attr;
+  if (tile_m > kMaxTileGemm2) return hipErrorInvalidValue;
   const int NT = (H + kTN - 1) / kTN, NB = fit_run(g, tile_m, NT, I / kKB), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes(tile_m, I / kKB, NB);
-  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
 #define FP8MOE_G2(TMV)                                                                                    \
   if (packed)                                                                                             \
@@ -862,6 +864,8 @@ hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w
     case 32: FP8MOE_G2(32); break;
     case 64: FP8MOE_G2(64); break;
     case 128: FP8MOE_G2(128); break;
+    case 144: FP8MOE_G2(144); break;
+    case 160: FP8MOE_G2(160); break;
     default: return hipErrorInvalidValue;
   }
 #undef FP8MOE_G2

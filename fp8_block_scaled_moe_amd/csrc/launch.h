@@ -29,13 +29,24 @@ hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int
 // Dynamic LDS of a grouped-GEMM launch with tile_m rows, KT K steps and runs of NB N tiles.
 size_t gemm_lds_bytes(int tile_m, int KT, int NB);
 
-// GEMM1 + SwiGLU + 1x128 requant.  tile_m in {16, 32, 64, 128}; packed: w13
-// in the MFMA-tiled layout of launch_pack_weights, else row-major.
+// Largest tile heights: the tile body of GEMM1 (with its SwiGLU/requant
+// epilogue) fills the 256 VGPRs at 144 rows, GEMM2's fits up to 160.
+constexpr int kMaxTileGemm1 = 144, kMaxTileGemm2 = 160;
+// Tile height the cost model's 128-row class runs with.  GEMM2: its largest
+// body (fewer tiles stream each expert's weights; measured 3% faster than 128
+// rows at T=8192).  GEMM1: 128 rows (the 144-row body, at the VGPR limit,
+// measured 3% slower).
+constexpr int kClass128TileGemm1 = 128, kClass128TileGemm2 = 160;
+
+// GEMM1 + SwiGLU + 1x128 requant.  tile_m (largest tile height) in
+// {16, 32, 64, 128, 144}; packed: w13 in the MFMA-tiled layout of
+// launch_pack_weights, else row-major.
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
                         const float* w13_scale, const GroupedRows& g, int H, int I,
                         uint8_t* q, float* q_scale, int tile_m, bool packed, hipStream_t stream);
 
-// GEMM2 with the top-k weight epilogue, Y indexed by source row.  tile_m in {16, 32, 64, 128}.
+// GEMM2 with the top-k weight epilogue, Y indexed by source row.  tile_m in
+// {16, 32, 64, 128, 144, 160}.
 hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w2,
                         const float* w2_scale, const float* topk_weights, const GroupedRows& g,
                         int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream);

@@ -114,12 +114,15 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *   workspace / workspace_bytes       device scratch of at least
  *                                     moe_fused_fp8_workspace_size() bytes,
  *                                     256-byte aligned, owned by the caller
- *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128: the
- *            largest number of token rows per GEMM tile (16 is the swap-AB
- *            class: tokens on the 16-wide MFMA side); applies to both GEMMs
- *            when given.  The routing pads each expert to 16 rows only, and
- *            the GEMMs cut each expert into ceil(rows / tile_m) tiles of
- *            equal height (a multiple of 16, at most tile_m)
+ *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128, 144,
+ *            160: the largest number of token rows per GEMM tile (16 is the
+ *            swap-AB class: tokens on the 16-wide MFMA side); applies to
+ *            both GEMMs when given, GEMM1 capped at 144 rows (its largest
+ *            tile body).  Auto runs the cost model's 128-row class with
+ *            128-row tiles in GEMM1 and 160-row tiles in GEMM2.  The routing
+ *            pads each expert to 16 rows only, and the GEMMs cut each expert
+ *            into ceil(rows / tile_m) tiles of equal height (a multiple of
+ *            16, at most tile_m)
  *   tile_n   -1 (auto) or 256: GEMM2 output columns per tile (GEMM1 always
  *            covers 128 columns of I, one requantisation block, per tile)
  *   weight_layout  FP8MOE_WEIGHTS_ROW_MAJOR (w13, w2 as above) or
@@ -160,8 +163,9 @@ int moe_fused_fp8(const void* x, const float* x_scale,
  * moe_gemm2_weighted: for every row p with src = sorted_src[p] >= 0:
  *     Y[src, :] = bf16( topk_weights[src] * (deq(q[p]) . w2[e]^T) ).
  *   Y bf16 [T*K, H]; rows of dropped slots are not written.
- *   `align` is the one the routing was built with; tile_m is -1 (auto: the
- *   cost model's choice) or 16/32/64/128.  cap is the length of sorted_src.
+ *   `align` is the one the routing was built with; tile_m is -1 (auto, as
+ *   for moe_fused_fp8) or 16/32/64/128/144/160 (moe_gemm1_swiglu_quant caps
+ *   it at 144).  cap is the length of sorted_src.
  * moe_combine: out[t, :] = bf16( sum over j with 0 <= topk_ids[t, j] < E of
  *   Y[t*K + j, :] ) summed in fp32 in ascending j; zeros for tokens with no
  *   valid slot.

@@ -109,7 +109,7 @@ def test_stage_validation():
                                               k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1),
                                               k.get("layout", 0), NULL)
     assert g1(align=24) == E_ALIGN
-    assert g1(align=16, tm=48) == E_TILE          # tile heights 16/32/64/128 only
+    assert g1(align=16, tm=48) == E_TILE          # tile heights 16/32/64/128/144/160 only
     assert g1(cap=-1) == E_SHAPE
     assert g1(T=0) == OK
     assert g1(layout=3) == E_SHAPE

@@ -22,7 +22,7 @@ from tests.gpu_helpers import say, assert_close_to_oracle, e4m3_ordinal, dev_exp
 
 pytestmark = pytest.mark.gpu
 
-TILES = (16, 32, 64, 128)
+TILES = (16, 32, 64, 128, 144, 160)
 
 
 def run_fused(p, tile_m=-1, tile_n=-1):

@@ -26,7 +26,7 @@ from tests.gpu_helpers import say, assert_close_to_oracle
 pytestmark = pytest.mark.gpu
 
 ALIGNS = (16, 32, 64, 128)
-TILES = (16, 32, 64, 128)
+TILES = (16, 32, 64, 128, 144, 160)
 SENTINEL_Q = 0x5A          # an e4m3 code the stage would only write by coincidence; checked on unwritten rows only
 SENTINEL_Y = 12345.0       # exactly representable in bf16
 
