@@ -62,8 +62,8 @@ METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roof
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "337a058de330dadc03e469b627f19d52fac256f06c2f1a79a151aa3d66e8754e",
-    "gemm1_fetch_kib": 5557923, "gemm1_write_kib": 198560,
+    "gemm_sources_sha256": "b449a2ecfd825747c5769422ebde799263a03083381c7c61ec512ae29926bd5c",
+    "gemm1_fetch_kib": 5568587, "gemm1_write_kib": 156772,
     "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm.hip", "fp8_block_scaled_moe_amd/csrc/device_common.h",
