@@ -162,19 +162,21 @@ def flush_caches():
     _FLUSH.fill_(1)
 
 
+def cold_once_ms(fn):
+    """ms of one call of fn with the caches flushed before it (flush not timed)."""
+    s = torch.cuda.current_stream()
+    flush_caches()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 def cold_time_ms(fn, iters):
     """Average ms of fn with the caches flushed before each call (flush not timed)."""
-    s = torch.cuda.current_stream()
-    total = 0.0
-    for _ in range(iters):
-        flush_caches()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(s)
-        fn()
-        b.record(s)
-        torch.cuda.synchronize()
-        total += a.elapsed_time(b)
-    return total / iters
+    return sum(cold_once_ms(fn) for _ in range(iters)) / iters
 
 
 STREAM_BYTES = 2 << 30
@@ -226,12 +228,17 @@ def skewed_bench(iters=10):
         p.w13_p, p.w2_p = packed
         ws = fm.alloc_workspace(T, d["H"], d["I"], d["E"], d["K"], "cuda")
         o = torch.empty((T, d["H"]), dtype=torch.bfloat16, device="cuda")
-        res = {}
         forced = (16, 32, 64, 128, 160)   # 160: GEMM1 runs 144 (its largest body)
-        for tm in (-1,) + forced:
-            fn = lambda: fused(p, o, ws, tile_m=tm)
-            fn()
-            res[tm] = cold_time_ms(fn, iters)
+        configs = (-1,) + forced
+        fns = {tm: (lambda tm=tm: fused(p, o, ws, tile_m=tm)) for tm in configs}
+        for _ in range(3):   # warm-up of every configuration (also lets the clocks settle)
+            for tm in configs:
+                fns[tm]()
+        # configurations interleaved, so any drift in clocks or caches falls on all alike
+        res = {tm: 0.0 for tm in configs}
+        for _ in range(iters):
+            for tm in configs:
+                res[tm] += cold_once_ms(fns[tm]) / iters
         nbytes, active = algorithmic_bytes(p)
         best = min(res[t] for t in forced)
         auto_tm = fm.select_tile(T * d["K"], d["I"], d["H"], d["E"], 256, True)[0]
