@@ -100,7 +100,7 @@ int device_num_cu() {
 }
 
 // Largest tile height a GEMM runs with: the requested one (GEMM1 at most
-// 144 rows), else the cost model's class, the 128-row class running with
+// 128 rows), else the cost model's class, the 128-row class running with
 // kClass128Tile* rows.
 int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
   const int cap = gated ? kMaxTileGemm1 : kMaxTileGemm2;

@@ -139,64 +139,101 @@ __device__ __forceinline__ v8i weight_frag(__amdgpu_buffer_rsrc_t rsrc, int voff
 // most 15 rows per tile are computed beyond the segment.
 struct TileCoord { int mt, run, e, p0, h, tm; };
 
-__device__ __forceinline__ int wave_sum(int v) {
+template <int TMAX>
+__device__ __forceinline__ int tiles_of(int len) { return (len + TMAX - 1) / TMAX; }
+
+// Tile counts of experts c + 4 lane .. c + 4 lane + 3 (0 past E) from one
+// round of independent loads, and the wave's inclusive scan of their sums.
+template <int TMAX>
+struct ChunkTiles {
+  int start[5];   // padded[e] for the lane's four experts and the next
+  int nt[4];
+  int incl;       // tiles of experts c .. c + 4 lane + 3
+  int total;      // tiles of the chunk's 256 experts
+  __device__ __forceinline__ void load(const int32_t* __restrict__ padded, int E, int c, int lane) {
+    const int e0 = c + 4 * lane;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-template <int TMAX>
-__device__ __forceinline__ int expert_tiles(const int32_t* __restrict__ padded, int e) {
-  return (padded[e + 1] - padded[e] + TMAX - 1) / TMAX;
-}
-
-// Work item L of this workgroup -> (expert, N run, M tile).  Items are
-// ordered expert-major, then N run, then M tile, so expert e's items start at
-// NG * (tiles of experts before e).  Both passes over the experts are a
-// wave-wide coalesced load plus shuffles (all waves compute the same values).
-template <int TMAX>
-__device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
-                                           const int32_t* __restrict__ sorted_src, int E, int NG, TileCoord& tc) {
-  const int lane = threadIdx.x & 63;
-  int tot = 0;
-  for (int e = lane; e < E; e += 64) tot += expert_tiles<TMAX>(padded, e);
-  const int items = __builtin_amdgcn_readfirstlane(wave_sum(tot)) * NG;
-  const int per_xcd = (items + kNumXcd - 1) / kNumXcd;
-  const int b = blockIdx.x;
-  const int slot = b / kNumXcd;
-  const int L = (b % kNumXcd) * per_xcd + slot;
-  if (slot >= per_xcd || L >= items) return false;
-  // The expert owning M tile t = L / NG is the number of experts whose tiles
-  // all come before t (their running tile count is <= t; empty experts
-  // included), and the sum of those experts' tiles is its first tile.
-  const int t = L / NG;
-  int cnt = 0, before = 0, base = 0;
-  for (int c = 0; c < E && base <= t; c += 64) {
-    const int e = c + lane;
-    const int nt = e < E ? expert_tiles<TMAX>(padded, e) : 0;
-    int incl = nt;   // inclusive scan of the chunk's tile counts
+    for (int k = 0; k < 5; ++k) start[k] = padded[min(e0 + k, E)];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      nt[k] = e0 + k < E ? tiles_of<TMAX>(start[k + 1] - start[k]) : 0;
+      sum += nt[k];
+    }
+    incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o);
       if (lane >= o) incl += v;
     }
-    if (e < E && base + incl <= t) {
-      ++cnt;
-      before += nt;
-    }
-    base += __shfl(incl, 63);
+    total = __builtin_amdgcn_readlane(incl, 63);
   }
-  const int e = __builtin_amdgcn_readfirstlane(wave_sum(cnt));
-  const int first = __builtin_amdgcn_readfirstlane(wave_sum(before));
-  const int nm = expert_tiles<TMAX>(padded, e);   // >= 1: the expert owns tile t
-  const int len = padded[e + 1] - padded[e];
+};
+
+// Work item L of this workgroup -> (expert, N run, M tile).  Items are
+// ordered expert-major, then N run, then M tile, so expert e's items start at
+// NG * (tiles of experts before e).  One round of coalesced loads per 256
+// experts and a wave scan (all waves compute the same values).
+template <int TMAX>
+__device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
+                                           const int32_t* __restrict__ sorted_src, int E, int NG, TileCoord& tc) {
+  const int lane = threadIdx.x & 63;
+  ChunkTiles<TMAX> ch;
+  ch.load(padded, E, 0, lane);
+  int tot = ch.total;
+  for (int c = 256; c < E; c += 256) {   // more than 256 experts: one more round per 256
+    ChunkTiles<TMAX> more;
+    more.load(padded, E, c, lane);
+    tot += more.total;
+  }
+  const int items = __builtin_amdgcn_readfirstlane(tot) * NG;   // uniform: every lane holds the totals
+  const int per_xcd = (items + kNumXcd - 1) / kNumXcd;
+  const int b = blockIdx.x;
+  const int slot = b / kNumXcd;
+  const int L = (b % kNumXcd) * per_xcd + slot;
+  if (slot >= per_xcd || L >= items) return false;
+  // M tile t = L / NG: find its chunk, then its lane (the number of lanes
+  // whose experts' tiles all precede t), then the expert within the lane
+  const int t = __builtin_amdgcn_readfirstlane(L / NG);
+  int base = 0, c = 0;
+  while (base + ch.total <= t) {   // t < tot, so this stops at a chunk of the experts
+    base += ch.total;
+    c += 256;
+    ch.load(padded, E, c, lane);
+  }
+  const int own = __builtin_amdgcn_readfirstlane(__popcll(__ballot(base + ch.incl <= t)));
+  // the owning lane's values, read into scalar registers (the tile's
+  // coordinates are wave-uniform, and so is everything derived from them)
+  int o_nt[4], o_start[5];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o_nt[i] = __builtin_amdgcn_readlane(ch.nt[i], own);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) o_start[i] = __builtin_amdgcn_readlane(ch.start[i], own);
+  int first = __builtin_amdgcn_readfirstlane(base) + __builtin_amdgcn_readlane(ch.incl, own) -
+              (o_nt[0] + o_nt[1] + o_nt[2] + o_nt[3]);
+  int k = 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i)   // skip the lane's experts whose tiles all precede t
+    if (k == i && first + o_nt[i] <= t) {
+      first += o_nt[i];
+      k = i + 1;
+    }
+  int nm = o_nt[0], s0 = o_start[0], s1 = o_start[1];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (k == i) {
+      nm = o_nt[i];
+      s0 = o_start[i];
+      s1 = o_start[i + 1];
+    }
+  const int len = s1 - s0;   // nm >= 1: the expert owns tile t
   const int j = L - NG * first;
   tc.run = j / nm;
   tc.mt = j - tc.run * nm;
   tc.tm = ((len + nm - 1) / nm + 15) / 16 * 16;
-  tc.p0 = padded[e] + tc.mt * tc.tm;
+  tc.p0 = s0 + tc.mt * tc.tm;
   tc.h = min(tc.tm, len - tc.mt * tc.tm);
-  tc.e = e;
+  tc.e = c + 4 * own + k;
   return sorted_src[tc.p0] >= 0;  // false: segment padding only, nothing to compute
 }
 
@@ -804,7 +841,7 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
 #define FP8MOE_ATTR(TMV)                                                        \
     if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, false>); \
     if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, true>)
-    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144);
+    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128);
 #undef FP8MOE_ATTR
     return e;
   }();
@@ -826,7 +863,6 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
     case 32: FP8MOE_G1(32); break;
     case 64: FP8MOE_G1(64); break;
     case 128: FP8MOE_G1(128); break;
-    case 144: FP8MOE_G1(144); break;
     default: return hipErrorInvalidValue;
   }
 #undef FP8MOE_G1

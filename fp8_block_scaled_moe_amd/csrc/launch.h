@@ -29,17 +29,17 @@ hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int
 // Dynamic LDS of a grouped-GEMM launch with tile_m rows, KT K steps and runs of NB N tiles.
 size_t gemm_lds_bytes(int tile_m, int KT, int NB);
 
-// Largest tile heights: the tile body of GEMM1 (with its SwiGLU/requant
-// epilogue) fills the 256 VGPRs at 144 rows, GEMM2's fits up to 160.
-constexpr int kMaxTileGemm1 = 144, kMaxTileGemm2 = 160;
-// Tile height the cost model's 128-row class runs with.  GEMM2: its largest
-// body (fewer tiles stream each expert's weights; measured 3% faster than 128
-// rows at T=8192).  GEMM1: 128 rows (the 144-row body, at the VGPR limit,
-// measured 3% slower).
-constexpr int kClass128TileGemm1 = 128, kClass128TileGemm2 = 160;
+// Largest tile heights.  GEMM2's body fits 256 VGPRs up to 160 rows.  GEMM1's
+// body (with its SwiGLU/requant epilogue) reaches the VGPR limit at 144 rows
+// and measured 3% slower than 128 there, so GEMM1 stops at 128.
+constexpr int kMaxTileGemm1 = 128, kMaxTileGemm2 = 160;
+// Tile height the cost model's 128-row class runs with: each GEMM's largest
+// (GEMM2 at 160 rows: fewer tiles stream each expert's weights, measured 3%
+// faster than 128 rows at T=8192).
+constexpr int kClass128TileGemm1 = kMaxTileGemm1, kClass128TileGemm2 = kMaxTileGemm2;
 
 // GEMM1 + SwiGLU + 1x128 requant.  tile_m (largest tile height) in
-// {16, 32, 64, 128, 144}; packed: w13 in the MFMA-tiled layout of
+// {16, 32, 64, 128}; packed: w13 in the MFMA-tiled layout of
 // launch_pack_weights, else row-major.
 hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
                         const float* w13_scale, const GroupedRows& g, int H, int I,

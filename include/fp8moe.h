@@ -117,7 +117,7 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128, 144,
  *            160: the largest number of token rows per GEMM tile (16 is the
  *            swap-AB class: tokens on the 16-wide MFMA side); applies to
- *            both GEMMs when given, GEMM1 capped at 144 rows (its largest
+ *            both GEMMs when given, GEMM1 capped at 128 rows (its largest
  *            tile body).  Auto runs the cost model's 128-row class with
  *            128-row tiles in GEMM1 and 160-row tiles in GEMM2.  The routing
  *            pads each expert to 16 rows only, and the GEMMs cut each expert
@@ -165,7 +165,7 @@ int moe_fused_fp8(const void* x, const float* x_scale,
  *   Y bf16 [T*K, H]; rows of dropped slots are not written.
  *   `align` is the one the routing was built with; tile_m is -1 (auto, as
  *   for moe_fused_fp8) or 16/32/64/128/144/160 (moe_gemm1_swiglu_quant caps
- *   it at 144).  cap is the length of sorted_src.
+ *   it at 128).  cap is the length of sorted_src.
  * moe_combine: out[t, :] = bf16( sum over j with 0 <= topk_ids[t, j] < E of
  *   Y[t*K + j, :] ) summed in fp32 in ascending j; zeros for tokens with no
  *   valid slot.
