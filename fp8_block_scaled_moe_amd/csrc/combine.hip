@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   u32x4c o;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    o[k] = (uint32_t)f32_to_bf16(acc[2 * k]) | ((uint32_t)f32_to_bf16(acc[2 * k + 1]) << 16);
+    o[k] = pack2_bf16(acc[2 * k], acc[2 * k + 1]);
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4c*>(out + (size_t)t * H + (size_t)c * 8));
 }
 

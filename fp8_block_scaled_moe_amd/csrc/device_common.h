@@ -40,12 +40,16 @@ __device__ __forceinline__ uint32_t one_e4m3(float a) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, a, 0, false) & 0xffu;
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 -> two bf16 in one 32-bit word (lo in bits 0..15), round to
+// nearest even, one v_cvt_pk_bf16_f32.  Checked on gfx950 against the integer
+// formulation of the rounding (add 0x7FFF plus the kept lsb, keep the high
+// half) on 23 M inputs: random patterns, every tie, fp32 subnormals and the
+// values that round to infinity; identical bits.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

@@ -734,8 +734,8 @@ __device__ __forceinline__ void gemm2_tile(
         const int col = c0 + 16 * w + 4 * g;
         if (col < H) {
           uint2 v;
-          v.x = (uint32_t)f32_to_bf16(wt * acc[ts][w][0]) | ((uint32_t)f32_to_bf16(wt * acc[ts][w][1]) << 16);
-          v.y = (uint32_t)f32_to_bf16(wt * acc[ts][w][2]) | ((uint32_t)f32_to_bf16(wt * acc[ts][w][3]) << 16);
+          v.x = pack2_bf16(wt * acc[ts][w][0], wt * acc[ts][w][1]);
+          v.y = pack2_bf16(wt * acc[ts][w][2], wt * acc[ts][w][3]);
           *reinterpret_cast<uint2*>(yrow + col) = v;
         }
       }
