@@ -62,8 +62,11 @@ METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roof
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "b449a2ecfd825747c5769422ebde799263a03083381c7c61ec512ae29926bd5c",
-    "gemm1_fetch_kib": 5568587, "gemm1_write_kib": 156772,
+    "gemm_sources_sha256": "d8a79bd3530b91e0c74d2e34a0ceafb037025e5510fc2f42e2812ff387fa258e",
+    "gemm1_fetch_kib": 5571007, "gemm1_write_kib": 156943,
+    # rocprofv3 --pmc GRBM_COUNT (same command): GPU clock cycles per dispatch summed over
+    # the 8 XCDs, and the dispatch's average duration under that pass
+    "gemm1_grbm_count": 36129440, "gemm1_grbm_dur_us": 2681.79,
     "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm.hip", "fp8_block_scaled_moe_amd/csrc/device_common.h",
@@ -87,7 +90,9 @@ def traffic_from(g1f, g1w, sf, sw):
     note = (f"GEMM1 HBM bytes per launch: FETCH_SIZE {g1f:.0f} KiB x {fetch_scale:.4f} + WRITE_SIZE {g1w:.0f} KiB x "
             f"{write_scale:.4f} (scales: the 2 GiB stream kernel's known bytes / its counter readings)")
     return traffic, note
-PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published (2.4 GHz)
+PEAK_CLOCK_GHZ = 2.4
+NUM_XCD = 8
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
 
@@ -396,6 +401,12 @@ def main():
             tc["gemm1_fetch_kib"], tc["gemm1_write_kib"], tc["stream_fetch_kib"], tc["stream_write_kib"])
     else:
         roofline["traffic_note"] = "no counters recorded for the current GEMM sources"
+    if tc["gemm_sources_sha256"] == gemm_sources_sha256():
+        # the same peak at the clock GEMM1 actually sustains (power-limited under fp8 MFMA + HBM load)
+        ghz = tc["gemm1_grbm_count"] / NUM_XCD / (tc["gemm1_grbm_dur_us"] * 1e3)
+        peak_s = PEAK_FP8_TFLOPS * ghz / PEAK_CLOCK_GHZ
+        roofline.update({"sustained_clock_ghz": round(ghz, 3), "peak_at_sustained_clock": round(peak_s, 1),
+                         "frac_at_sustained_clock": round(g1_tflops / peak_s, 4)})
     roofline["algorithmic_bytes"] = int(pre.E * 2 * pre.I * pre.H + pre.T * pre.H + 4 * pre.T * (pre.H // 128)
                                         + pre.T * pre.K * pre.I + 4 * pre.T * pre.K * (pre.I // 128))
     if args.profile == "prefill":
