@@ -23,9 +23,10 @@ FlashInfer pull requests):
     section 1 (gated activation to MXFP8 with 1x32 E8M0 scales, size routing).
 
 Modules:
-  formats     -- e4m3 / bf16 / E8M0 codecs and block quantisers
+  formats     -- e4m3 / bf16 / E8M0 codecs, block and 1x32 MX quantisers
   route       -- stable counting sort of (token, slot) rows by expert
-  moe         -- the fused-MoE reference, stage by stage
+  moe         -- the fused-MoE reference, stage by stage (FP8 block-scaled,
+                 and the MXFP8 1x32 E8M0 variant)
   gated_act   -- standalone SwiGLU + MXFP8 reference
   tile_select -- the tile_m ladder (integer logic, compared bit-exactly)
 """

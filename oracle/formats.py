@@ -205,3 +205,32 @@ def dequant_blocks(q, s, block=128):
     N, K = q.shape
     v = e4m3_decode_table(q).reshape(N // block, block, K // block, block)
     return (v * np.asarray(s, dtype=np.float64)[:, None, :, None]).reshape(N, K)
+
+
+# ---------------------------------------------------------------- MX (1x32 E8M0) blocks
+
+def quantize_rows_mx(x, block=32):
+    """Per-row MXFP8 quantisation of a float32 matrix [R, C].
+
+    For each row and each run of `block` consecutive columns: amax = max |x|,
+    e = e8m0_exponent_for_amax(amax) (the power-of-two scale that keeps
+    amax / 2^e within the e4m3 range), codes = enc_sat(x * 2^-e) (the scaling
+    is exact).  This is the 1x32 E8M0 layout of the PR-8023 page (title,
+    section 1).
+    Returns (codes uint8 [R, C], E8M0 codes uint8 [R, C/block]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    assert C % block == 0
+    xb = x.reshape(R, C // block, block).astype(np.float64)
+    e = e8m0_exponent_for_amax(np.max(np.abs(xb), axis=2))
+    codes = e4m3_encode_sat(np.ldexp(xb, (-e)[:, :, None])).reshape(R, C)
+    return codes, e8m0_code(e)
+
+
+def dequant_rows_mx(q, sf, block=32):
+    """float64 values of MX codes [R, C] with E8M0 scale codes [R, C/block]: decode(q) * 2^(sf-127)."""
+    q = np.asarray(q)
+    R, C = q.shape
+    v = e4m3_decode_table(q).reshape(R, C // block, block)
+    return (v * e8m0_decode(sf)[:, :, None]).reshape(R, C)

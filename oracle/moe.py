@@ -25,6 +25,10 @@ Inputs (numpy, or anything indexable by expert for the weights):
   w2_s  f32    [E][H/128, I/128]
   topk_ids     int  [T, K]        ids outside [0, E) are dropped slots
   topk_weights f32  [T, K]
+
+moe_reference_mx is the MXFP8 variant (1x32 E8M0 scales on every operand,
+the intermediate requantised in the gated-act kernel's format); its readings
+are listed above its definition.
 """
 
 import numpy as np
@@ -77,15 +81,8 @@ def expert_ffn(xq_rows, xs_rows, w13_q, w13_s, w2_q, w2_s, stages=None):
     return Y
 
 
-def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
-                  tokens=None, return_stages=False):
-    """Reference fused MoE layer.
-
-    Returns (out_bits, out) for the requested tokens (all tokens by default,
-    in ascending token order): out_bits uint16 bf16 patterns [n_tok, H] and
-    out float32 values of those patterns.  With return_stages=True a third
-    item maps each expert to its rows and per-stage intermediates.
-    """
+def _layer(expert_fn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights, tokens, return_stages):
+    """Route rows to experts, run expert_fn on each expert's rows, combine."""
     ids = np.asarray(topk_ids)
     wts = np.asarray(topk_weights, dtype=np.float32)
     T, K = ids.shape
@@ -101,8 +98,8 @@ def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
         tj = rows[e]
         tok_idx = np.array([t for t, _ in tj], dtype=np.int64)
         st = {} if return_stages else None
-        Y = expert_ffn(np.asarray(x_q)[tok_idx], np.asarray(x_s)[tok_idx],
-                       w13_q[e], w13_s[e], w2_q[e], w2_s[e], st)
+        Y = expert_fn(np.asarray(x_q)[tok_idx], np.asarray(x_s)[tok_idx],
+                      w13_q[e], w13_s[e], w2_q[e], w2_s[e], st)
         for r, (t, j) in enumerate(tj):
             Ysl[(t, j)] = Y[r]
         if return_stages:
@@ -120,3 +117,56 @@ def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
     if return_stages:
         return out_bits, out, stages
     return out_bits, out
+
+
+def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
+                  tokens=None, return_stages=False):
+    """Reference fused MoE layer.
+
+    Returns (out_bits, out) for the requested tokens (all tokens by default,
+    in ascending token order): out_bits uint16 bf16 patterns [n_tok, H] and
+    out float32 values of those patterns.  With return_stages=True a third
+    item maps each expert to its rows and per-stage intermediates.
+    """
+    return _layer(expert_ffn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
+                  tokens, return_stages)
+
+
+# ---------------------------------------------------------------- MXFP8 variant
+#
+# The SM120 grouped-GEMM page names an MXFP8 grouped MoE kernel family beside
+# the FP8 groupwise one (its file list, and the benchmark line for the mxfp8
+# grouped MoE at per-expert M of about 192) without stating its operand
+# layout; the PR-8023 page fixes the MXFP8 block format (1x32, E8M0 scales).
+# Readings taken here:
+#   * every operand carries one E8M0 scale per 32 consecutive elements along
+#     the contraction dimension: x [T, H] with scales [T, H/32], w13 [2I, H]
+#     with [2I, H/32] (per weight row), w2 [H, I] with [H, I/32];
+#   * the intermediate requantisation is the gated-act kernel's: the SwiGLU
+#     output (rounded once to float32) -> 1x32 blocks, E8M0 exponent the
+#     smallest e with amax <= 448 * 2^e, codes enc_sat(act * 2^-e);
+#   * everything else (gate rows first, float64 GEMMs, the combine in
+#     ascending slot order, one bf16 rounding) is as in the FP8 layer above.
+
+def expert_ffn_mx(xq_rows, xsf_rows, w13_q, w13_sf, w2_q, w2_sf, stages=None):
+    """One expert on its gathered rows, MXFP8 operands: GEMM1 -> SwiGLU -> MX requant -> GEMM2."""
+    A = formats.dequant_rows_mx(xq_rows, xsf_rows)                         # [n, H]
+    W13 = formats.dequant_rows_mx(np.asarray(w13_q), np.asarray(w13_sf))    # [2I, H]
+    I = W13.shape[0] // 2
+    H1 = A @ W13.T                                                         # GEMM1, [n, 2I]
+    g, u = H1[:, :I], H1[:, I:]
+    act = silu_mul(g, u).astype(np.float32)                                # SwiGLU, one fp32 rounding
+    q, sf = formats.quantize_rows_mx(act, 32)                              # MX requant
+    W2 = formats.dequant_rows_mx(np.asarray(w2_q), np.asarray(w2_sf))      # [H, I]
+    Y = formats.dequant_rows_mx(q, sf) @ W2.T                              # GEMM2, [n, H]
+    if stages is not None:
+        stages.update(H1=H1, act=act, q=q, s=sf, Y=Y)
+    return Y
+
+
+def moe_reference_mx(x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
+                     tokens=None, return_stages=False):
+    """Reference MXFP8 MoE layer; arguments and results as moe_reference, with
+    E8M0 scale codes (uint8) x_sf [T, H/32], w13_sf [E][2I, H/32], w2_sf [E][H, I/32]."""
+    return _layer(expert_ffn_mx, x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
+                  tokens, return_stages)

@@ -6,7 +6,8 @@ renormalised weights, N(0,1) activations, N(0, 0.02^2) expert weights, and the
 harness quantisation of those fp32 values into the fp8 e4m3 codes plus fp32
 block scales that the expert path takes as input (1x128 for activations,
 128x128 for weights; scale = amax/448, codes from torch's own float8_e4m3fn
-cast after clamping to +-448).  None of the expert computation (GEMMs,
+cast after clamping to +-448; or, for the MXFP8 variant, 1x32 blocks along
+the contraction dimension with power-of-two E8M0 scales).  None of the expert computation (GEMMs,
 SwiGLU, requantisation, combine) is here.
 
 Seeds: numpy streams come from SeedSequence([cfg, tag, idx, *extra]); torch
@@ -82,6 +83,25 @@ def quant_blocks_128(w):
     return q.view(torch.uint8).reshape(N, K), s.contiguous()
 
 
+def quant_rows_mx(x):
+    """fp32 torch [R, C] -> (uint8 e4m3 codes [R, C], uint8 E8M0 codes [R, C/32]).
+
+    Harness MXFP8 quantisation of 1x32 blocks: with amax = m * 2^p (frexp,
+    0.5 <= m < 1) and 448 = 0.875 * 2^9, the smallest e with amax <= 448 * 2^e
+    is p - 9 when m <= 0.875 and p - 8 otherwise; clamped to [-127, 127],
+    -127 for an all-zero block.  Codes: torch's e4m3 cast of x * 2^-e after
+    clamping to +-448.
+    """
+    R, C = x.shape
+    xb = x.reshape(R, C // 32, 32)
+    amax = xb.abs().amax(dim=2)
+    m, p = torch.frexp(amax)
+    e = p.to(torch.int32) - 9 + (m > 0.875).to(torch.int32)
+    e = torch.where(amax == 0, torch.full_like(e, -127), e).clamp_(-127, 127)
+    q = torch.ldexp(xb, (-e).to(xb.dtype)[:, :, None]).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(R, C), (e + 127).to(torch.uint8).contiguous()
+
+
 # ---------------------------------------------------------------- activations and weights
 
 def activations(T, H, cfg, extra=()):
@@ -112,6 +132,25 @@ def expert_weight_set(E, N, K, cfg, tag, device="cpu", std=0.02):
             g.manual_seed(torch_seed(cfg, tag, e))
             w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * std
         qe, se = quant_blocks_128(w)
+        q[e].copy_(qe)
+        s[e].copy_(se)
+    return q, s
+
+
+def expert_weight_set_mx(E, N, K, cfg, tag, device="cpu", std=0.02):
+    """The same fp32 weights as expert_weight_set, MXFP8-quantised along K:
+    (codes uint8 [E, N, K], E8M0 codes uint8 [E, N, K/32])."""
+    q = torch.empty((E, N, K), dtype=torch.uint8, device=device)
+    s = torch.empty((E, N, K // 32), dtype=torch.uint8, device=device)
+    dev = torch.device(device)
+    for e in range(E):
+        if dev.type == "cpu":
+            w = torch.from_numpy(expert_weights_fp32(E, N, K, cfg, tag, e, std))
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(torch_seed(cfg, tag, e))
+            w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * std
+        qe, se = quant_rows_mx(w)
         q[e].copy_(qe)
         s[e].copy_(se)
     return q, s
@@ -148,6 +187,16 @@ def moe_tokens(T, H, E, K, cfg, extra=(), zipf_s=None, device="cpu"):
             torch.from_numpy(w).to(device))
 
 
+def moe_tokens_mx(T, H, E, K, cfg, extra=(), zipf_s=None, device="cpu"):
+    """Token-side MXFP8 inputs (same activations and routing as moe_tokens):
+    (x_q, x_sf E8M0 [T, H/32], topk_ids, topk_weights)."""
+    ids, w = router(T, E, K, cfg, extra, zipf_s)
+    x = torch.from_numpy(activations(T, H, cfg, extra))
+    x_q, x_sf = quant_rows_mx(x)
+    return (x_q.to(device), x_sf.to(device), torch.from_numpy(ids).to(device),
+            torch.from_numpy(w).to(device))
+
+
 def moe_problem(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weight_cfg=None,
                 weight_device=None):
     """A full MoE problem.  Weights use weight_cfg (default cfg) so several token
@@ -159,6 +208,18 @@ def moe_problem(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weight_
     w2_q, w2_s = expert_weight_set(E, H, I, wc, TAG_W2, wd)
     return MoEInputs(T, H, I, E, K, x_q, x_s, w13_q.to(device), w13_s.to(device),
                      w2_q.to(device), w2_s.to(device), ids, w)
+
+
+def moe_problem_mx(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weight_cfg=None,
+                   weight_device=None):
+    """moe_problem with MXFP8 operands (the scale fields hold E8M0 codes)."""
+    wc = cfg if weight_cfg is None else weight_cfg
+    wd = device if weight_device is None else weight_device
+    x_q, x_sf, ids, w = moe_tokens_mx(T, H, E, K, cfg, extra, zipf_s, device)
+    w13_q, w13_sf = expert_weight_set_mx(E, 2 * I, H, wc, TAG_W13, wd)
+    w2_q, w2_sf = expert_weight_set_mx(E, H, I, wc, TAG_W2, wd)
+    return MoEInputs(T, H, I, E, K, x_q, x_sf, w13_q.to(device), w13_sf.to(device),
+                     w2_q.to(device), w2_sf.to(device), ids, w)
 
 
 # named configurations (token count T, hidden H, intermediate I, experts E, top-k K)
