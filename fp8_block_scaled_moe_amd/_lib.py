@@ -25,6 +25,13 @@ SIGNATURES = {
                                               _vp, _vp, _i64, _i32, _i32, _vp]),
     "moe_gemm2_weighted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
                                           _vp, _i64, _i32, _i32, _i32, _vp]),
+    "moe_fused_mxfp8_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
+    "moe_fused_mxfp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                       _vp, _vp, _sz, _i32, _i32, _i32, _vp]),
+    "moe_gemm1_swiglu_quant_mx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                                 _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
+    "moe_gemm2_weighted_mx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                             _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
     "moe_pack_weights": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "gated_act_fp8_quant": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _vp]),

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8moe.so")
 
-SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm.hip", "combine.hip", "gated_act.hip", "pack.hip"]
+SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm1.hip", "gemm2.hip", "gemm1_mx.hip", "gemm2_mx.hip",
+           "combine.hip", "gated_act.hip", "pack.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -61,7 +62,7 @@ def build(verbose=False):
             print(out)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])

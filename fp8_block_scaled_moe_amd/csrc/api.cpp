@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <string>
+#include <type_traits>
 
 #include "fp8moe.h"
 #include "launch.h"
@@ -53,7 +54,8 @@ struct WsLayout {
   size_t counts, m_indptr, padded, sorted_src, src_to_sorted, q, q_scale, Y, total;
 };
 
-WsLayout ws_layout(int64_t T, int H, int I, int E, int K) {
+// MXFP8: q_scale holds one E8M0 byte per 32 columns instead of a float per 128.
+WsLayout ws_layout(int64_t T, int H, int I, int E, int K, bool mx) {
   const int64_t R = T * K;
   const int64_t cap = R + (int64_t)E * (128 - 1);  // worst case: align 128
   WsLayout w{};
@@ -65,7 +67,7 @@ WsLayout ws_layout(int64_t T, int H, int I, int E, int K) {
   w.sorted_src = take(sizeof(int32_t) * cap);
   w.src_to_sorted = take(sizeof(int32_t) * (R > 0 ? R : 1));
   w.q = take((size_t)cap * I);
-  w.q_scale = take(sizeof(float) * (size_t)cap * (I / 128));
+  w.q_scale = take(mx ? (size_t)cap * (I / 32) : sizeof(float) * (size_t)cap * (I / 128));
   w.Y = take(sizeof(uint16_t) * (size_t)(R > 0 ? R : 1) * H);
   w.total = off;
   return w;
@@ -107,6 +109,133 @@ int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
   if (requested != -1) return requested < cap ? requested : cap;
   const int cls = select_tile_m(R, n, k, E, device_num_cu(), mi355x_classes(gated));
   return cls == 128 ? (gated ? kClass128TileGemm1 : kClass128TileGemm2) : cls;
+}
+
+// Scale pointer type of each format: fp32 block scales (FP8) or E8M0 codes
+// (MXFP8); the launchers are chosen by overload on it.
+template <bool MX>
+using scale_ptr_t = std::conditional_t<MX, uint8_t, float>;
+
+hipError_t gemm1_launch(const uint8_t* x, const float* xs, const uint8_t* w, const float* ws, const GroupedRows& g,
+                        int H, int I, uint8_t* q, float* qs, int tm, bool packed, hipStream_t st) {
+  return launch_gemm1(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+}
+hipError_t gemm1_launch(const uint8_t* x, const uint8_t* xs, const uint8_t* w, const uint8_t* ws,
+                        const GroupedRows& g, int H, int I, uint8_t* q, uint8_t* qs, int tm, bool packed,
+                        hipStream_t st) {
+  return launch_gemm1_mx(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+}
+hipError_t gemm2_launch(const uint8_t* q, const float* qs, const uint8_t* w, const float* ws, const float* tw,
+                        const GroupedRows& g, int H, int I, uint16_t* Y, int tm, bool packed, hipStream_t st) {
+  return launch_gemm2(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+}
+hipError_t gemm2_launch(const uint8_t* q, const uint8_t* qs, const uint8_t* w, const uint8_t* ws, const float* tw,
+                        const GroupedRows& g, int H, int I, uint16_t* Y, int tm, bool packed, hipStream_t st) {
+  return launch_gemm2_mx(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+}
+
+template <bool MX>
+int fused_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, const scale_ptr_t<MX>* w13_scale,
+               const void* w2, const scale_ptr_t<MX>* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+               int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, void* workspace,
+               size_t workspace_bytes, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
+  const bool packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
+  if (tile_m != -1 && !valid_tile_m(tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
+  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
+  if (T == 0) return ok();
+  if (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  const WsLayout L = ws_layout(T, H, I, E, K, MX);
+  if (!workspace) return fail(FP8MOE_ERR_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % kAlignWs) return fail(FP8MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(FP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+
+  const int64_t R = T * K;
+  const int tm1 = pick_tile_m(tile_m, R, I, H, E, true);
+  const int tm2 = pick_tile_m(tile_m, R, H, I, E, false);
+  // segments padded to 16 rows only: the GEMMs cover each expert with tiles
+  // of up to tm rows and one shorter last tile
+  const int align = 16;
+  const int64_t cap = R + (int64_t)E * (align - 1);
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* m_indptr = reinterpret_cast<int32_t*>(ws + L.m_indptr);
+  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
+  int32_t* sorted_src = reinterpret_cast<int32_t*>(ws + L.sorted_src);
+  int32_t* src_to_sorted = reinterpret_cast<int32_t*>(ws + L.src_to_sorted);
+  uint8_t* q = ws + L.q;
+  scale_ptr_t<MX>* q_scale = reinterpret_cast<scale_ptr_t<MX>*>(ws + L.q_scale);
+  uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t err = launch_route_permute(topk_ids, (int)R, E, align, (int)cap, counts, m_indptr, padded,
+                                        sorted_src, src_to_sorted, s);
+  if (err != hipSuccess) return hip_fail(err, "route_permute launch");
+  GroupedRows g{padded, sorted_src, cap, E, K, R, device_num_cu()};
+  err = gemm1_launch(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale, g, H,
+                     I, q, q_scale, tm1, packed, s);
+  if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
+  err = gemm2_launch(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2, packed,
+                     s);
+  if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
+  err = launch_combine(Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
+  if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return ok();
+}
+
+template <bool MX>
+int gemm1_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, const scale_ptr_t<MX>* w13_scale,
+               const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H, int32_t I, int32_t E,
+               int32_t K, int32_t align, void* q, scale_ptr_t<MX>* q_scale, int64_t cap, int32_t tile_m,
+               int32_t weight_layout, void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
+  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
+  if (tile_m != -1 && !valid_tile_m(tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
+  if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
+  if (T == 0 || cap == 0) return ok();
+  if (!x || !x_scale || !w13 || !w13_scale || !padded_indptr || !sorted_src || !q || !q_scale)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
+  GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
+  hipError_t err = gemm1_launch(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
+                                w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
+                                weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
+  return ok();
+}
+
+template <bool MX>
+int gemm2_impl(const void* q, const scale_ptr_t<MX>* q_scale, const void* w2, const scale_ptr_t<MX>* w2_scale,
+               const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights, int64_t T,
+               int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y, int64_t cap, int32_t tile_m,
+               int32_t tile_n, int32_t weight_layout, void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
+  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
+  if (tile_m != -1 && !valid_tile_m(tile_m))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
+  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
+  if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
+  if (T == 0 || cap == 0) return ok();
+  if (!q || !q_scale || !w2 || !w2_scale || !padded_indptr || !sorted_src || !topk_weights || !Y)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
+  GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
+  hipError_t err = gemm2_launch(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2), w2_scale,
+                                topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm,
+                                weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
+  return ok();
 }
 
 }  // namespace
@@ -159,7 +288,15 @@ int moe_fused_fp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
   if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
-  *bytes = ws_layout(T, H, I, E, K).total;
+  *bytes = ws_layout(T, H, I, E, K, false).total;
+  return ok();
+}
+
+int moe_fused_mxfp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, size_t* bytes) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
+  *bytes = ws_layout(T, H, I, E, K, true).total;
   return ok();
 }
 
@@ -168,101 +305,48 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
                   const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                   void* out, void* workspace, size_t workspace_bytes, int32_t tile_m, int32_t tile_n,
                   int32_t weight_layout, void* stream) {
-  int st = check_dims(T, H, I, E, K);
-  if (st) return st;
-  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
-  const bool packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
-  if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
-  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
-  if (T == 0) return ok();
-  if (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out)
-    return fail(FP8MOE_ERR_NULL, "null tensor argument");
-  const WsLayout L = ws_layout(T, H, I, E, K);
-  if (!workspace) return fail(FP8MOE_ERR_WORKSPACE, "workspace is null");
-  if ((uintptr_t)workspace % kAlignWs) return fail(FP8MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(FP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  return fused_impl<false>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, out,
+                           workspace, workspace_bytes, tile_m, tile_n, weight_layout, stream);
+}
 
-  const int64_t R = T * K;
-  const int tm1 = pick_tile_m(tile_m, R, I, H, E, true);
-  const int tm2 = pick_tile_m(tile_m, R, H, I, E, false);
-  // segments padded to 16 rows only: the GEMMs cover each expert with tiles
-  // of up to tm rows and one shorter last tile
-  const int align = 16;
-  const int64_t cap = R + (int64_t)E * (align - 1);
-
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  int32_t* m_indptr = reinterpret_cast<int32_t*>(ws + L.m_indptr);
-  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
-  int32_t* sorted_src = reinterpret_cast<int32_t*>(ws + L.sorted_src);
-  int32_t* src_to_sorted = reinterpret_cast<int32_t*>(ws + L.src_to_sorted);
-  uint8_t* q = ws + L.q;
-  float* q_scale = reinterpret_cast<float*>(ws + L.q_scale);
-  uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
-  hipStream_t s = (hipStream_t)stream;
-
-  hipError_t err = launch_route_permute(topk_ids, (int)R, E, align, (int)cap, counts, m_indptr, padded,
-                                        sorted_src, src_to_sorted, s);
-  if (err != hipSuccess) return hip_fail(err, "route_permute launch");
-  GroupedRows g{padded, sorted_src, cap, E, K, R, device_num_cu()};
-  err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
-                     g, H, I, q, q_scale, tm1, packed, s);
-  if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
-  err = launch_gemm2(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2,
-                     256, packed, s);
-  if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
-  err = launch_combine(Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
-  if (err != hipSuccess) return hip_fail(err, "combine launch");
-  return ok();
+int moe_fused_mxfp8(const void* x, const uint8_t* x_sf, const void* w13, const uint8_t* w13_sf, const void* w2,
+                    const uint8_t* w2_sf, const int32_t* topk_ids, const float* topk_weights, int64_t T, int32_t H,
+                    int32_t I, int32_t E, int32_t K, void* out, void* workspace, size_t workspace_bytes,
+                    int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+  return fused_impl<true>(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, T, H, I, E, K, out, workspace,
+                          workspace_bytes, tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
                            const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
                            int32_t I, int32_t E, int32_t K, int32_t align, void* q, float* q_scale,
                            int64_t cap, int32_t tile_m, int32_t weight_layout, void* stream) {
-  int st = check_dims(T, H, I, E, K);
-  if (st) return st;
-  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
-  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
-  if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
-  if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
-  if (T == 0 || cap == 0) return ok();
-  if (!x || !x_scale || !w13 || !w13_scale || !padded_indptr || !sorted_src || !q || !q_scale)
-    return fail(FP8MOE_ERR_NULL, "null tensor argument");
-  int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
-  GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
-  hipError_t err = launch_gemm1(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
-                                w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
-                                weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
-  if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
-  return ok();
+  return gemm1_impl<false>(x, x_scale, w13, w13_scale, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_scale,
+                           cap, tile_m, weight_layout, stream);
+}
+
+int moe_gemm1_swiglu_quant_mx(const void* x, const uint8_t* x_sf, const void* w13, const uint8_t* w13_sf,
+                              const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
+                              int32_t I, int32_t E, int32_t K, int32_t align, void* q, uint8_t* q_sf, int64_t cap,
+                              int32_t tile_m, int32_t weight_layout, void* stream) {
+  return gemm1_impl<true>(x, x_sf, w13, w13_sf, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_sf, cap,
+                          tile_m, weight_layout, stream);
 }
 
 int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, const float* w2_scale,
                        const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
                        int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y,
                        int64_t cap, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
-  int st = check_dims(T, H, I, E, K);
-  if (st) return st;
-  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
-  if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
-  if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
-  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
-  if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
-  if (T == 0 || cap == 0) return ok();
-  if (!q || !q_scale || !w2 || !w2_scale || !padded_indptr || !sorted_src || !topk_weights || !Y)
-    return fail(FP8MOE_ERR_NULL, "null tensor argument");
-  int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
-  GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
-  hipError_t err = launch_gemm2(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2),
-                                w2_scale, topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm, 256,
-                                weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
-  if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
-  return ok();
+  return gemm2_impl<false>(q, q_scale, w2, w2_scale, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align,
+                           Y, cap, tile_m, tile_n, weight_layout, stream);
+}
+
+int moe_gemm2_weighted_mx(const void* q, const uint8_t* q_sf, const void* w2, const uint8_t* w2_sf,
+                          const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y, int64_t cap,
+                          int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+  return gemm2_impl<true>(q, q_sf, w2, w2_sf, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align, Y, cap,
+                          tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {

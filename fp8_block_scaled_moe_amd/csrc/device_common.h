@@ -16,9 +16,11 @@ constexpr int kScaleBlock = 128;     // 1x128 activation / 128x128 weight scale 
 constexpr int kNumXcd = 8;           // MI355X: 8 accelerator dies, workgroups dealt round-robin
 
 // One 16x16x128 fp8 (e4m3) MFMA: c += a . b over 128 K.
-// Lane l holds A row (l % 16) and B column (l % 16), K bytes [32*(l/16), +32);
-// the result lane l holds rows 4*(l/16) + r (r = 0..3) of column l % 16.
-// The scaled form with both E8M0 scales at 127 (2^0) is the plain product.
+// Lane l holds A row (l % 16) and B column (l % 16): its 32 bytes are K
+// elements 16g..16g+15 and 64+16g..64+16g+15 for lane group g = l / 16
+// (measured with one-hot operands and per-lane scales on gfx950); the result
+// lane l holds rows 4*(l/16) + r (r = 0..3) of column l % 16.  The scaled
+// form with both E8M0 scales at 127 (2^0) is the plain product.
 __device__ __forceinline__ v4f mfma16x16x128_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
@@ -50,6 +52,18 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// E8M0 exponent of an MXFP8 block: the smallest e with amax <= 448 * 2^e
+// (frexp: amax = m * 2^x, 448 = 0.875 * 2^9, so e = x - 9 if m <= 0.875 else
+// x - 8), clamped to [-127, 127]; -127 for amax == 0 (and NaN).  Codes are
+// then e4m3(v * 2^-e), an exact power-of-two scaling, and never saturate.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int x;
+  const float m = frexpf(amax, &x);
+  const int e = m <= 0.875f ? x - 9 : x - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

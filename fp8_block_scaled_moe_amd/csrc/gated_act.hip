@@ -44,14 +44,6 @@ __device__ __forceinline__ void unpack8(const u32x4& v, float (&f)[8]) {
   }
 }
 
-__device__ __forceinline__ int e8m0_exponent(float amax) {
-  if (!(amax > 0.f)) return -127;
-  int x;
-  const float m = frexpf(amax, &x);
-  const int e = m <= 0.875f ? x - 9 : x - 8;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
 // The fp32 block amax cannot be trusted to decide the exponent: its frexp
 // mantissa is within 2^-15 of 0.875 (the boundary 448 * 2^e), or it is below
 // 2^-60 (zero, NaN and blocks of flushed activations included).

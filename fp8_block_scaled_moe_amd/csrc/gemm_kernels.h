@@ -1,17 +1,30 @@
-// Grouped FP8 (e4m3) GEMMs of the MoE expert path on gfx950 (CDNA4).
+// Grouped FP8 (e4m3) GEMMs of the MoE expert path on gfx950 (CDNA4): the
+// kernels and their launch logic, instantiated by gemm1.hip / gemm2.hip (FP8
+// block-scaled operands) and gemm1_mx.hip / gemm2_mx.hip (MXFP8 operands).
 //
-//   GEMM1: h = x[token] . w13[e]^T over gate+up, then SwiGLU and the 1x128
-//          FP8 requantisation in the epilogue (AlphaMoE page, section
-//          "Problem": stages 1-3 fused so the activation never reaches HBM in
+//   GEMM1: h = x[token] . w13[e]^T over gate+up, then SwiGLU and the FP8
+//          requantisation in the epilogue (AlphaMoE page, section "Problem":
+//          stages 1-3 fused so the activation never reaches HBM in
 //          fp32/bf16; operand layout of the SM120 page, section 1: both
 //          operands K-contiguous, gate rows first, then up rows).
 //   GEMM2: y = deq(q) . w2[e]^T, epilogue Y[src] = bf16(topk_weight[src] * y)
 //          (stage 4; the combine is a separate gather-reduce).
 //
-// Block scaling: one v_mfma 16x16x128 covers exactly one 128-wide scale
-// block.  It accumulates the raw fp8 dot product into a zero accumulator and
-// the fp32 result is folded as acc += p * (s_token * s_block), one FMA per
-// output element and K step.
+// Block scaling, FP8 variant (1x128 activation and 128x128 weight scales in
+// fp32): one v_mfma 16x16x128 covers exactly one 128-wide scale block.  It
+// accumulates the raw fp8 dot product into a zero accumulator and the fp32
+// result is folded as acc += p * (s_token * s_block), one FMA per output
+// element and K step.  The intermediate is requantised per 1x128 block with
+// s = amax / 448.
+//
+// Block scaling, MXFP8 variant (one E8M0 scale per 32 K elements of every
+// operand row; the SM120 page's mxfp8 grouped GEMM family, in the 1x32 E8M0
+// format of the PR-8023 page): the scaled MFMA applies both operands' scales
+// itself.  Lane l supplies the scale of its operand row l % 16 for the 32-K
+// block l / 16 of the step (one byte of a VGPR, chosen by the instruction's
+// op_sel), so the MFMA accumulates straight into acc and no VALU fold
+// remains.  The intermediate is requantised per 1x32 block to E8M0 + e4m3 as
+// in the gated-act kernel.
 //
 // Weight streaming.  For these shapes the layer is a stream of expert
 // weights (every active expert's weights are read once, ~256 routed rows
@@ -79,9 +92,37 @@ struct Cfg {
   // floats per K step of the token scales in LDS (scale_slot order): whole
   // 64-float quad groups once TS >= 4
   static constexpr int TSLOT = TS >= 4 ? (TS + 3) / 4 * 64 : TM;
+  // MXFP8: dwords of E8M0 token scales a lane reads per K step (byte ts of
+  // dword ts / 4 is token sub-tile ts's)
+  static constexpr int TSW = (TS + 3) / 4;
   __host__ __device__ static constexpr int block_of(int wave, int i) { return (wave * A_PER_WAVE + i) % NBLK; }
 };
 
+
+// Scale type of the block-scaled operands: fp32 block scales or E8M0 codes.
+template <bool MX>
+using scale_t = std::conditional_t<MX, uint8_t, float>;
+
+// One 16x16x128 MXFP8 MFMA, c += a . b with the E8M0 scales applied: sa is
+// the A operand lane's scale code (byte 0), byte SEL of sb the B operand's.
+// Inside a 128-byte K step both operands take bytes {16g..16g+15} and
+// {64+16g..64+16g+15} for lane group g = lane / 16 (the hardware's own K
+// order), so the 32-K block k of the step is bytes 0..15 of lane groups
+// 2(k%2), 2(k%2)+1 for k < 2 and bytes 16..31 of them for k >= 2 -- exactly
+// the elements lane 16k + row's scale covers.
+template <int SEL>
+__device__ __forceinline__ v4f mfma16x16x128_mx(const v8i& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, SEL, (int)sb);
+}
+__device__ __forceinline__ v4f mfma16x16x128_mx_sel(int sel, const v8i& a, const v8i& b, const v4f& c, uint32_t sa,
+                                                    uint32_t sb) {
+  switch (sel) {   // sel is a constant of the unrolled sub-tile loop
+    case 0: return mfma16x16x128_mx<0>(a, b, c, sa, sb);
+    case 1: return mfma16x16x128_mx<1>(a, b, c, sa, sb);
+    case 2: return mfma16x16x128_mx<2>(a, b, c, sa, sb);
+    default: return mfma16x16x128_mx<3>(a, b, c, sa, sb);
+  }
+}
 
 __device__ __forceinline__ int swz_key(int r) { return ((r >> 1) & 7) ^ (((r >> 2) ^ (r >> 3)) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * kKB + ((c ^ swz_key(r)) << 4); }
@@ -320,20 +361,48 @@ __device__ __forceinline__ void read_token_scales(const float* p, float (&sa)[TS
   }
 }
 
+// The MXFP8 token scales of the M tile -> LDS: E8M0 code of row 16*ts + l16,
+// 32-K block g of K step k at byte ((4k + g) * 16 + l16) * 4*TSW + ts, so the
+// lane (g, l16) of step k reads its TS codes as TSW consecutive dwords.
+// row_sf(r) gives the row's 4*KT codes (nullptr for a pad row: code 0).  Each
+// thread keeps one row and reads its codes a K step (4 codes) at a time.
+template <int TM, typename RowSf>
+__device__ __forceinline__ void stage_token_scales_mx(uint8_t* SX, int KT, RowSf row_sf, int tid) {
+  constexpr int TSW = Cfg<TM>::TSW;
+  constexpr int TPR = kThreads / TM;   // threads per row
+  const int r = tid / TPR, part = tid % TPR;
+  if (r >= TM) return;
+  const uint8_t* rs = row_sf(r);
+  uint8_t* dst = SX + (r & 15) * 4 * TSW + (r >> 4);
+  for (int k = part; k < KT; k += TPR) {
+    const uint32_t v = rs ? *reinterpret_cast<const uint32_t*>(rs + 4 * k) : 0u;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dst[(4 * k + g) * 64 * TSW] = (uint8_t)(v >> (8 * g));
+  }
+}
+
 // Dynamic LDS layout (the four token buffers [TM][128] are static arrays of
-// the main loop): the M tile's token scales [KT][TSLOT], the run's weight block
-// scales [NB][KT][2], the epilogue scratch (GEMM1: per-wave row max [8][TM];
-// GEMM2: source row and top-k weight [2][TM]).
-template <int TM>
+// the main loop): the M tile's token scales (FP8: fp32 [KT][TSLOT]; MXFP8:
+// E8M0 [KT][4][16][4*TSW]), the run's weight block scales (FP8 only: fp32
+// [NB][KT][2]; MXFP8 weight scales stream from global memory with the
+// weights), the epilogue scratch (GEMM1: per-wave row max [8][TM]; GEMM2:
+// source row and top-k weight [2][TM]).
+template <int TM, bool MX>
 struct Lds {
+  __host__ __device__ static constexpr size_t token_bytes(int KT) {
+    return MX ? 256 * (size_t)Cfg<TM>::TSW * KT : 4 * (size_t)Cfg<TM>::TSLOT * KT;
+  }
+  __host__ __device__ static constexpr size_t weight_bytes(int KT, int NB) { return MX ? 0 : 8 * (size_t)NB * KT; }
   __host__ __device__ static constexpr size_t bytes(int KT, int NB) {
-    return 4 * (size_t)Cfg<TM>::TSLOT * KT + 8 * (size_t)NB * KT + 4 * (size_t)kWaves * TM;
+    return token_bytes(KT) + weight_bytes(KT, NB) + 4 * (size_t)kWaves * TM;
   }
   __device__ static float* token_scales(uint8_t* smem) { return reinterpret_cast<float*>(smem); }
   __device__ static float* weight_scales(uint8_t* smem, int KT) {
-    return token_scales(smem) + (size_t)Cfg<TM>::TSLOT * KT;
+    return reinterpret_cast<float*>(smem + token_bytes(KT));
   }
-  __device__ static float* scratch(uint8_t* smem, int KT, int NB) { return weight_scales(smem, KT) + 2 * (size_t)NB * KT; }
+  __device__ static float* scratch(uint8_t* smem, int KT, int NB) {
+    return reinterpret_cast<float*>(smem + token_bytes(KT) + weight_bytes(KT, NB));
+  }
 };
 
 // ------------------------------------------------------------------------------------------
@@ -354,16 +423,21 @@ struct Lds {
 //
 // wband(n, w) gives the scalar byte offset of sub-tile w's 16-row band in N
 // tile n (band row * kdim) within the expert's weight block `wrsrc`; kdim is
-// the K extent in bytes (H for GEMM1, I for GEMM2).
-template <int TM, bool GATED, bool PACKED, typename WBand, typename Epi>
+// the K extent in bytes (H for GEMM1, I for GEMM2).  MXFP8: `srsrc` covers
+// the expert's E8M0 weight scales, row-major [rows][kdim / 32]; lane l's
+// scale of a K step is one byte at row band + l % 16, block 4k + l / 16,
+// loaded with the step's weights into the same ring.
+template <int TM, bool GATED, bool PACKED, bool MX, typename WBand, typename Epi>
 __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& tb,
                                             const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
-                                            __amdgpu_buffer_rsrc_t wrsrc, int kdim, int sb_sel, int KT, int nn,
-                                            int tid, int lane, v4f (&acc)[Cfg<TM>::TS][2], WBand wband, Epi epi) {
+                                            __amdgpu_buffer_rsrc_t wrsrc, __amdgpu_buffer_rsrc_t srsrc, int kdim,
+                                            int sb_sel, int KT, int nn, int tid, int lane,
+                                            v4f (&acc)[Cfg<TM>::TS][2], WBand wband, Epi epi) {
   using C = Cfg<TM>;
-  constexpr int TS = C::TS, D = C::D, APW = C::A_PER_WAVE;
-  const float* SAs = Lds<TM>::token_scales(smem);
-  const float* SBs = Lds<TM>::weight_scales(smem, KT);
+  constexpr int TS = C::TS, D = C::D, APW = C::A_PER_WAVE, TSW = C::TSW;
+  const float* SAs = Lds<TM, MX>::token_scales(smem);
+  const float* SBs = Lds<TM, MX>::weight_scales(smem, KT);
+  const uint8_t* SXs = reinterpret_cast<const uint8_t*>(SAs);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const int S = nn * KT;
   // this lane's two 16-byte reads of token sub-tile 0 (sub-tile ts adds 2048 bytes:
@@ -379,15 +453,22 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     return join(*reinterpret_cast<const v4i*>(t + o0 + 2048 * ts), *reinterpret_cast<const v4i*>(t + o1 + 2048 * ts));
   };
 
-  v8i wr[D][2];   // weight ring: slot s holds step j with j % D == s
+  v8i wr[D][2];        // weight ring: slot s holds step j with j % D == s
+  uint32_t wsc[D][2];  // MXFP8: the lane's weight scale code of each ring slot
 
   const int wvoff = weight_lane_offset<PACKED>(lane, kdim);
+  const int svoff = r0 * (kdim >> 5) + g;       // MXFP8: the lane's scale byte within a band's K step
   constexpr int kKStep = PACKED ? 2048 : kKB;   // bytes between K steps within a band
   int nw = 0, kw = 0;
   int wb[2] = {wband(0, 0), wband(0, 1)};
   auto load_w = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wrsrc, wvoff, wb[w] + kw * kKStep);
+    if constexpr (MX) {
+      // band row * kdim / 32 = the band's first scale byte; 4 blocks per K step
+#pragma unroll
+      for (int w = 0; w < 2; ++w) wsc[s][w] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, svoff, (wb[w] >> 5) + 4 * kw, 0);
+    }
     if (kw + 1 < KT) {
       ++kw;
     } else if (nw + 1 < nn) {
@@ -416,24 +497,33 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   // The direct-to-LDS loads a wave issued one step back (for the step after
   // next) must have landed before the barrier that hands their buffer to the
   // other waves.  Vector memory operations complete in issue order for the
-  // counter, and younger than those loads are that step's 4 weight loads and
-  // this step's APW + 4 loads, so the wait is vmcnt(8 + APW).  Every step
+  // counter, and younger than those loads are that step's WL weight loads
+  // and this step's APW + WL loads (WL = 4 weight fragment loads, plus the 2
+  // scale bytes for MXFP8), so the wait is vmcnt(2 WL + APW).  Every step
   // issues all of them (the producers never skip), so the count holds.
-  auto publish_wait = [&]() __attribute__((always_inline)) { vmcnt_wait<8 + APW>(); };
+  constexpr int WL = MX ? 6 : 4;
+  auto publish_wait = [&]() __attribute__((always_inline)) { vmcnt_wait<2 * WL + APW>(); };
 
   // carried across the step boundary: the first two fragments and the scales of the next step
   v8i af[3];
   float sa[TS];
   float sb0, sb1;
+  uint32_t sx[TSW];   // MXFP8 token scale codes
   auto read_scales = [&](int n, int k) __attribute__((always_inline)) {
-    read_token_scales<TS>(SAs + (size_t)k * C::TSLOT + scale_slot<TS>(r0, 0), sa);
-    const float* b = SBs + 2 * ((size_t)n * KT + k);
-    if constexpr (GATED) {
-      const v2f v = *reinterpret_cast<const v2f*>(b);
-      sb0 = v[0];
-      sb1 = v[1];
+    if constexpr (MX) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(SXs + ((4 * k + g) * 16 + r0) * 4 * TSW);
+#pragma unroll
+      for (int i = 0; i < TSW; ++i) sx[i] = p[i];
     } else {
-      sb0 = sb1 = b[sb_sel];
+      read_token_scales<TS>(SAs + (size_t)k * C::TSLOT + scale_slot<TS>(r0, 0), sa);
+      const float* b = SBs + 2 * ((size_t)n * KT + k);
+      if constexpr (GATED) {
+        const v2f v = *reinterpret_cast<const v2f*>(b);
+        sb0 = v[0];
+        sb1 = v[1];
+      } else {
+        sb0 = sb1 = b[sb_sel];
+      }
     }
   };
   auto prefetch = [&](int bi, int n, int k) __attribute__((always_inline)) {
@@ -448,19 +538,28 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   auto step = [&](int s, int nx, int kx) __attribute__((always_inline)) {
     dma_a((s + 3) & 3);        // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
     __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
-    v4f pr[2][2];
-    auto fold = [&](int ts) __attribute__((always_inline)) {
-      acc[ts][0] += pr[ts & 1][0] * (sa[ts] * sb0);
-      acc[ts][1] += pr[ts & 1][1] * (sa[ts] * sb1);
-    };
+    if constexpr (MX) {
 #pragma unroll
-    for (int ts = 0; ts < TS; ++ts) {
-      if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
-      pr[ts & 1][0] = mfma16x16x128_fp8(wr[s][0], af[ts % 3], zero);
-      pr[ts & 1][1] = mfma16x16x128_fp8(wr[s][1], af[ts % 3], zero);
-      if (ts >= 1) fold(ts - 1);
+      for (int ts = 0; ts < TS; ++ts) {
+        if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
+        acc[ts][0] = mfma16x16x128_mx_sel(ts & 3, wr[s][0], af[ts % 3], acc[ts][0], wsc[s][0], sx[ts >> 2]);
+        acc[ts][1] = mfma16x16x128_mx_sel(ts & 3, wr[s][1], af[ts % 3], acc[ts][1], wsc[s][1], sx[ts >> 2]);
+      }
+    } else {
+      v4f pr[2][2];
+      auto fold = [&](int ts) __attribute__((always_inline)) {
+        acc[ts][0] += pr[ts & 1][0] * (sa[ts] * sb0);
+        acc[ts][1] += pr[ts & 1][1] * (sa[ts] * sb1);
+      };
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) {
+        if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
+        pr[ts & 1][0] = mfma16x16x128_fp8(wr[s][0], af[ts % 3], zero);
+        pr[ts & 1][1] = mfma16x16x128_fp8(wr[s][1], af[ts % 3], zero);
+        if (ts >= 1) fold(ts - 1);
+      }
+      fold(TS - 1);
     }
-    fold(TS - 1);
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
       asm volatile("" : "+v"(acc[ts][0]));
@@ -479,13 +578,13 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
 
   // prologue: rows of steps 0..2 into buffers 0..2, weights of steps 0..3;
   // rows of steps 0 and 1 must have landed before the first barrier (younger
-  // than them: step 2's rows and the 16 weight loads)
+  // than them: step 2's rows and the D * WL weight loads)
   dma_a(0);
   dma_a(1);
   dma_a(2);
 #pragma unroll
   for (int s = 0; s < D; ++s) load_w(s);
-  vmcnt_wait<APW + 4 * D>();
+  vmcnt_wait<APW + WL * D>();
   __syncthreads();
   prefetch(0, 0, 0);
 
@@ -523,15 +622,17 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
 }
 
 // ------------------------------------------------------------------------------------------
-// GEMM1 + SwiGLU + 1x128 FP8 requantisation over a run of N tiles of 128 I
+// GEMM1 + SwiGLU + FP8 requantisation over a run of N tiles of 128 I
 // columns, for a tile body of TM rows; rows tc.h.. of the body are past the
 // expert's segment and are treated as padding (read token 0, never stored).
-template <int TM, bool PACKED>
+// FP8: one 1x128 block per row and N tile, fp32 scale amax / 448.  MXFP8:
+// four 1x32 blocks per row and N tile, E8M0 codes.
+template <int TM, bool PACKED, bool MX>
 __device__ __forceinline__ void gemm1_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ x,
-    const float* __restrict__ x_scale, const uint8_t* __restrict__ w13, const float* __restrict__ w13_scale,
-    const int32_t* __restrict__ sorted_src, int K, int H, int I, int NB, uint8_t* __restrict__ q,
-    float* __restrict__ q_scale) {
+    const scale_t<MX>* __restrict__ x_scale, const uint8_t* __restrict__ w13,
+    const scale_t<MX>* __restrict__ w13_scale, const int32_t* __restrict__ sorted_src, int K, int H, int I,
+    int NB, uint8_t* __restrict__ q, scale_t<MX>* __restrict__ q_scale) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS;
   const int NT = I / 128;
@@ -542,9 +643,7 @@ __device__ __forceinline__ void gemm1_tile(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int KT = H / kKB, HB = H / kKB, IB = I / 128;
-  float* SAs = Lds<TM>::token_scales(smem);
-  float* SBs = Lds<TM>::weight_scales(smem, KT);
-  float* red = Lds<TM>::scratch(smem, KT, NB);
+  float* red = Lds<TM, MX>::scratch(smem, KT, NB);
 
   // source of this lane's 16-byte chunk of each direct-to-LDS block: LDS
   // chunk qc holds row qc / 8, logical chunk (qc % 8) XOR the row's key
@@ -562,21 +661,32 @@ __device__ __forceinline__ void gemm1_tile(
   const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
   const __amdgpu_buffer_rsrc_t wrsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, 2 * I * H, kWeightRsrcFlags);
-  const float* sexp = w13_scale + (size_t)tc.e * (2 * IB) * HB;
   auto wband = [&](int n, int w) -> int {
     const int c = 128 * (nt0 + n) + 16 * wave;   // first row of the 16-row band
     return (w ? I + c : c) * H;
   };
-  stage_weight_scales(SBs, KT, nn, [&](int n, int which) -> const float* {
-    return sexp + (size_t)(which ? IB + nt0 + n : nt0 + n) * HB;
-  }, tid);
-  stage_token_scales<TM>(SAs, KT, [&](int r) -> const float* {
-    const int src = r < h ? sorted_src[tc.p0 + r] : -1;
-    return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
-  }, tid);
+  __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
+  if constexpr (MX) {
+    const uint8_t* sexp = w13_scale + (size_t)tc.e * (2 * (size_t)I) * (H / 32);
+    srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, 2 * I * (H / 32), kWeightRsrcFlags);
+    stage_token_scales_mx<TM>(smem, KT, [&](int r) -> const uint8_t* {
+      const int src = r < h ? sorted_src[tc.p0 + r] : -1;
+      return src >= 0 ? x_scale + (size_t)(src / K) * (H / 32) : nullptr;
+    }, tid);
+  } else {
+    const float* sexp = w13_scale + (size_t)tc.e * (2 * IB) * HB;
+    stage_weight_scales(Lds<TM, MX>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
+      return sexp + (size_t)(which ? IB + nt0 + n : nt0 + n) * HB;
+    }, tid);
+    stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
+      const int src = r < h ? sorted_src[tc.p0 + r] : -1;
+      return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
+    }, tid);
+  }
 
-  // epilogue of N tile n: act = silu(gate) * up; per token row amax over the
-  // tile's 128 columns (one requant block) across the 8 waves through LDS
+  // epilogue of N tile n: act = silu(gate) * up; per token row amax over a
+  // requant block's columns: FP8 all 8 waves (128 columns), MXFP8 the wave
+  // pair 2p, 2p+1 (32 columns), through LDS
   auto epi = [&](int n, v4f (&acc)[TS][2]) __attribute__((always_inline)) {
     const int n0 = 128 * (nt0 + n), c0 = n0 + 16 * wave;
     float act[TS][4];
@@ -600,15 +710,23 @@ __device__ __forceinline__ void gemm1_tile(
     for (int ts = 0; ts < TS; ++ts) {
       if (16 * ts >= h) break;   // sub-tiles past the segment (h is a multiple of 16)
       const int row = 16 * ts + l16;
-      float amax = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w * TM + row]);
-      const float sc = amax > 0.f ? amax / kE4m3Max : 1.0f;
-      const float inv = 1.0f / sc;
       const size_t prow = (size_t)(tc.p0 + row);
-      *reinterpret_cast<uint32_t*>(q + prow * I + c0 + 4 * g) =
-          pack4_e4m3(act[ts][0] * inv, act[ts][1] * inv, act[ts][2] * inv, act[ts][3] * inv);
-      if (wave == 0 && g == 0) q_scale[prow * IB + n0 / 128] = sc;
+      uint32_t* qd = reinterpret_cast<uint32_t*>(q + prow * I + c0 + 4 * g);
+      if constexpr (MX) {
+        const float amax = fmaxf(red[wave * TM + row], red[(wave ^ 1) * TM + row]);
+        const int e = e8m0_exponent(amax);
+        *qd = pack4_e4m3(ldexpf(act[ts][0], -e), ldexpf(act[ts][1], -e), ldexpf(act[ts][2], -e),
+                         ldexpf(act[ts][3], -e));
+        if ((wave & 1) == 0 && g == 0) q_scale[prow * (I / 32) + c0 / 32] = (uint8_t)(e + 127);
+      } else {
+        float amax = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w * TM + row]);
+        const float sc = amax > 0.f ? amax / kE4m3Max : 1.0f;
+        const float inv = 1.0f / sc;
+        *qd = pack4_e4m3(act[ts][0] * inv, act[ts][1] * inv, act[ts][2] * inv, act[ts][3] * inv);
+        if (wave == 0 && g == 0) q_scale[prow * IB + n0 / 128] = sc;
+      }
     }
     // the next N tile's epilogue rewrites red only after the following step
     // barriers, by which point every wave has read it
@@ -617,7 +735,7 @@ __device__ __forceinline__ void gemm1_tile(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, true, PACKED>(smem, tb, a_src, wrsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
+  ws_mainloop<TM, true, PACKED, MX>(smem, tb, a_src, wrsrc, srsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
 }
 
 // The token buffers are the kernel's; each workgroup runs the tile body of
@@ -644,19 +762,19 @@ __device__ __forceinline__ void gemm1_tile(
     default: if constexpr (TMAX >= 160) { BODY(160); } break;                      \
   }
 
-template <int TMAX, bool PACKED>
+template <int TMAX, bool PACKED, bool MX>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
-    const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
-    const float* __restrict__ w13_scale, const int32_t* __restrict__ padded,
+    const uint8_t* __restrict__ x, const scale_t<MX>* __restrict__ x_scale, const uint8_t* __restrict__ w13,
+    const scale_t<MX>* __restrict__ w13_scale, const int32_t* __restrict__ padded,
     const int32_t* __restrict__ sorted_src, int E, int K, int H, int I, int NB, uint8_t* __restrict__ q,
-    float* __restrict__ q_scale) {
+    scale_t<MX>* __restrict__ q_scale) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int NT = I / 128, NG = (NT + NB - 1) / NB;
   TileCoord tc;
   if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
   FP8MOE_TOKEN_BUFFERS(TMAX);
 #define FP8MOE_G1_BODY(TMV) \
-  gemm1_tile<TMV, PACKED>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB, q, q_scale)
+  gemm1_tile<TMV, PACKED, MX>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB, q, q_scale)
   FP8MOE_BODIES(FP8MOE_G1_BODY)
 #undef FP8MOE_G1_BODY
 }
@@ -665,12 +783,12 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
 // GEMM2 with the top-k weight epilogue, over a run of N tiles of 256 H
 // columns, for a tile body of TM rows; rows tc.h.. of the body are past the
 // expert's segment (they re-read the tile's last row and are never stored).
-template <int TM, bool PACKED>
+template <int TM, bool PACKED, bool MX>
 __device__ __forceinline__ void gemm2_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ q,
-    const float* __restrict__ q_scale, const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
-    const float* __restrict__ topk_weights, const int32_t* __restrict__ sorted_src, int H, int I, int NB,
-    uint16_t* __restrict__ Y) {
+    const scale_t<MX>* __restrict__ q_scale, const uint8_t* __restrict__ w2,
+    const scale_t<MX>* __restrict__ w2_scale, const float* __restrict__ topk_weights,
+    const int32_t* __restrict__ sorted_src, int H, int I, int NB, uint16_t* __restrict__ Y) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS;
   const int NT = (H + kTN - 1) / kTN;
@@ -681,9 +799,7 @@ __device__ __forceinline__ void gemm2_tile(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int KT = I / kKB, IB = I / kKB, HB = H / 128;
-  float* SAs = Lds<TM>::token_scales(smem);
-  float* SBs = Lds<TM>::weight_scales(smem, KT);
-  int* srow = reinterpret_cast<int*>(Lds<TM>::scratch(smem, KT, NB));
+  int* srow = reinterpret_cast<int*>(Lds<TM, MX>::scratch(smem, KT, NB));
   float* wrow_w = reinterpret_cast<float*>(srow + TM);
 
   // token rows: q rows p0.. (a pad row holds whatever is there; its outputs are never stored)
@@ -703,17 +819,27 @@ __device__ __forceinline__ void gemm2_tile(
     // bands past H (the last N tile when H % 256 == 128) read the last band
     return min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16) * I;
   };
-  // N tile n spans scale blocks 2(nt0+n) and 2(nt0+n)+1 (the second clamped
-  // at the last block; only columns < H are stored); waves 4..7 use the second
-  const float* sexp = w2_scale + (size_t)tc.e * HB * IB;
-  stage_weight_scales(SBs, KT, nn, [&](int n, int which) -> const float* {
-    const int nb = min(2 * (nt0 + n) + which, HB - 1);
-    return sexp + (size_t)nb * IB;
-  }, tid);
-  stage_token_scales<TM>(SAs, KT, [&](int r) -> const float* {
-    const int p = tc.p0 + r;
-    return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
-  }, tid);
+  __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
+  if constexpr (MX) {
+    const uint8_t* sexp = w2_scale + (size_t)tc.e * H * (size_t)(I / 32);
+    srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, H * (I / 32), kWeightRsrcFlags);
+    stage_token_scales_mx<TM>(smem, KT, [&](int r) -> const uint8_t* {
+      const int p = tc.p0 + r;
+      return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * (I / 32) : nullptr;
+    }, tid);
+  } else {
+    // N tile n spans scale blocks 2(nt0+n) and 2(nt0+n)+1 (the second clamped
+    // at the last block; only columns < H are stored); waves 4..7 use the second
+    const float* sexp = w2_scale + (size_t)tc.e * HB * IB;
+    stage_weight_scales(Lds<TM, MX>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
+      const int nb = min(2 * (nt0 + n) + which, HB - 1);
+      return sexp + (size_t)nb * IB;
+    }, tid);
+    stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
+      const int p = tc.p0 + r;
+      return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
+    }, tid);
+  }
   // source row and top-k weight of each tile row, for the epilogues
   for (int r = tid; r < TM; r += kThreads) {
     const int src = r < h ? sorted_src[tc.p0 + r] : -1;
@@ -745,13 +871,14 @@ __device__ __forceinline__ void gemm2_tile(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, false, PACKED>(smem, tb, a_src, wrsrc, I, wave >> 2, KT, nn, tid, lane, acc, wband, epi);
+  ws_mainloop<TM, false, PACKED, MX>(smem, tb, a_src, wrsrc, srsrc, I, wave >> 2, KT, nn, tid, lane, acc, wband,
+                                     epi);
 }
 
-template <int TMAX, bool PACKED>
+template <int TMAX, bool PACKED, bool MX>
 __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ w2,
-    const float* __restrict__ w2_scale, const float* __restrict__ topk_weights,
+    const uint8_t* __restrict__ q, const scale_t<MX>* __restrict__ q_scale, const uint8_t* __restrict__ w2,
+    const scale_t<MX>* __restrict__ w2_scale, const float* __restrict__ topk_weights,
     const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src, int E, int H, int I, int NB,
     uint16_t* __restrict__ Y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -760,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
   FP8MOE_TOKEN_BUFFERS(TMAX);
 #define FP8MOE_G2_BODY(TMV) \
-  gemm2_tile<TMV, PACKED>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB, Y)
+  gemm2_tile<TMV, PACKED, MX>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB, Y)
   FP8MOE_BODIES(FP8MOE_G2_BODY)
 #undef FP8MOE_G2_BODY
 }
@@ -774,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
 // (measured on GEMM2 at T=64 and T=8192: a quarter was fastest at both);
 // never so long that fewer than 2 workgroups per CU remain.  Then spread
 // evenly over the runs of an M tile.
-static int run_length(const GroupedRows& g, int tm, int NT, int KT) {
+static inline int run_length(const GroupedRows& g, int tm, int NT, int KT) {
   const int64_t cu = g.num_cu > 0 ? g.num_cu : 256;
   const int64_t mt_cap = g.cap / tm;
   int64_t mt_est = g.rows / tm + (g.E < g.rows ? g.E : g.rows) / 2 + 1;
@@ -789,20 +916,32 @@ static int run_length(const GroupedRows& g, int tm, int NT, int KT) {
   return (int)((NT + ng - 1) / ng);
 }
 
-size_t gemm_lds_bytes(int tile_m, int KT, int NB);
+template <bool MX>
+static inline size_t gemm_lds_bytes(int tile_m, int KT, int NB) {
+  switch (tile_m) {
+    case 16: return Lds<16, MX>::bytes(KT, NB);
+    case 32: return Lds<32, MX>::bytes(KT, NB);
+    case 64: return Lds<64, MX>::bytes(KT, NB);
+    case 128: return Lds<128, MX>::bytes(KT, NB);
+    case 144: return Lds<144, MX>::bytes(KT, NB);
+    default: return Lds<160, MX>::bytes(KT, NB);
+  }
+}
+
 // dynamic LDS beside the four static token buffers of a kernel with tiles of
 // up to tm rows
-static size_t max_dyn_lds(int tm) { return kMaxGemmLds - 4 * (size_t)tm * kKB; }
+static inline size_t max_dyn_lds(int tm) { return kMaxGemmLds - 4 * (size_t)tm * kKB; }
 
 constexpr int kRing = Cfg<16>::D;   // the weight ring depth of every tile body
 static_assert(Cfg<128>::D == kRing && Cfg<160>::D == kRing, "one ring depth");
 
 // run_length, shortened until the run's weight scales fit in LDS; one N tile
 // per workgroup unless the K steps fill whole rounds of the weight ring
-static int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
+template <bool MX>
+static inline int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
   if (KT % kRing != 0) return 1;
   int nb = run_length(g, tm, NT, KT);
-  while (nb > 1 && gemm_lds_bytes(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
+  while (nb > 1 && gemm_lds_bytes<MX>(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
   const int ng = (NT + nb - 1) / nb;
   return (NT + ng - 1) / ng;
 }
@@ -810,22 +949,11 @@ static int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
 // Workgroups for every possible tile: each tile holds >= 16 rows, and an
 // expert has at most one tile shorter than tm.  Those past the actual tile
 // count (known on the device only) exit at once.
-static unsigned grid_for(const GroupedRows& g, int tm, int ng) {
+static inline unsigned grid_for(const GroupedRows& g, int tm, int ng) {
   const int64_t by_rows = g.cap / 16, by_experts = g.cap / tm + g.E;
   const int64_t items = (by_rows < by_experts ? by_rows : by_experts) * ng;
   const int64_t b = (items + kNumXcd - 1) / kNumXcd * kNumXcd;
   return (unsigned)(b > 0 ? b : kNumXcd);
-}
-
-size_t gemm_lds_bytes(int tile_m, int KT, int NB) {
-  switch (tile_m) {
-    case 16: return Lds<16>::bytes(KT, NB);
-    case 32: return Lds<32>::bytes(KT, NB);
-    case 64: return Lds<64>::bytes(KT, NB);
-    case 128: return Lds<128>::bytes(KT, NB);
-    case 144: return Lds<144>::bytes(KT, NB);
-    default: return Lds<160>::bytes(KT, NB);
-  }
 }
 
 template <int TMAX, typename Kern>
@@ -833,30 +961,31 @@ static hipError_t allow_lds(Kern k) {
   return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_dyn_lds(TMAX));
 }
 
-hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w13,
-                        const float* w13_scale, const GroupedRows& g, int H, int I,
-                        uint8_t* q, float* q_scale, int tile_m, bool packed, hipStream_t stream) {
+template <bool MX>
+static hipError_t launch_gemm1_t(const uint8_t* x, const scale_t<MX>* x_scale, const uint8_t* w13,
+                                 const scale_t<MX>* w13_scale, const GroupedRows& g, int H, int I, uint8_t* q,
+                                 scale_t<MX>* q_scale, int tile_m, bool packed, hipStream_t stream) {
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
-#define FP8MOE_ATTR(TMV)                                                        \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, false>); \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, true>)
+#define FP8MOE_ATTR(TMV)                                                            \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, false, MX>); \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, true, MX>)
     FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128);
 #undef FP8MOE_ATTR
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (tile_m > kMaxTileGemm1) return hipErrorInvalidValue;
-  const int NT = I / 128, NB = fit_run(g, tile_m, NT, H / kKB), NG = (NT + NB - 1) / NB;
-  const size_t lds = gemm_lds_bytes(tile_m, H / kKB, NB);
+  const int NT = I / 128, NB = fit_run<MX>(g, tile_m, NT, H / kKB), NG = (NT + NB - 1) / NB;
+  const size_t lds = gemm_lds_bytes<MX>(tile_m, H / kKB, NB);
   if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
-#define FP8MOE_G1(TMV)                                                                                 \
-  if (packed)                                                                                          \
-    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, true>), grid, block, lds, stream, x, x_scale, w13, \
-                       w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale);       \
-  else                                                                                                 \
-    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, false>), grid, block, lds, stream, x, x_scale, w13, \
+#define FP8MOE_G1(TMV)                                                                                     \
+  if (packed)                                                                                              \
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, true, MX>), grid, block, lds, stream, x, x_scale, w13, \
+                       w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale);           \
+  else                                                                                                     \
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, false, MX>), grid, block, lds, stream, x, x_scale, w13, \
                        w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale)
   switch (tile_m) {
     case 16: FP8MOE_G1(16); break;
@@ -869,31 +998,33 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w2,
-                        const float* w2_scale, const float* topk_weights, const GroupedRows& g,
-                        int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream) {
+template <bool MX>
+static hipError_t launch_gemm2_t(const uint8_t* q, const scale_t<MX>* q_scale, const uint8_t* w2,
+                                 const scale_t<MX>* w2_scale, const float* topk_weights, const GroupedRows& g,
+                                 int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed,
+                                 hipStream_t stream) {
   if (tile_n != kTN) return hipErrorInvalidValue;
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
-#define FP8MOE_ATTR(TMV)                                                    \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, false>); \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, true>)
+#define FP8MOE_ATTR(TMV)                                                        \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, false, MX>); \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, true, MX>)
     FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144); FP8MOE_ATTR(160);
 #undef FP8MOE_ATTR
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (tile_m > kMaxTileGemm2) return hipErrorInvalidValue;
-  const int NT = (H + kTN - 1) / kTN, NB = fit_run(g, tile_m, NT, I / kKB), NG = (NT + NB - 1) / NB;
-  const size_t lds = gemm_lds_bytes(tile_m, I / kKB, NB);
+  const int NT = (H + kTN - 1) / kTN, NB = fit_run<MX>(g, tile_m, NT, I / kKB), NG = (NT + NB - 1) / NB;
+  const size_t lds = gemm_lds_bytes<MX>(tile_m, I / kKB, NB);
   if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
-#define FP8MOE_G2(TMV)                                                                                    \
-  if (packed)                                                                                             \
-    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, true>), grid, block, lds, stream, q, q_scale, w2, w2_scale, \
-                       topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y);                    \
-  else                                                                                                    \
-    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, false>), grid, block, lds, stream, q, q_scale, w2,       \
+#define FP8MOE_G2(TMV)                                                                                        \
+  if (packed)                                                                                                 \
+    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, true, MX>), grid, block, lds, stream, q, q_scale, w2,        \
+                       w2_scale, topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y);              \
+  else                                                                                                        \
+    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, false, MX>), grid, block, lds, stream, q, q_scale, w2,       \
                        w2_scale, topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y)
   switch (tile_m) {
     case 16: FP8MOE_G2(16); break;

@@ -26,9 +26,6 @@ hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int
                                 int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
                                 int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream);
 
-// Dynamic LDS of a grouped-GEMM launch with tile_m rows, KT K steps and runs of NB N tiles.
-size_t gemm_lds_bytes(int tile_m, int KT, int NB);
-
 // Largest tile heights.  GEMM2's body fits 256 VGPRs up to 160 rows.  GEMM1's
 // body (with its SwiGLU/requant epilogue) reaches the VGPR limit at 144 rows
 // and measured 3% slower than 128 there, so GEMM1 stops at 128.
@@ -50,6 +47,17 @@ hipError_t launch_gemm1(const uint8_t* x, const float* x_scale, const uint8_t* w
 hipError_t launch_gemm2(const uint8_t* q, const float* q_scale, const uint8_t* w2,
                         const float* w2_scale, const float* topk_weights, const GroupedRows& g,
                         int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream);
+
+// MXFP8 variants: every scale is an E8M0 code per 32 K elements of a row
+// (x_sf [T][H/32], w13_sf [E][2I][H/32], q_sf [cap][I/32], w2_sf [E][H][I/32]);
+// GEMM1 requantises the intermediate to 1x32 E8M0 + e4m3.  Same tiles, layouts
+// and limits as the FP8 launchers.
+hipError_t launch_gemm1_mx(const uint8_t* x, const uint8_t* x_sf, const uint8_t* w13, const uint8_t* w13_sf,
+                           const GroupedRows& g, int H, int I, uint8_t* q, uint8_t* q_sf, int tile_m, bool packed,
+                           hipStream_t stream);
+hipError_t launch_gemm2_mx(const uint8_t* q, const uint8_t* q_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                           const float* topk_weights, const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m,
+                           int tile_n, bool packed, hipStream_t stream);
 
 // Row-major e4m3 [E][N][K] -> MFMA-tiled layout (N % 16 == 0, K % 128 == 0).
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);

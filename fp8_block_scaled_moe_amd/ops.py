@@ -36,8 +36,11 @@ def _need(t, dtype, name, ndim=None):
 
 
 def _u8(t):
-    """fp8 e4m3 tensors may be passed as torch.float8_e4m3fn or as uint8 codes."""
-    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+    """fp8 e4m3 tensors may be passed as torch.float8_e4m3fn or as uint8 codes, E8M0
+    scale tensors as torch.float8_e8m0fnu or as uint8 codes."""
+    if t is not None and t.dtype in (torch.float8_e4m3fn, torch.float8_e8m0fnu):
+        return t.view(torch.uint8)
+    return t
 
 
 # ---------------------------------------------------------------- routing
@@ -168,6 +171,108 @@ def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, t
     check(lib().moe_gemm2_weighted(_p(q), _p(q_scale), _p(w2), _p(w2_scale), _p(route["padded_indptr"]),
                                    _p(route["sorted_src"]), _p(topk_weights), T, H, I, E, K, align, _p(Y), cap,
                                    tile_m, tile_n, weight_layout, _stream(dev)))
+    return Y
+
+
+# ---------------------------------------------------------------- MXFP8 variant
+
+def fused_mx_workspace_size(T, H, I, E, K):
+    n = ctypes.c_size_t(0)
+    check(lib().moe_fused_mxfp8_workspace_size(T, H, I, E, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace_mx(T, H, I, E, K, device):
+    """A device workspace for moe_fused_mxfp8."""
+    return torch.empty(fused_mx_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
+
+
+def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
+                    out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
+    """MXFP8 MoE layer (1x32 E8M0 scales on every operand; E8M0 codes as uint8).
+    x_sf [T, H/32], w13_sf [E, 2I, H/32], w2_sf [E, H, I/32].  Returns bf16 [T, H]."""
+    x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
+    x_sf, w13_sf, w2_sf = _u8(x_sf), _u8(w13_sf), _u8(w2_sf)
+    _need(x, torch.uint8, "x", 2)
+    _need(x_sf, torch.uint8, "x_sf", 2)
+    _need(w13, torch.uint8, "w13", 3)
+    _need(w13_sf, torch.uint8, "w13_sf", 3)
+    _need(w2, torch.uint8, "w2", 3)
+    _need(w2_sf, torch.uint8, "w2_sf", 3)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    K = topk_ids.shape[1]
+    if H2 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
+        raise ValueError("inconsistent x / w13 / w2 shapes")
+    if tuple(x_sf.shape) != (T, H // 32) or tuple(w13_sf.shape) != (E, 2 * I, H // 32) \
+            or tuple(w2_sf.shape) != (E, H, I // 32):
+        raise ValueError("inconsistent E8M0 scale shapes")
+    if tuple(topk_ids.shape) != (T, K) or tuple(topk_weights.shape) != (T, K):
+        raise ValueError("topk_ids / topk_weights must be [T, K]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", 2)
+    if workspace is None:
+        workspace = alloc_workspace_mx(T, H, I, E, K, dev)
+    check(lib().moe_fused_mxfp8(_p(x), _p(x_sf), _p(w13), _p(w13_sf), _p(w2), _p(w2_sf),
+                                _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
+                                workspace.numel() * workspace.element_size(), tile_m, tile_n, weight_layout,
+                                _stream(dev)))
+    return out
+
+
+def gemm1_swiglu_quant_mx(x, x_sf, w13, w13_sf, route, T, K, align, tile_m=-1,
+                          weight_layout=WEIGHTS_ROW_MAJOR, q=None, q_sf=None):
+    """MXFP8 GEMM1 + SwiGLU + 1x32 E8M0 requant stage.  Returns (q uint8 [cap, I], q_sf uint8
+    [cap, I/32]); q / q_sf given: written in place (rows the stage does not write keep their contents)."""
+    x, w13, x_sf, w13_sf = _u8(x), _u8(w13), _u8(x_sf), _u8(w13_sf)
+    _need(x, torch.uint8, "x", 2)
+    _need(x_sf, torch.uint8, "x_sf", 2)
+    _need(w13, torch.uint8, "w13", 3)
+    _need(w13_sf, torch.uint8, "w13_sf", 3)
+    E, I2, H = w13.shape
+    I = I2 // 2
+    if tuple(x_sf.shape) != (x.shape[0], H // 32) or tuple(w13_sf.shape) != (E, I2, H // 32):
+        raise ValueError("inconsistent E8M0 scale shapes")
+    cap = route["sorted_src"].numel()
+    dev = x.device
+    q = torch.zeros((cap, I), dtype=torch.uint8, device=dev) if q is None else q
+    qs = torch.zeros((cap, I // 32), dtype=torch.uint8, device=dev) if q_sf is None else _u8(q_sf)
+    _need(q, torch.uint8, "q", 2)
+    _need(qs, torch.uint8, "q_sf", 2)
+    if tuple(q.shape) != (cap, I) or tuple(qs.shape) != (cap, I // 32):
+        raise ValueError("q / q_sf must be [cap, I] / [cap, I/32]")
+    check(lib().moe_gemm1_swiglu_quant_mx(_p(x), _p(x_sf), _p(w13), _p(w13_sf), _p(route["padded_indptr"]),
+                                          _p(route["sorted_src"]), T, H, I, E, K, align, _p(q), _p(qs), cap,
+                                          tile_m, weight_layout, _stream(dev)))
+    return q, qs
+
+
+def gemm2_weighted_mx(q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
+                      weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
+    """MXFP8 GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H]; rows of dropped slots are not
+    written (zero when Y is allocated here)."""
+    q, q_sf, w2, w2_sf = _u8(q), _u8(q_sf), _u8(w2), _u8(w2_sf)
+    _need(q, torch.uint8, "q", 2)
+    _need(q_sf, torch.uint8, "q_sf", 2)
+    _need(w2, torch.uint8, "w2", 3)
+    _need(w2_sf, torch.uint8, "w2_sf", 3)
+    E, H, I = w2.shape
+    cap = route["sorted_src"].numel()
+    if tuple(q.shape) != (cap, I) or tuple(q_sf.shape) != (cap, I // 32) or tuple(w2_sf.shape) != (E, H, I // 32):
+        raise ValueError("inconsistent q / q_sf / w2_sf shapes")
+    dev = q.device
+    Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev) if Y is None else Y
+    _need(Y, torch.bfloat16, "Y", 2)
+    if tuple(Y.shape) != (T * K, H):
+        raise ValueError("Y must be [T*K, H]")
+    check(lib().moe_gemm2_weighted_mx(_p(q), _p(q_sf), _p(w2), _p(w2_sf), _p(route["padded_indptr"]),
+                                      _p(route["sorted_src"]), _p(topk_weights), T, H, I, E, K, align, _p(Y),
+                                      cap, tile_m, tile_n, weight_layout, _stream(dev)))
     return Y
 
 

@@ -186,6 +186,49 @@ int moe_gemm2_weighted(const void* q, const float* q_scale,
 int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E,
                 int32_t K, void* out, void* stream);
 
+/* ---------------------------------------------------------------- MXFP8 variant of the layer and its stages
+ * The same layer with MXFP8 operands: the SM120 grouped-GEMM page lists an
+ * mxfp8 grouped MoE GEMM family beside the FP8 groupwise one (its file list
+ * and benchmark lines), and the PR-8023 page fixes the MXFP8 block format.
+ * Every operand carries one E8M0 scale code (value 2^(code - 127)) per 32
+ * consecutive elements along the contraction dimension, applied inside the
+ * MFMA (no fp32 fold):
+ *   x_sf    uint8 [T, H/32]        activation scales
+ *   w13_sf  uint8 [E, 2I, H/32]    per weight row (gate rows first)
+ *   w2_sf   uint8 [E, H, I/32]
+ * and the intermediate is requantised as gated_act_fp8_quant does: per row
+ * and 32 columns of I, e = the smallest exponent with amax <= 448 * 2^e
+ * (clamped to [-127, 127], -127 for an all-zero block), q = e4m3(act * 2^-e),
+ *   q_sf    uint8 [cap, I/32]      E8M0 codes e + 127.
+ * Weights, tokens, routing, tiles, layouts, limits, errors, ownership and
+ * determinism are those of the FP8 entry points above; moe_pack_weights
+ * packs the e4m3 weights for FP8MOE_WEIGHTS_MFMA_TILED and the scale codes
+ * keep their row-major layout.  The workspace of moe_fused_mxfp8 is sized by
+ * moe_fused_mxfp8_workspace_size.
+ */
+int moe_fused_mxfp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                   size_t* bytes);
+int moe_fused_mxfp8(const void* x, const uint8_t* x_sf,
+                    const void* w13, const uint8_t* w13_sf,
+                    const void* w2, const uint8_t* w2_sf,
+                    const int32_t* topk_ids, const float* topk_weights,
+                    int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream);
+int moe_gemm1_swiglu_quant_mx(const void* x, const uint8_t* x_sf,
+                              const void* w13, const uint8_t* w13_sf,
+                              const int32_t* padded_indptr, const int32_t* sorted_src,
+                              int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                              void* q, uint8_t* q_sf, int64_t cap,
+                              int32_t tile_m, int32_t weight_layout, void* stream);
+int moe_gemm2_weighted_mx(const void* q, const uint8_t* q_sf,
+                          const void* w2, const uint8_t* w2_sf,
+                          const int32_t* padded_indptr, const int32_t* sorted_src,
+                          const float* topk_weights,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                          void* Y, int64_t cap, int32_t tile_m, int32_t tile_n,
+                          int32_t weight_layout, void* stream);
+
 /* ---------------------------------------------------------------- weight packing
  * moe_pack_weights: expert weights e4m3 [E, N, K] row-major (w13 with N = 2I,
  * K = H, or w2 with N = H, K = I) -> FP8MOE_WEIGHTS_MFMA_TILED, the layout

@@ -46,3 +46,58 @@ def dev_experts(t):
         def __getitem__(self, e):
             return t[e].cpu().numpy()
     return _V()
+
+
+# gfx950's fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) does not sum its 128
+# products exactly: against exact float64 sums over 2.6 M outputs (random e4m3
+# codes, unit and random E8M0 scales, zero and non-zero accumulators) its error
+# stayed below 4.7e-5 * sum|terms| (median 7e-7 * sum|terms|), the same with the
+# accumulator added inside the instruction or outside in fp32.  Tolerances
+# that follow GEMM results through a quantisation use this bound, with margin.
+MFMA_REL_BOUND = 2.0 ** -13
+
+
+def swiglu_error_bound(g, u, sg, su, rel=MFMA_REL_BOUND):
+    """Bound on |act_gpu - act_ref| for act = silu(g) * u when g and u carry errors up to
+    rel * sg and rel * su (sg, su = sum of |products| of each GEMM1 output); silu' <= 1.1,
+    plus fp32 SwiGLU evaluation (a few ulp of act)."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    dg, du = rel * np.asarray(sg, np.float64), rel * np.asarray(su, np.float64)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    act = silu * u
+    return 1.1 * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du + np.abs(act) * 2.0 ** -20
+
+
+_E4M3_SORTED = None
+
+
+def e4m3_rounding_interval(codes):
+    """The interval of (scaled) reals that round to each e4m3 code under saturating
+    round-to-nearest: [lo, hi] bounded by the midpoints to the neighbouring codes
+    (+-inf beyond +-448)."""
+    global _E4M3_SORTED
+    if _E4M3_SORTED is None:
+        v = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+        _E4M3_SORTED = np.unique(v[np.isfinite(v)])             # -448 .. 448, one zero
+    vals = _E4M3_SORTED
+    c = np.asarray(codes, dtype=np.uint8)
+    x = torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+    i = np.searchsorted(vals, x)
+    lo = np.where(i > 0, (vals[np.maximum(i - 1, 0)] + x) / 2, -np.inf)
+    hi = np.where(i < len(vals) - 1, (vals[np.minimum(i + 1, len(vals) - 1)] + x) / 2, np.inf)
+    return lo, hi
+
+
+def e8m0_exponent_range(amax_lo, amax_hi):
+    """Smallest and largest E8M0 exponent (smallest e with amax <= 448 * 2^e, clamped to
+    [-127, 127]) over block amax values in [amax_lo, amax_hi]."""
+    def ex(a):
+        a = np.maximum(np.asarray(a, np.float64), 0.0)
+        with np.errstate(divide="ignore"):
+            e = np.ceil(np.log2(np.where(a > 0, a, 1.0) / 448.0))
+        e = np.where(a > 448.0 * np.exp2(e), e + 1, e)                  # exact correction of the log
+        e = np.where(a <= 448.0 * np.exp2(e - 1), e - 1, e)
+        return np.clip(np.where(a > 0, e, -127), -127, 127).astype(np.int64)
+    return ex(amax_lo), ex(amax_hi)

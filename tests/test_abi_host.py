@@ -64,12 +64,14 @@ def test_route_permute_validation():
     assert "top-k" in lib().moe_last_error().decode() or lib().moe_last_error().decode()
 
 
-def _fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE, layout=0):
-    return lib().moe_fused_fp8(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn, layout,
-                               NULL)
+FUSED = ("moe_fused_fp8", "moe_fused_mxfp8")
 
 
-def test_fused_validation():
+@pytest.mark.parametrize("fn", FUSED)
+def test_fused_validation(fn):
+    def _fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE, layout=0):
+        return getattr(lib(), fn)(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn,
+                                  layout, NULL)
     assert _fused(T=-1) == E_SHAPE
     assert _fused(H=200) == E_ALIGN
     assert _fused(I=100) == E_ALIGN
@@ -93,29 +95,32 @@ def test_fused_validation():
     assert lib().moe_last_error().decode() == ""
 
 
-def test_workspace_size():
-    n = fm.fused_workspace_size(16, 256, 128, 4, 2)
+@pytest.mark.parametrize("size", [fm.fused_workspace_size, fm.fused_mx_workspace_size])
+def test_workspace_size(size):
+    n = size(16, 256, 128, 4, 2)
     R, cap = 32, 32 + 4 * 127
+    # q, its scales (a float per 128 columns or an E8M0 byte per 32: the same bytes), Y, sorted_src
     assert n >= cap * 128 + cap * 4 + R * 256 * 2 + cap * 4
-    big = fm.fused_workspace_size(8192, 7168, 2048, 256, 8)
+    big = size(8192, 7168, 2048, 256, 8)
     assert big < 2 ** 31
     with pytest.raises(fm.Fp8MoeError):
-        fm.fused_workspace_size(16, 100, 128, 4, 2)
+        size(16, 100, 128, 4, 2)
 
 
-def test_stage_validation():
+@pytest.mark.parametrize("mx", [False, True])
+def test_stage_validation(mx):
     L = lib()
-    g1 = lambda **k: L.moe_gemm1_swiglu_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("T", 16), 256, 128, 4, 2,
-                                              k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1),
-                                              k.get("layout", 0), NULL)
+    f1 = L.moe_gemm1_swiglu_quant_mx if mx else L.moe_gemm1_swiglu_quant
+    f2 = L.moe_gemm2_weighted_mx if mx else L.moe_gemm2_weighted
+    g1 = lambda **k: f1(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("T", 16), 256, 128, 4, 2, k.get("align", 16),
+                        FAKE, FAKE, k.get("cap", 100), k.get("tm", -1), k.get("layout", 0), NULL)
     assert g1(align=24) == E_ALIGN
     assert g1(align=16, tm=48) == E_TILE          # tile heights 16/32/64/128/144/160 only
     assert g1(cap=-1) == E_SHAPE
     assert g1(T=0) == OK
     assert g1(layout=3) == E_SHAPE
-    g2 = lambda **k: L.moe_gemm2_weighted(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 256, 128, 4, 2,
-                                          k.get("align", 16), FAKE, 100, k.get("tm", -1), k.get("tn", -1),
-                                          k.get("layout", 0), NULL)
+    g2 = lambda **k: f2(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 256, 128, 4, 2, k.get("align", 16), FAKE,
+                        100, k.get("tm", -1), k.get("tn", -1), k.get("layout", 0), NULL)
     assert g2(tn=64) == E_TILE
     assert g2(align=32, tm=96) == E_TILE
     assert g2(layout=2) == E_SHAPE

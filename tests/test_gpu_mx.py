@@ -1,0 +1,259 @@
+"""MXFP8 variant of the MoE layer (and its stages) on the GPU against the MX oracle.
+
+Same bar as the FP8 layer: relative Frobenius error <= 1e-2 and max abs
+error <= 0.05 * max|ref| for layer outputs; GEMM2 on integer operands with
+power-of-two E8M0 scales must match the float64 brute force bit for bit
+(every partial sum is exact in fp32), which pins the lane -> 32-K-block
+scale mapping of the block-scaled MFMA.  The intermediate is checked
+against a band derived from the MFMA's measured precision (MFMA_REL_BOUND in
+gpu_helpers): each E8M0 exponent and each e4m3 code must be what some
+activation within that band of the oracle's gives.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_moe_amd as fm
+import synth
+from oracle import moe as OM
+from oracle import formats as F
+from oracle.route import route_reference
+from tests.gpu_helpers import (say, assert_close_to_oracle, e4m3_ordinal, dev_experts, swiglu_error_bound,
+                               e4m3_rounding_interval, e8m0_exponent_range)
+
+pytestmark = pytest.mark.gpu
+
+TILES = (16, 32, 64, 128, 144, 160)
+
+
+def run_mx(p, tile_m=-1, layout=fm.WEIGHTS_ROW_MAJOR, w13=None, w2=None):
+    return fm.moe_fused_mxfp8(p.x_q, p.x_s, p.w13_q if w13 is None else w13, p.w13_s,
+                              p.w2_q if w2 is None else w2, p.w2_s, p.topk_ids, p.topk_weights,
+                              tile_m=tile_m, weight_layout=layout)
+
+
+def oracle_mx(ph, tokens=None, stages=False):
+    a = (ph.x_q.numpy(), ph.x_s.numpy(), ph.w13_q.numpy(), ph.w13_s.numpy(), ph.w2_q.numpy(), ph.w2_s.numpy(),
+         ph.topk_ids.numpy(), ph.topk_weights.numpy())
+    r = OM.moe_reference_mx(*a, tokens=tokens, return_stages=stages)
+    return r if stages else r[1]
+
+
+@pytest.fixture(scope="module")
+def tiny_mx():
+    d = synth.TINY
+    p = synth.moe_problem_mx(d["T"], d["H"], d["I"], d["E"], d["K"], synth.CFG_TINY)
+    return p, p.to("cuda")
+
+
+def test_tiny_all_tiles_and_layouts_match_oracle(tiny_mx):
+    ph, pd = tiny_mx
+    ref = oracle_mx(ph)
+    p13, p2 = fm.pack_weights(pd.w13_q), fm.pack_weights(pd.w2_q)
+    outs = []
+    for layout, w13, w2 in ((fm.WEIGHTS_ROW_MAJOR, None, None), (fm.WEIGHTS_MFMA_TILED, p13, p2)):
+        for tm in (-1,) + TILES:
+            say("tiny mx layout", layout, "tile_m", tm)
+            out = run_mx(pd, tm, layout, w13, w2)
+            torch.cuda.synchronize()
+            assert_close_to_oracle(out, ref, f"tiny mx layout={layout} tile_m={tm}")
+            outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "MX outputs differ between tile sizes or weight layouts"
+    assert torch.equal(run_mx(pd), outs[0]), "MX layer is not deterministic"
+
+
+def check_mx_requant(q, q_sf, st, A, W13):
+    """GPU intermediate (codes q, E8M0 q_sf) of one expert's rows against the oracle's
+    stages st, with A the rows' dequantised activations and W13 the expert's dequantised
+    gate/up weights.  The GEMM1 outputs carry at most MFMA_REL_BOUND * sum|terms| of
+    error (the MFMA's measured precision), so every block exponent must be the E8M0
+    exponent of some amax within the resulting band around the oracle's, and every code
+    the rounding of a value within the band around the oracle's activation (at the
+    GPU's own exponent)."""
+    I = W13.shape[0] // 2
+    H1, act = st["H1"], st["act"].astype(np.float64)
+    S = np.abs(A) @ np.abs(W13).T
+    dact = swiglu_error_bound(H1[:, :I], H1[:, I:], S[:, :I], S[:, I:])
+    n = act.shape[0]
+    blk = lambda m: m.reshape(n, I // 32, 32)
+    amax = np.abs(blk(act)).max(axis=2)
+    damax = blk(dact).max(axis=2)
+    e_lo, e_hi = e8m0_exponent_range(amax - damax, amax + damax)
+    e_gpu = q_sf.astype(np.int64) - 127
+    assert np.all((e_gpu >= e_lo) & (e_gpu <= e_hi)), "E8M0 exponent outside the band"
+    lo, hi = e4m3_rounding_interval(q)
+    scale = np.repeat(np.exp2(e_gpu.astype(np.float64)), 32, axis=1)
+    ok = (act + dact >= lo * scale) & (act - dact <= hi * scale)
+    assert np.all(ok), f"{np.count_nonzero(~ok)} codes are not a rounding of any value in the band"
+    # and in the typical case the codes are simply the oracle's
+    same = np.repeat(e_gpu == st["s"].astype(np.int64) - 127, 32, axis=1)
+    d = np.abs(e4m3_ordinal(q) - e4m3_ordinal(st["q"]))[same]
+    assert np.count_nonzero(d) <= 0.02 * max(d.size, 1)
+
+
+def test_tiny_stages_match_oracle(tiny_mx):
+    ph, pd = tiny_mx
+    T, H, I, E, K = ph.T, ph.H, ph.I, ph.E, ph.K
+    _, _, stages = oracle_mx(ph, stages=True)
+    w = ph.topk_weights.numpy()
+    x_deq = F.dequant_rows_mx(ph.x_q.numpy(), ph.x_s.numpy())
+    outs = []
+    for align in (16, 128):
+        say("tiny mx stages align", align)
+        r = fm.route_permute(pd.topk_ids, E, align)
+        q, qs = fm.gemm1_swiglu_quant_mx(pd.x_q, pd.x_s, pd.w13_q, pd.w13_s, r, T, K, align, tile_m=16)
+        Y = fm.gemm2_weighted_mx(q, qs, pd.w2_q, pd.w2_s, r, pd.topk_weights, T, K, align, tile_m=16)
+        out = fm.combine(Y, pd.topk_ids, E)
+        torch.cuda.synchronize()
+        ss = r["src_to_sorted"].cpu().numpy()
+        qh, qsh, Yh = q.cpu().numpy(), qs.cpu().numpy(), Y.float().cpu().numpy()
+        for e, st in stages.items():
+            pos = np.array([ss[t * K + j] for t, j in st["rows"]])
+            toks = [t for t, _ in st["rows"]]
+            W13 = F.dequant_rows_mx(ph.w13_q.numpy()[e], ph.w13_s.numpy()[e])
+            check_mx_requant(qh[pos], qsh[pos], st, x_deq[toks], W13)
+            ref_y = np.stack([w[t, j] * st["Y"][i] for i, (t, j) in enumerate(st["rows"])])
+            srcs = [t * K + j for t, j in st["rows"]]
+            assert_close_to_oracle(Yh[srcs], ref_y, f"mx Y expert {e}")
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]), "stages differ between routing alignments"
+    assert torch.equal(outs[0], run_mx(pd)), "fused MX layer differs from its stages"
+
+
+@pytest.mark.parametrize("tile_m", TILES)
+def test_gemm2_mx_integer_inputs_bit_exact(tile_m):
+    """Integer e4m3 values (|v| <= 4) with E8M0 scales 2^-2..2^2 per 32-K block on both
+    operands: every product is a multiple of 2^-4 below 2^8 and every partial sum
+    (at most 384 terms) stays below 2^17, so fp32 accumulation is exact and Y must
+    equal the float64 brute force rounded once to bf16.  I = 384 gives three K
+    steps (a partial round of the operand ring) and H = 384 a half-empty last N tile."""
+    rng = np.random.default_rng(43)
+    T, H, I, E, K = 40, 384, 384, 3, 2
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    align = 16
+    r = route_reference(ids, E, align)
+    cap = len(r["sorted_src"])
+    qv = rng.integers(-4, 5, size=(cap, I)).astype(np.float32)
+    q = torch.from_numpy(qv).to(torch.float8_e4m3fn).view(torch.uint8)
+    qsf = (127 + rng.integers(-2, 3, size=(cap, I // 32))).astype(np.uint8)
+    wv = rng.integers(-4, 5, size=(E, H, I)).astype(np.float32)
+    w2 = torch.from_numpy(wv).to(torch.float8_e4m3fn).view(torch.uint8)
+    wsf = (127 + rng.integers(-2, 3, size=(E, H, I // 32))).astype(np.uint8)
+    wts = np.ones((T, K), np.float32)
+    route_d = {k: torch.from_numpy(v).cuda() for k, v in r.items()}
+    say("gemm2 mx integer exact tile_m", tile_m)
+    Y = fm.gemm2_weighted_mx(q.cuda(), torch.from_numpy(qsf).cuda(), w2.cuda(), torch.from_numpy(wsf).cuda(),
+                             route_d, torch.from_numpy(wts).cuda(), T, K, align, tile_m=tile_m)
+    torch.cuda.synchronize()
+    Yh = Y.float().cpu().numpy()
+    for e in range(E):
+        wd = wv[e].astype(np.float64) * np.ldexp(1.0, np.repeat(wsf[e].astype(np.int64) - 127, 32, axis=1))
+        for p in range(r["padded_indptr"][e], r["padded_indptr"][e] + r["counts"][e]):
+            src = r["sorted_src"][p]
+            a = qv[p].astype(np.float64) * np.ldexp(1.0, np.repeat(qsf[p].astype(np.int64) - 127, 32))
+            exact = wd @ a
+            ref = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
+            assert np.array_equal(Yh[src], ref), (e, p)
+
+
+def test_mx_edge_cases(tiny_mx):
+    ph, pd = tiny_mx
+    E = ph.E
+    say("mx edge: T=0")
+    out = fm.moe_fused_mxfp8(pd.x_q[:0], pd.x_s[:0], pd.w13_q, pd.w13_s, pd.w2_q, pd.w2_s, pd.topk_ids[:0],
+                             pd.topk_weights[:0])
+    assert out.shape == (0, ph.H)
+    say("mx edge: dropped slots, unused experts")
+    ids = ph.topk_ids.numpy().copy()
+    ids[:, :] = np.where(ids == 3, 1, ids)      # expert 3 gets no tokens
+    ids[2, 1] = -1                              # dropped slot
+    ids[5, :] = E + 7                           # token with every slot dropped
+    ph2 = ph.with_tokens(ph.x_q, ph.x_s, torch.from_numpy(ids), ph.topk_weights)
+    pd2 = pd.with_tokens(pd.x_q, pd.x_s, torch.from_numpy(ids).cuda(), pd.topk_weights)
+    ref = oracle_mx(ph2)
+    for tm in (-1, 16, 128, 160):
+        out = run_mx(pd2, tm)
+        torch.cuda.synchronize()
+        assert_close_to_oracle(out, ref, f"mx edge tile_m={tm}")
+        assert torch.all(out[5] == 0)
+    say("mx edge: E=1 K=1")
+    p = synth.moe_problem_mx(33, 256, 256, 1, 1, synth.CFG_TINY, extra=(7,))
+    assert_close_to_oracle(run_mx(p.to("cuda")), oracle_mx(p), "mx E=1")
+
+
+# ---------------------------------------------------------------- skewed configs
+
+@pytest.fixture(scope="module")
+def skewed_weights_mx():
+    d = synth.SKEWED_DIMS
+    w13_q, w13_s = synth.expert_weight_set_mx(d["E"], 2 * d["I"], d["H"], synth.CFG_SKEWED, synth.TAG_W13)
+    w2_q, w2_s = synth.expert_weight_set_mx(d["E"], d["H"], d["I"], synth.CFG_SKEWED, synth.TAG_W2)
+    host = (w13_q, w13_s, w2_q, w2_s)
+    return host, tuple(t.cuda() for t in host)
+
+
+@pytest.mark.parametrize("T", synth.SKEWED_TS)
+def test_skewed_mx(T, skewed_weights_mx):
+    d = synth.SKEWED_DIMS
+    (h13, h13s, h2, h2s), (d13, d13s, d2, d2s) = skewed_weights_mx
+    x_q, x_s, ids, w = synth.moe_tokens_mx(T, d["H"], d["E"], d["K"], synth.CFG_SKEWED, extra=(T,),
+                                           zipf_s=synth.ZIPF_S)
+    ph = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q, x_s, h13, h13s, h2, h2s, ids, w)
+    pd = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), d13, d13s, d2, d2s,
+                         ids.cuda(), w.cuda())
+    tokens = None if T <= 512 else sorted(np.random.default_rng(T).choice(T, 48, replace=False).tolist())
+    ref = oracle_mx(ph, tokens)
+    outs = []
+    for tm in (-1,) + TILES:
+        say("skewed mx T", T, "tile_m", tm)
+        out = run_mx(pd, tm)
+        torch.cuda.synchronize()
+        got = out if tokens is None else out[tokens]
+        assert_close_to_oracle(got, ref, f"skewed mx T={T} tile_m={tm}")
+        outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+# ---------------------------------------------------------------- decode / prefill (full size)
+
+@pytest.fixture(scope="module")
+def large_weights_mx():
+    d = synth.LARGE_DIMS
+    say("generating 256-expert MXFP8 weights on the device")
+    w13_q, w13_s = synth.expert_weight_set_mx(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
+    w2_q, w2_s = synth.expert_weight_set_mx(d["E"], d["H"], d["I"], synth.CFG_LARGE, synth.TAG_W2, "cuda")
+    torch.cuda.synchronize()
+    return w13_q, w13_s, w2_q, w2_s
+
+
+def _large_mx(T, cfg, weights):
+    d = synth.LARGE_DIMS
+    x_q, x_s, ids, w = synth.moe_tokens_mx(T, d["H"], d["E"], d["K"], cfg)
+    w13_q, w13_s, w2_q, w2_s = weights
+    return synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), w13_q, w13_s, w2_q, w2_s,
+                           ids.cuda(), w.cuda())
+
+
+@pytest.mark.parametrize("name,T,cfg,ntok", [("decode", 64, synth.CFG_LARGE, 6), ("prefill", 8192, synth.CFG_PREFILL, 4)])
+def test_large_mx_sampled(name, T, cfg, ntok, large_weights_mx):
+    pd = _large_mx(T, cfg, large_weights_mx)
+    say(name, "mx fused auto tile")
+    out = run_mx(pd)
+    torch.cuda.synchronize()
+    tokens = sorted(np.random.default_rng(T + 2).choice(T, ntok, replace=False).tolist())
+    ref = OM.moe_reference_mx(pd.x_q.cpu().numpy(), pd.x_s.cpu().numpy(), dev_experts(pd.w13_q),
+                              dev_experts(pd.w13_s), dev_experts(pd.w2_q), dev_experts(pd.w2_s),
+                              pd.topk_ids.cpu().numpy(), pd.topk_weights.cpu().numpy(), tokens=tokens)[1]
+    assert_close_to_oracle(out[tokens], ref, f"{name} mx sampled tokens {tokens}")
+    say(name, "mx determinism and packed weights")
+    assert torch.equal(out, run_mx(pd))
+    p13, p2 = fm.pack_weights(pd.w13_q), fm.pack_weights(pd.w2_q)
+    assert torch.equal(out, run_mx(pd, layout=fm.WEIGHTS_MFMA_TILED, w13=p13, w2=p2))
+    del p13, p2
+    if name == "decode":
+        for tm in TILES:
+            say("decode mx tile_m", tm)
+            assert torch.equal(run_mx(pd, tm), out)
