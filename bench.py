@@ -23,14 +23,17 @@ The line also carries:
                 achievable-bandwidth reference, and the kernel whose HBM
                 counters calibrate the traffic figure.
   stages        per-stage average times of both workloads.
+  mxfp8         the MXFP8 variant of the layer (1x32 E8M0 scales on every
+                operand, intermediate requantised to 1x32 E8M0) on the same
+                prefill and decode shapes: us, TFLOP/s, GB/s and stage times.
   cpu_baseline  the CPU oracle timed on a bounded sample of prefill tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                      [--no-extras] [--profile {prefill,decode,gated}] [--traffic-kib F,W,SF,SW]
+                      [--no-extras] [--profile {prefill,decode,gated,mx}] [--traffic-kib F,W,SF,SW]
 
 --profile runs one workload only, for rocprofv3 passes: prefill (the layer,
 its stages and the 2 GiB stream kernel), decode (prefill, then the decode
-layer) or gated (the gated-act sweep).  --traffic-kib takes GEMM1's
+layer), gated (the gated-act sweep) or mx (the MXFP8 layer).  --traffic-kib takes GEMM1's
 FETCH_SIZE and WRITE_SIZE per dispatch and the stream kernel's (KiB, as
 rocprofv3 --pmc reports them) and fills roofline.traffic from them instead of
 the readings recorded in TRAFFIC_COUNTERS.
@@ -69,8 +72,8 @@ TRAFFIC_COUNTERS = {
     "gemm1_grbm_count": 36129440, "gemm1_grbm_dur_us": 2681.79,
     "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
-GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm.hip", "fp8_block_scaled_moe_amd/csrc/device_common.h",
-                "fp8_block_scaled_moe_amd/csrc/launch.h")
+GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm_kernels.h", "fp8_block_scaled_moe_amd/csrc/gemm1.hip",
+                "fp8_block_scaled_moe_amd/csrc/device_common.h", "fp8_block_scaled_moe_amd/csrc/launch.h")
 
 
 def gemm_sources_sha256():
@@ -299,6 +302,70 @@ def stage_times(p, steps, warmup):
     return out
 
 
+def mx_problem(T, cfg, weights, packed):
+    d = synth.LARGE_DIMS
+    x_q, x_sf, ids, w = synth.moe_tokens_mx(T, d["H"], d["E"], d["K"], cfg)
+    w13_q, w13_sf, w2_q, w2_sf = weights
+    p = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_sf.cuda(), w13_q, w13_sf, w2_q, w2_sf,
+                        ids.cuda(), w.cuda())
+    p.w13_p, p.w13_sp, p.w2_p, p.w2_sp = packed
+    return p
+
+
+def mx_algorithmic_bytes(p):
+    """As algorithmic_bytes, with one E8M0 byte per 32 elements for every scale."""
+    ids = p.topk_ids.cpu().numpy()
+    active = np.unique(ids[(ids >= 0) & (ids < p.E)]).size
+    H, I = p.H, p.I
+    per_expert = 3 * H * I + 3 * H * I // 32
+    io = p.T * H + p.T * (H // 32) + 8 * p.T * p.K + 2 * p.T * H
+    return active * per_expert + io, active
+
+
+def mx_bench(steps, warmup):
+    """The MXFP8 layer on the prefill and decode shapes (packed weights, auto tiles)."""
+    d = synth.LARGE_DIMS
+    log("generating 256-expert MXFP8 weights on the device")
+    w13 = synth.expert_weight_set_mx(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
+    w2 = synth.expert_weight_set_mx(d["E"], d["H"], d["I"], synth.CFG_LARGE, synth.TAG_W2, "cuda")
+    # the production layouts: e4m3 weights and their E8M0 scales packed once per weight set
+    packed = (fm.pack_weights(w13[0]), fm.pack_mx_scales(w13[1]), fm.pack_weights(w2[0]), fm.pack_mx_scales(w2[1]))
+    weights = (*w13, *w2)
+    res = {}
+    for name, T, cfg in (("prefill", 8192, synth.CFG_PREFILL), ("decode", 64, synth.CFG_LARGE)):
+        p = mx_problem(T, cfg, weights, packed)
+        ws = fm.alloc_workspace_mx(p.T, p.H, p.I, p.E, p.K, "cuda")
+        out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
+        L = fm.WEIGHTS_MFMA_TILED
+        ms = event_time_ms(lambda: fm.moe_fused_mxfp8(p.x_q, p.x_s, p.w13_p, p.w13_sp, p.w2_p, p.w2_sp, p.topk_ids,
+                                                      p.topk_weights, out=out, workspace=ws, weight_layout=L),
+                           steps if name == "prefill" else max(steps, 10), warmup)
+        align = 16
+        route = fm.route_permute(p.topk_ids, p.E, align)
+        q, qs = fm.gemm1_swiglu_quant_mx(p.x_q, p.x_s, p.w13_p, p.w13_sp, route, p.T, p.K, align, weight_layout=L)
+        Y = fm.gemm2_weighted_mx(q, qs, p.w2_p, p.w2_sp, route, p.topk_weights, p.T, p.K, align, weight_layout=L)
+        n = max(3, steps // 2)
+        g1 = event_time_ms(lambda: fm.gemm1_swiglu_quant_mx(p.x_q, p.x_s, p.w13_p, p.w13_sp, route, p.T, p.K, align,
+                                                            weight_layout=L, q=q, q_sf=qs), n, 1)
+        g2 = event_time_ms(lambda: fm.gemm2_weighted_mx(q, qs, p.w2_p, p.w2_sp, route, p.topk_weights, p.T, p.K,
+                                                        align, weight_layout=L, Y=Y), n, 1)
+        nbytes, active = mx_algorithmic_bytes(p)
+        flops = layer_flops(p)
+        g1_tflops = 4.0 * p.T * p.K * p.H * p.I / (g1 * 1e-3) / 1e12
+        res[name] = {"us_per_layer": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4), "gemm1_TFLOPs": round(g1_tflops, 1),
+                     "algorithmic_bytes": int(nbytes), "active_experts": int(active),
+                     "workload": f"{name} T={T} H=7168 I=2048 E=256 top-8, MXFP8 (1x32 E8M0) operands"}
+        log(f"mxfp8 {name}", res[name])
+        del ws, out, q, qs, Y
+    del packed, w13, w2
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(p, ntok=20):
     """The CPU oracle, as it stands, on a bounded sample of prefill tokens."""
     from oracle.moe import moe_reference
@@ -329,7 +396,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the gated-act and skewed sweeps")
-    ap.add_argument("--profile", choices=("prefill", "decode", "gated"), default=None,
+    ap.add_argument("--profile", choices=("prefill", "decode", "gated", "mx"), default=None,
                     help="one workload only, for rocprofv3 passes: prefill (+ stages, stream kernel), "
                          "decode (+ stages) or gated (the gated-act sweep)")
     ap.add_argument("--traffic-kib", default=None,
@@ -342,6 +409,9 @@ def main():
     torch.cuda.init()
     if args.profile == "gated":
         print(json.dumps({"profile": "gated", "gated_act": gated_act_bench(iters=5)}), flush=True)
+        return
+    if args.profile == "mx":
+        print(json.dumps({"profile": "mx", "mxfp8": mx_bench(args.steps, args.warmup)}), flush=True)
         return
     d = synth.LARGE_DIMS
     log("generating 256-expert fp8 weights on the device")
@@ -457,6 +527,8 @@ def main():
         result["gated_act"] = gated_act_bench()
         log("skewed-routing sweep")
         result["skewed"] = skewed_bench()
+        log("MXFP8 layer")
+        result["mxfp8"] = mx_bench(max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = cpu_baseline(pre)

@@ -33,6 +33,8 @@ SIGNATURES = {
     "moe_gemm2_weighted_mx": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                              _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
     "moe_pack_weights": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
+    "moe_pack_mx_scales_bytes": (_i64, [_i64, _i32, _i32]),
+    "moe_pack_mx_scales": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "gated_act_fp8_quant": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _vp]),
     "moe_select_tile": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),

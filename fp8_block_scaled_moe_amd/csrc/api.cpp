@@ -362,6 +362,25 @@ int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out,
   return ok();
 }
 
+int64_t moe_pack_mx_scales_bytes(int64_t E, int32_t N, int32_t K) {
+  if (E < 1 || N <= 0 || K <= 0 || N % 16 || K % 128)
+    return fail(FP8MOE_ERR_SHAPE, "MX scale pack needs E >= 1, N %% 16 == 0, K %% 128 == 0 (E=%lld N=%d K=%d)",
+                (long long)E, N, K);
+  ok();
+  return mx_scales_packed_bytes(E, N, K);
+}
+
+int moe_pack_mx_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {
+  const int64_t n = moe_pack_mx_scales_bytes(E, N, K);
+  if (n < 0) return (int)n;
+  if (!in || !out) return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out, na = (uintptr_t)(E * (int64_t)N * (K / 32));
+  if (a < b + (uintptr_t)n && b < a + na) return fail(FP8MOE_ERR_SHAPE, "pack in and out overlap");
+  hipError_t err = launch_pack_mx_scales(in, E, N, K, static_cast<uint8_t*>(out), (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "pack_mx_scales launch");
+  return ok();
+}
+
 int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E, int32_t K, void* out,
                 void* stream) {
   if (T < 0 || H <= 0 || E < 1) return fail(FP8MOE_ERR_SHAPE, "invalid T/H/E");

@@ -110,18 +110,37 @@ using scale_t = std::conditional_t<MX, uint8_t, float>;
 // order), so the 32-K block k of the step is bytes 0..15 of lane groups
 // 2(k%2), 2(k%2)+1 for k < 2 and bytes 16..31 of them for k >= 2 -- exactly
 // the elements lane 16k + row's scale covers.
-template <int SEL>
+template <int SA, int SB>
 __device__ __forceinline__ v4f mfma16x16x128_mx(const v8i& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, SEL, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, SA, (int)sa, SB, (int)sb);
 }
-__device__ __forceinline__ v4f mfma16x16x128_mx_sel(int sel, const v8i& a, const v8i& b, const v4f& c, uint32_t sa,
-                                                    uint32_t sb) {
-  switch (sel) {   // sel is a constant of the unrolled sub-tile loop
-    case 0: return mfma16x16x128_mx<0>(a, b, c, sa, sb);
-    case 1: return mfma16x16x128_mx<1>(a, b, c, sa, sb);
-    case 2: return mfma16x16x128_mx<2>(a, b, c, sa, sb);
-    default: return mfma16x16x128_mx<3>(a, b, c, sa, sb);
+// byte sela of sa and byte selb of sb; both are constants of the unrolled loops
+__device__ __forceinline__ v4f mfma16x16x128_mx_sel(int sela, int selb, const v8i& a, const v8i& b, const v4f& c,
+                                                    uint32_t sa, uint32_t sb) {
+#define FP8MOE_MX_CASE(A, B) \
+  case 4 * A + B: return mfma16x16x128_mx<A, B>(a, b, c, sa, sb);
+  switch (4 * sela + selb) {
+    FP8MOE_MX_CASE(0, 0) FP8MOE_MX_CASE(0, 1) FP8MOE_MX_CASE(0, 2) FP8MOE_MX_CASE(0, 3)
+    FP8MOE_MX_CASE(1, 0) FP8MOE_MX_CASE(1, 1) FP8MOE_MX_CASE(1, 2) FP8MOE_MX_CASE(1, 3)
+    FP8MOE_MX_CASE(2, 0) FP8MOE_MX_CASE(2, 1) FP8MOE_MX_CASE(2, 2) FP8MOE_MX_CASE(2, 3)
+    FP8MOE_MX_CASE(3, 0) FP8MOE_MX_CASE(3, 1) FP8MOE_MX_CASE(3, 2)
+    default: return mfma16x16x128_mx<3, 3>(a, b, c, sa, sb);
   }
+#undef FP8MOE_MX_CASE
+}
+
+// MXFP8 weight scales in the MFMA-tiled layout (moe_pack_mx_scales): per
+// 16-row band, groups of 4 K steps of 256 bytes, lane l's dword holding its
+// scale code of each of the 4 steps, so a wave reads the scales of a whole
+// round of the operand ring with one contiguous dword load per band.
+constexpr int kMxScaleGroup = 4;     // K steps per packed scale dword
+__host__ __device__ constexpr int mx_scale_groups(int KT) { return (KT + kMxScaleGroup - 1) / kMxScaleGroup; }
+
+// Bytes of one expert's MXFP8 weight scales for N rows and a K extent of kdim:
+// row-major [N][kdim/32], or MFMA-tiled [N/16][groups][64 lanes][4].
+template <bool PACKED>
+__host__ __device__ constexpr int mx_weight_scale_bytes(int N, int kdim) {
+  return PACKED ? N / 16 * mx_scale_groups(kdim / kKB) * 256 : N * (kdim / 32);
 }
 
 __device__ __forceinline__ int swz_key(int r) { return ((r >> 1) & 7) ^ (((r >> 2) ^ (r >> 3)) & 1); }
@@ -316,19 +335,37 @@ __device__ __forceinline__ int scale_slot(int l16, int ts) {
   else return l16 * TS + ts;
 }
 
+// Scale staging issues a batch of kStageBatch loads per thread before any of
+// their LDS stores (a load-then-store loop would wait out one global load
+// latency per iteration).  Loads are unconditional: out-of-range indices are
+// clamped to a valid element and pad rows read a valid row, their stored
+// value replaced by 0.
+constexpr int kStageBatch = 8;
+
 // The token scales of the M tile -> LDS as [kb][TSLOT] in scale_slot order.
-// row_scale(r) gives the row's scale vector (nullptr for a pad row).  Each
-// thread keeps one row and walks its K steps, so after the one row lookup
-// its loads are independent.
+// row_scale(r) gives the row's scale vector (nullptr for a pad row); any_row
+// is a valid row (read in place of a pad row's, never stored).  Each thread
+// keeps one row and walks its K steps.
 template <int TM, typename RowScale>
-__device__ __forceinline__ void stage_token_scales(float* SAs, int KT, RowScale row_scale, int tid) {
+__device__ __forceinline__ void stage_token_scales(float* SAs, int KT, RowScale row_scale, const float* any_row,
+                                                   int tid) {
   constexpr int TS = Cfg<TM>::TS, TSLOT = Cfg<TM>::TSLOT;
   constexpr int TPR = kThreads / TM;   // threads per row
   const int r = tid / TPR, part = tid % TPR;
   if (r >= TM) return;
   const float* rs = row_scale(r);
+  const float* src = rs ? rs : any_row;
   float* dst = SAs + scale_slot<TS>(r & 15, r >> 4);
-  for (int kb = part; kb < KT; kb += TPR) dst[kb * TSLOT] = rs ? rs[kb] : 0.f;
+  for (int k0 = part; k0 < KT; k0 += TPR * kStageBatch) {
+    float v[kStageBatch];
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) v[b] = src[min(k0 + b * TPR, KT - 1)];
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int kb = k0 + b * TPR;
+      if (kb < KT) dst[kb * TSLOT] = rs ? v[b] : 0.f;
+    }
+  }
 }
 
 // The two weight block-scale rows of each N tile of the run -> LDS as
@@ -337,10 +374,24 @@ __device__ __forceinline__ void stage_token_scales(float* SAs, int KT, RowScale 
 // LDS queue too).  rows(n, which) gives the scale row.
 template <typename Rows>
 __device__ __forceinline__ void stage_weight_scales(float* SBs, int KT, int nn, Rows rows, int tid) {
-  for (int i = tid; i < nn * KT; i += kThreads) {
-    const int n = i / KT, kb = i - n * KT;
-    SBs[2 * i] = rows(n, 0)[kb];
-    SBs[2 * i + 1] = rows(n, 1)[kb];
+  const int total = nn * KT;
+  for (int i0 = tid; i0 < total; i0 += kThreads * kStageBatch) {
+    float v[kStageBatch][2];
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int i = min(i0 + b * kThreads, total - 1);
+      const int n = i / KT, kb = i - n * KT;
+      v[b][0] = rows(n, 0)[kb];
+      v[b][1] = rows(n, 1)[kb];
+    }
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int i = i0 + b * kThreads;
+      if (i < total) {
+        SBs[2 * i] = v[b][0];
+        SBs[2 * i + 1] = v[b][1];
+      }
+    }
   }
 }
 
@@ -364,20 +415,32 @@ __device__ __forceinline__ void read_token_scales(const float* p, float (&sa)[TS
 // The MXFP8 token scales of the M tile -> LDS: E8M0 code of row 16*ts + l16,
 // 32-K block g of K step k at byte ((4k + g) * 16 + l16) * 4*TSW + ts, so the
 // lane (g, l16) of step k reads its TS codes as TSW consecutive dwords.
-// row_sf(r) gives the row's 4*KT codes (nullptr for a pad row: code 0).  Each
-// thread keeps one row and reads its codes a K step (4 codes) at a time.
+// row_sf(r) gives the row's 4*KT codes (nullptr for a pad row: code 0);
+// any_row is a valid row.  Each thread keeps one row and reads its codes a
+// K step (4 codes, one dword) at a time.
 template <int TM, typename RowSf>
-__device__ __forceinline__ void stage_token_scales_mx(uint8_t* SX, int KT, RowSf row_sf, int tid) {
+__device__ __forceinline__ void stage_token_scales_mx(uint8_t* SX, int KT, RowSf row_sf, const uint8_t* any_row,
+                                                      int tid) {
   constexpr int TSW = Cfg<TM>::TSW;
   constexpr int TPR = kThreads / TM;   // threads per row
   const int r = tid / TPR, part = tid % TPR;
   if (r >= TM) return;
   const uint8_t* rs = row_sf(r);
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(rs ? rs : any_row);
   uint8_t* dst = SX + (r & 15) * 4 * TSW + (r >> 4);
-  for (int k = part; k < KT; k += TPR) {
-    const uint32_t v = rs ? *reinterpret_cast<const uint32_t*>(rs + 4 * k) : 0u;
+  for (int k0 = part; k0 < KT; k0 += TPR * kStageBatch) {
+    uint32_t v[kStageBatch];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) dst[(4 * k + g) * 64 * TSW] = (uint8_t)(v >> (8 * g));
+    for (int b = 0; b < kStageBatch; ++b) v[b] = src[min(k0 + b * TPR, KT - 1)];
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int k = k0 + b * TPR;
+      if (k < KT) {
+        const uint32_t c = rs ? v[b] : 0u;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dst[(4 * k + g) * 64 * TSW] = (uint8_t)(c >> (8 * g));
+      }
+    }
   }
 }
 
@@ -421,12 +484,15 @@ struct Lds {
 // fetched at step j whatever N tile they belong to, so the pipeline does not
 // drain between the N tiles of a run.
 //
-// wband(n, w) gives the scalar byte offset of sub-tile w's 16-row band in N
-// tile n (band row * kdim) within the expert's weight block `wrsrc`; kdim is
-// the K extent in bytes (H for GEMM1, I for GEMM2).  MXFP8: `srsrc` covers
-// the expert's E8M0 weight scales, row-major [rows][kdim / 32]; lane l's
-// scale of a K step is one byte at row band + l % 16, block 4k + l / 16,
-// loaded with the step's weights into the same ring.
+// wband(n, w) gives the first row of sub-tile w's 16-row band in N tile n
+// within the expert's weight block `wrsrc`; kdim is the K extent in bytes (H
+// for GEMM1, I for GEMM2).  MXFP8: `srsrc` covers the expert's E8M0 weight
+// scales.  Row-major ([rows][kdim / 32]): lane l's scale of a K step is one
+// byte at row band + l % 16, block 4k + l / 16, loaded with the step's
+// weights into the same ring.  MFMA-tiled: the first step of each round (K
+// steps 4m..4m+3 of an N tile) loads the dword of scale group m for the next
+// round, which becomes the current one when the round ends; step s of a
+// round selects byte s (op_sel of the A operand).
 template <int TM, bool GATED, bool PACKED, bool MX, typename WBand, typename Epi>
 __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& tb,
                                             const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
@@ -454,28 +520,47 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   };
 
   v8i wr[D][2];        // weight ring: slot s holds step j with j % D == s
-  uint32_t wsc[D][2];  // MXFP8: the lane's weight scale code of each ring slot
+  uint32_t wsc[D][2];  // MXFP8, row-major scales: the lane's weight scale code of each ring slot
+  uint32_t wsg[2], wsg_next[2];   // MXFP8, MFMA-tiled scales: this round's and the next round's dwords
+  constexpr bool MXT = MX && PACKED;
 
   const int wvoff = weight_lane_offset<PACKED>(lane, kdim);
-  const int svoff = r0 * (kdim >> 5) + g;       // MXFP8: the lane's scale byte within a band's K step
+  // MXFP8: the lane's scale byte within a band's K step (row-major), or its
+  // dword within a band's scale group (MFMA-tiled)
+  const int svoff = MXT ? 4 * lane : r0 * (kdim >> 5) + g;
+  const int sgroup = mx_scale_groups(kdim / kKB) * 256;   // bytes per band of MFMA-tiled scales
   constexpr int kKStep = PACKED ? 2048 : kKB;   // bytes between K steps within a band
   int nw = 0, kw = 0;
-  int wb[2] = {wband(0, 0), wband(0, 1)};
+  int wb[2], sb[2];
+  auto set_bands = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int row = wband(n, w);
+      wb[w] = row * kdim;
+      sb[w] = MXT ? (row >> 4) * sgroup : row * (kdim >> 5);
+    }
+  };
+  set_bands(0);
   auto load_w = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wrsrc, wvoff, wb[w] + kw * kKStep);
-    if constexpr (MX) {
-      // band row * kdim / 32 = the band's first scale byte; 4 blocks per K step
+    if constexpr (MXT) {
+      if (s == 0) {   // kw is the first step of a scale group here
 #pragma unroll
-      for (int w = 0; w < 2; ++w) wsc[s][w] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, svoff, (wb[w] >> 5) + 4 * kw, 0);
+        for (int w = 0; w < 2; ++w)
+          wsg_next[w] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, svoff, sb[w] + (kw / kMxScaleGroup) * 256, 0);
+      }
+    } else if constexpr (MX) {
+      // 4 blocks of 32 per K step
+#pragma unroll
+      for (int w = 0; w < 2; ++w) wsc[s][w] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, svoff, sb[w] + 4 * kw, 0);
     }
     if (kw + 1 < KT) {
       ++kw;
     } else if (nw + 1 < nn) {
       kw = 0;
       ++nw;
-      wb[0] = wband(nw, 0);
-      wb[1] = wband(nw, 1);
+      set_bands(nw);
     }
   };
   // token rows of K step ka -> buffer bi, straight from global memory into
@@ -497,12 +582,21 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   // The direct-to-LDS loads a wave issued one step back (for the step after
   // next) must have landed before the barrier that hands their buffer to the
   // other waves.  Vector memory operations complete in issue order for the
-  // counter, and younger than those loads are that step's WL weight loads
-  // and this step's APW + WL loads (WL = 4 weight fragment loads, plus the 2
-  // scale bytes for MXFP8), so the wait is vmcnt(2 WL + APW).  Every step
-  // issues all of them (the producers never skip), so the count holds.
-  constexpr int WL = MX ? 6 : 4;
-  auto publish_wait = [&]() __attribute__((always_inline)) { vmcnt_wait<2 * WL + APW>(); };
+  // counter, and younger than those loads are that step's weight loads and
+  // this step's APW + weight loads: step s issues WL(s) = 4 weight fragment
+  // loads, plus 2 scale bytes (MXFP8, row-major scales) or, at s == 0, 2 scale
+  // dwords (MXFP8, MFMA-tiled scales), so the wait at step s is
+  // vmcnt(WL(s-1) + APW + WL(s)).  Every step issues all of them (the
+  // producers never skip), so the count holds.
+  auto wl = [](int st) constexpr -> int { return 4 + (MXT ? (st == 0 ? 2 : 0) : (MX ? 2 : 0)); };
+  auto publish_wait = [&](int s) __attribute__((always_inline)) {
+    switch (s) {   // s is a constant of the unrolled round
+      case 0: vmcnt_wait<wl(3) + APW + wl(0)>(); break;
+      case 1: vmcnt_wait<wl(0) + APW + wl(1)>(); break;
+      case 2: vmcnt_wait<wl(1) + APW + wl(2)>(); break;
+      default: vmcnt_wait<wl(2) + APW + wl(3)>(); break;
+    }
+  };
 
   // carried across the step boundary: the first two fragments and the scales of the next step
   v8i af[3];
@@ -539,11 +633,13 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     dma_a((s + 3) & 3);        // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
     __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
     if constexpr (MX) {
+      const uint32_t ws0 = MXT ? wsg[0] : wsc[s][0], ws1 = MXT ? wsg[1] : wsc[s][1];
+      const int sela = MXT ? s : 0;
 #pragma unroll
       for (int ts = 0; ts < TS; ++ts) {
         if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
-        acc[ts][0] = mfma16x16x128_mx_sel(ts & 3, wr[s][0], af[ts % 3], acc[ts][0], wsc[s][0], sx[ts >> 2]);
-        acc[ts][1] = mfma16x16x128_mx_sel(ts & 3, wr[s][1], af[ts % 3], acc[ts][1], wsc[s][1], sx[ts >> 2]);
+        acc[ts][0] = mfma16x16x128_mx_sel(sela, ts & 3, wr[s][0], af[ts % 3], acc[ts][0], ws0, sx[ts >> 2]);
+        acc[ts][1] = mfma16x16x128_mx_sel(sela, ts & 3, wr[s][1], af[ts % 3], acc[ts][1], ws1, sx[ts >> 2]);
       }
     } else {
       v4f pr[2][2];
@@ -567,8 +663,15 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     }
     load_w(s);
     prefetch((s + 1) & 3, nx, kx);
-    publish_wait();
+    publish_wait(s);
     step_barrier();
+  };
+  // MXFP8, MFMA-tiled scales: the next round's scale dwords become current
+  auto next_round = [&]() __attribute__((always_inline)) {
+    if constexpr (MXT) {
+      wsg[0] = wsg_next[0];
+      wsg[1] = wsg_next[1];
+    }
   };
   auto finish_tile = [&](int n) __attribute__((always_inline)) {
     epi(n, acc);
@@ -578,14 +681,15 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
 
   // prologue: rows of steps 0..2 into buffers 0..2, weights of steps 0..3;
   // rows of steps 0 and 1 must have landed before the first barrier (younger
-  // than them: step 2's rows and the D * WL weight loads)
+  // than them: step 2's rows and the weight loads of the 4 steps)
   dma_a(0);
   dma_a(1);
   dma_a(2);
 #pragma unroll
   for (int s = 0; s < D; ++s) load_w(s);
-  vmcnt_wait<APW + WL * D>();
+  vmcnt_wait<APW + wl(0) + wl(1) + wl(2) + wl(3)>();
   __syncthreads();
+  next_round();
   prefetch(0, 0, 0);
 
   // Rounds of D steps.  A run of several N tiles needs KT % D == 0 (the host
@@ -601,6 +705,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
       const bool end = k + 1 == KT;
       step(s, end ? n + 1 : n, end ? 0 : k + 1);
     }
+    next_round();
     j += D;
     kb += D;
     if (kb == KT) {
@@ -663,16 +768,17 @@ __device__ __forceinline__ void gemm1_tile(
       __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, 2 * I * H, kWeightRsrcFlags);
   auto wband = [&](int n, int w) -> int {
     const int c = 128 * (nt0 + n) + 16 * wave;   // first row of the 16-row band
-    return (w ? I + c : c) * H;
+    return w ? I + c : c;
   };
   __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
   if constexpr (MX) {
-    const uint8_t* sexp = w13_scale + (size_t)tc.e * (2 * (size_t)I) * (H / 32);
-    srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, 2 * I * (H / 32), kWeightRsrcFlags);
+    const int sbytes = mx_weight_scale_bytes<PACKED>(2 * I, H);
+    const uint8_t* sexp = w13_scale + (size_t)tc.e * sbytes;
+    srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, sbytes, kWeightRsrcFlags);
     stage_token_scales_mx<TM>(smem, KT, [&](int r) -> const uint8_t* {
       const int src = r < h ? sorted_src[tc.p0 + r] : -1;
       return src >= 0 ? x_scale + (size_t)(src / K) * (H / 32) : nullptr;
-    }, tid);
+    }, x_scale, tid);
   } else {
     const float* sexp = w13_scale + (size_t)tc.e * (2 * IB) * HB;
     stage_weight_scales(Lds<TM, MX>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
@@ -681,7 +787,7 @@ __device__ __forceinline__ void gemm1_tile(
     stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
       const int src = r < h ? sorted_src[tc.p0 + r] : -1;
       return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
-    }, tid);
+    }, x_scale, tid);
   }
 
   // epilogue of N tile n: act = silu(gate) * up; per token row amax over a
@@ -817,16 +923,17 @@ __device__ __forceinline__ void gemm2_tile(
                                                                          kWeightRsrcFlags);
   auto wband = [&](int n, int w) -> int {
     // bands past H (the last N tile when H % 256 == 128) read the last band
-    return min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16) * I;
+    return min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16);
   };
   __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
   if constexpr (MX) {
-    const uint8_t* sexp = w2_scale + (size_t)tc.e * H * (size_t)(I / 32);
-    srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, H * (I / 32), kWeightRsrcFlags);
+    const int sbytes = mx_weight_scale_bytes<PACKED>(H, I);
+    const uint8_t* sexp = w2_scale + (size_t)tc.e * sbytes;
+    srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, sbytes, kWeightRsrcFlags);
     stage_token_scales_mx<TM>(smem, KT, [&](int r) -> const uint8_t* {
       const int p = tc.p0 + r;
       return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * (I / 32) : nullptr;
-    }, tid);
+    }, q_scale + (size_t)tc.p0 * (I / 32), tid);
   } else {
     // N tile n spans scale blocks 2(nt0+n) and 2(nt0+n)+1 (the second clamped
     // at the last block; only columns < H are stored); waves 4..7 use the second
@@ -838,7 +945,7 @@ __device__ __forceinline__ void gemm2_tile(
     stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
       const int p = tc.p0 + r;
       return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
-    }, tid);
+    }, q_scale + (size_t)tc.p0 * IB, tid);
   }
   // source row and top-k weight of each tile row, for the epilogues
   for (int r = tid; r < TM; r += kThreads) {

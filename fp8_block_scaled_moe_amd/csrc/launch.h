@@ -61,6 +61,9 @@ hipError_t launch_gemm2_mx(const uint8_t* q, const uint8_t* q_sf, const uint8_t*
 
 // Row-major e4m3 [E][N][K] -> MFMA-tiled layout (N % 16 == 0, K % 128 == 0).
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);
+// Row-major E8M0 [E][N][K/32] -> MFMA-tiled MXFP8 scale layout of mx_scales_packed_bytes bytes.
+int64_t mx_scales_packed_bytes(int64_t E, int N, int K);
+hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* Y, const int32_t* topk_ids, int T, int H, int E, int K,
                           uint16_t* out, hipStream_t stream);

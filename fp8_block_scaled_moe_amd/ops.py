@@ -187,6 +187,33 @@ def alloc_workspace_mx(T, H, I, E, K, device):
     return torch.empty(fused_mx_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
 
 
+def pack_mx_scales(sf, out=None):
+    """MXFP8 weight scales, E8M0 codes [E, N, K/32] row-major -> the MFMA-tiled scale layout
+    (a flat uint8 tensor of moe_pack_mx_scales_bytes bytes; see moe_pack_mx_scales in
+    include/fp8moe.h).  Use with weights packed by pack_weights."""
+    sf = _u8(sf)
+    _need(sf, torch.uint8, "sf", 3)
+    E, N, KB = sf.shape
+    K = KB * 32
+    n = lib().moe_pack_mx_scales_bytes(E, N, K)
+    if n < 0:
+        check(int(n))
+    if out is None:
+        out = torch.empty(int(n), dtype=torch.uint8, device=sf.device)
+    _need(out, torch.uint8, "out")
+    if out.numel() != n:
+        raise ValueError(f"out must hold {n} bytes")
+    check(lib().moe_pack_mx_scales(_p(sf), E, N, K, _p(out), _stream(sf.device)))
+    return out
+
+
+def _mx_weight_scales_ok(sf, E, N, K, layout):
+    """Row-major scales are [E, N, K/32]; MFMA-tiled ones the flat output of pack_mx_scales."""
+    if layout == WEIGHTS_MFMA_TILED:
+        return sf.numel() == lib().moe_pack_mx_scales_bytes(E, N, K)
+    return tuple(sf.shape) == (E, N, K // 32)
+
+
 def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
                     out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
     """MXFP8 MoE layer (1x32 E8M0 scales on every operand; E8M0 codes as uint8).
@@ -196,9 +223,9 @@ def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
     _need(x, torch.uint8, "x", 2)
     _need(x_sf, torch.uint8, "x_sf", 2)
     _need(w13, torch.uint8, "w13", 3)
-    _need(w13_sf, torch.uint8, "w13_sf", 3)
+    _need(w13_sf, torch.uint8, "w13_sf")
     _need(w2, torch.uint8, "w2", 3)
-    _need(w2_sf, torch.uint8, "w2_sf", 3)
+    _need(w2_sf, torch.uint8, "w2_sf")
     _need(topk_ids, torch.int32, "topk_ids", 2)
     _need(topk_weights, torch.float32, "topk_weights", 2)
     T, H = x.shape
@@ -207,9 +234,9 @@ def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
     K = topk_ids.shape[1]
     if H2 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
         raise ValueError("inconsistent x / w13 / w2 shapes")
-    if tuple(x_sf.shape) != (T, H // 32) or tuple(w13_sf.shape) != (E, 2 * I, H // 32) \
-            or tuple(w2_sf.shape) != (E, H, I // 32):
-        raise ValueError("inconsistent E8M0 scale shapes")
+    if tuple(x_sf.shape) != (T, H // 32) or not _mx_weight_scales_ok(w13_sf, E, 2 * I, H, weight_layout) \
+            or not _mx_weight_scales_ok(w2_sf, E, H, I, weight_layout):
+        raise ValueError("inconsistent E8M0 scale shapes (MFMA-tiled weights need pack_mx_scales scales)")
     if tuple(topk_ids.shape) != (T, K) or tuple(topk_weights.shape) != (T, K):
         raise ValueError("topk_ids / topk_weights must be [T, K]")
     dev = x.device
@@ -233,11 +260,11 @@ def gemm1_swiglu_quant_mx(x, x_sf, w13, w13_sf, route, T, K, align, tile_m=-1,
     _need(x, torch.uint8, "x", 2)
     _need(x_sf, torch.uint8, "x_sf", 2)
     _need(w13, torch.uint8, "w13", 3)
-    _need(w13_sf, torch.uint8, "w13_sf", 3)
+    _need(w13_sf, torch.uint8, "w13_sf")
     E, I2, H = w13.shape
     I = I2 // 2
-    if tuple(x_sf.shape) != (x.shape[0], H // 32) or tuple(w13_sf.shape) != (E, I2, H // 32):
-        raise ValueError("inconsistent E8M0 scale shapes")
+    if tuple(x_sf.shape) != (x.shape[0], H // 32) or not _mx_weight_scales_ok(w13_sf, E, I2, H, weight_layout):
+        raise ValueError("inconsistent E8M0 scale shapes (MFMA-tiled weights need pack_mx_scales scales)")
     cap = route["sorted_src"].numel()
     dev = x.device
     q = torch.zeros((cap, I), dtype=torch.uint8, device=dev) if q is None else q
@@ -260,10 +287,11 @@ def gemm2_weighted_mx(q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile
     _need(q, torch.uint8, "q", 2)
     _need(q_sf, torch.uint8, "q_sf", 2)
     _need(w2, torch.uint8, "w2", 3)
-    _need(w2_sf, torch.uint8, "w2_sf", 3)
+    _need(w2_sf, torch.uint8, "w2_sf")
     E, H, I = w2.shape
     cap = route["sorted_src"].numel()
-    if tuple(q.shape) != (cap, I) or tuple(q_sf.shape) != (cap, I // 32) or tuple(w2_sf.shape) != (E, H, I // 32):
+    if tuple(q.shape) != (cap, I) or tuple(q_sf.shape) != (cap, I // 32) \
+            or not _mx_weight_scales_ok(w2_sf, E, H, I, weight_layout):
         raise ValueError("inconsistent q / q_sf / w2_sf shapes")
     dev = q.device
     Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev) if Y is None else Y

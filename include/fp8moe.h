@@ -200,10 +200,12 @@ int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, in
  * and 32 columns of I, e = the smallest exponent with amax <= 448 * 2^e
  * (clamped to [-127, 127], -127 for an all-zero block), q = e4m3(act * 2^-e),
  *   q_sf    uint8 [cap, I/32]      E8M0 codes e + 127.
- * Weights, tokens, routing, tiles, layouts, limits, errors, ownership and
- * determinism are those of the FP8 entry points above; moe_pack_weights
- * packs the e4m3 weights for FP8MOE_WEIGHTS_MFMA_TILED and the scale codes
- * keep their row-major layout.  The workspace of moe_fused_mxfp8 is sized by
+ * Weights, tokens, routing, tiles, limits, errors, ownership and
+ * determinism are those of the FP8 entry points above.  With
+ * FP8MOE_WEIGHTS_MFMA_TILED both the e4m3 weights (moe_pack_weights) and
+ * their E8M0 scale codes (moe_pack_mx_scales) are packed; with
+ * FP8MOE_WEIGHTS_ROW_MAJOR both are row-major as above.  Results are
+ * bit-identical.  The workspace of moe_fused_mxfp8 is sized by
  * moe_fused_mxfp8_workspace_size.
  */
 int moe_fused_mxfp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
@@ -242,6 +244,22 @@ int moe_gemm2_weighted_mx(const void* q, const uint8_t* q_sf,
  * of E*N*K bytes.  Asynchronous on `stream`.
  */
 int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out, void* stream);
+
+/* moe_pack_mx_scales: MXFP8 weight scales, E8M0 codes [E, N, K/32] row-major
+ * (w13_sf with N = 2I, K = H, or w2_sf with N = H, K = I) -> the
+ * FP8MOE_WEIGHTS_MFMA_TILED scale layout of the MXFP8 entry points, read with
+ * one contiguous dword load per wave, 16-row band and four 128-wide K steps:
+ *   out[e][b][m][l][j] = in[e][16b + l%16][4(4m + j) + l/16]
+ * for band b, group m of K steps 4m..4m+3, lane l in [0, 64), byte j in
+ * [0, 4); bytes of K steps past K/128 hold 127.  out is caller-owned device
+ * memory of moe_pack_mx_scales_bytes(E, N, K) = E * (N/16) * ceil(K/512) * 256
+ * bytes (E*N*K/32 when K % 512 == 0).  Requires E >= 1, N % 16 == 0,
+ * K % 128 == 0 (FP8MOE_ERR_SHAPE otherwise; moe_pack_mx_scales_bytes then
+ * returns that negative status), in and out non-NULL and not overlapping.
+ * Asynchronous on `stream`.
+ */
+int64_t moe_pack_mx_scales_bytes(int64_t E, int32_t N, int32_t K);
+int moe_pack_mx_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream);
 
 /* ---------------------------------------------------------------- gated activation + MXFP8
  * SwiGLU + MXFP8 quantisation (PR 8023 page, title and section 1):

@@ -130,6 +130,18 @@ def test_stage_validation(mx):
     assert L.moe_combine(NULL, NULL, 0, 128, 4, 2, NULL, NULL) == OK
 
 
+def test_pack_mx_scales_validation():
+    L = lib()
+    assert L.moe_pack_mx_scales_bytes(256, 4096, 7168) == 256 * 4096 * 7168 // 32
+    assert L.moe_pack_mx_scales_bytes(2, 32, 384) == 2 * 2 * 1 * 256          # 3 K steps -> one group of 4
+    assert L.moe_pack_mx_scales_bytes(2, 32, 640) == 2 * 2 * 2 * 256
+    assert L.moe_pack_mx_scales_bytes(2, 24, 384) == E_SHAPE
+    assert L.moe_pack_mx_scales_bytes(2, 32, 200) == E_SHAPE
+    assert L.moe_pack_mx_scales(FAKE, 0, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE
+    assert L.moe_pack_mx_scales(NULL, 1, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_NULL
+    assert L.moe_pack_mx_scales(FAKE, 1, 32, 128, FAKE, NULL) == E_SHAPE       # overlapping in / out
+
+
 def test_pack_weights_validation():
     f = lib().moe_pack_weights
     assert f(FAKE, 0, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE

@@ -27,10 +27,18 @@ pytestmark = pytest.mark.gpu
 TILES = (16, 32, 64, 128, 144, 160)
 
 
-def run_mx(p, tile_m=-1, layout=fm.WEIGHTS_ROW_MAJOR, w13=None, w2=None):
-    return fm.moe_fused_mxfp8(p.x_q, p.x_s, p.w13_q if w13 is None else w13, p.w13_s,
-                              p.w2_q if w2 is None else w2, p.w2_s, p.topk_ids, p.topk_weights,
-                              tile_m=tile_m, weight_layout=layout)
+def run_mx(p, tile_m=-1, packed=None):
+    """The MXFP8 layer; packed = (w13, w13_sf, w2, w2_sf) in the MFMA-tiled layouts, else row-major."""
+    if packed is None:
+        return fm.moe_fused_mxfp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids, p.topk_weights,
+                                  tile_m=tile_m)
+    w13, w13_sf, w2, w2_sf = packed
+    return fm.moe_fused_mxfp8(p.x_q, p.x_s, w13, w13_sf, w2, w2_sf, p.topk_ids, p.topk_weights, tile_m=tile_m,
+                              weight_layout=fm.WEIGHTS_MFMA_TILED)
+
+
+def pack_all(p):
+    return (fm.pack_weights(p.w13_q), fm.pack_mx_scales(p.w13_s), fm.pack_weights(p.w2_q), fm.pack_mx_scales(p.w2_s))
 
 
 def oracle_mx(ph, tokens=None, stages=False):
@@ -50,12 +58,12 @@ def tiny_mx():
 def test_tiny_all_tiles_and_layouts_match_oracle(tiny_mx):
     ph, pd = tiny_mx
     ref = oracle_mx(ph)
-    p13, p2 = fm.pack_weights(pd.w13_q), fm.pack_weights(pd.w2_q)
+    packed = pack_all(pd)
     outs = []
-    for layout, w13, w2 in ((fm.WEIGHTS_ROW_MAJOR, None, None), (fm.WEIGHTS_MFMA_TILED, p13, p2)):
+    for layout, pk in ((fm.WEIGHTS_ROW_MAJOR, None), (fm.WEIGHTS_MFMA_TILED, packed)):
         for tm in (-1,) + TILES:
             say("tiny mx layout", layout, "tile_m", tm)
-            out = run_mx(pd, tm, layout, w13, w2)
+            out = run_mx(pd, tm, pk)
             torch.cuda.synchronize()
             assert_close_to_oracle(out, ref, f"tiny mx layout={layout} tile_m={tm}")
             outs.append(out)
@@ -122,13 +130,16 @@ def test_tiny_stages_match_oracle(tiny_mx):
     assert torch.equal(outs[0], run_mx(pd)), "fused MX layer differs from its stages"
 
 
+@pytest.mark.parametrize("layout", [fm.WEIGHTS_ROW_MAJOR, fm.WEIGHTS_MFMA_TILED])
 @pytest.mark.parametrize("tile_m", TILES)
-def test_gemm2_mx_integer_inputs_bit_exact(tile_m):
+def test_gemm2_mx_integer_inputs_bit_exact(tile_m, layout):
     """Integer e4m3 values (|v| <= 4) with E8M0 scales 2^-2..2^2 per 32-K block on both
     operands: every product is a multiple of 2^-4 below 2^8 and every partial sum
     (at most 384 terms) stays below 2^17, so fp32 accumulation is exact and Y must
     equal the float64 brute force rounded once to bf16.  I = 384 gives three K
-    steps (a partial round of the operand ring) and H = 384 a half-empty last N tile."""
+    steps (a partial round of the operand ring) and H = 384 a half-empty last N tile.
+    With the MFMA-tiled layout the weight scales come from packed dwords, one
+    byte per K step selected by the MFMA's op_sel."""
     rng = np.random.default_rng(43)
     T, H, I, E, K = 40, 384, 384, 3, 2
     ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
@@ -143,9 +154,12 @@ def test_gemm2_mx_integer_inputs_bit_exact(tile_m):
     wsf = (127 + rng.integers(-2, 3, size=(E, H, I // 32))).astype(np.uint8)
     wts = np.ones((T, K), np.float32)
     route_d = {k: torch.from_numpy(v).cuda() for k, v in r.items()}
-    say("gemm2 mx integer exact tile_m", tile_m)
-    Y = fm.gemm2_weighted_mx(q.cuda(), torch.from_numpy(qsf).cuda(), w2.cuda(), torch.from_numpy(wsf).cuda(),
-                             route_d, torch.from_numpy(wts).cuda(), T, K, align, tile_m=tile_m)
+    say("gemm2 mx integer exact tile_m", tile_m, "layout", layout)
+    w2d, wsfd = w2.cuda(), torch.from_numpy(wsf).cuda()
+    if layout == fm.WEIGHTS_MFMA_TILED:
+        w2d, wsfd = fm.pack_weights(w2d), fm.pack_mx_scales(wsfd)
+    Y = fm.gemm2_weighted_mx(q.cuda(), torch.from_numpy(qsf).cuda(), w2d, wsfd, route_d,
+                             torch.from_numpy(wts).cuda(), T, K, align, tile_m=tile_m, weight_layout=layout)
     torch.cuda.synchronize()
     Yh = Y.float().cpu().numpy()
     for e in range(E):
@@ -156,6 +170,24 @@ def test_gemm2_mx_integer_inputs_bit_exact(tile_m):
             exact = wd @ a
             ref = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
             assert np.array_equal(Yh[src], ref), (e, p)
+
+
+@pytest.mark.parametrize("E,N,K", [(2, 32, 384), (1, 16, 128), (3, 48, 7168), (2, 64, 640)])
+def test_pack_mx_scales_layout(E, N, K):
+    """The packed scale layout, element by element: out[e][b][m][l][j] is the code of row
+    16b + l%16, 32-K block 4(4m + j) + l/16, and 127 past the last K step."""
+    rng = np.random.default_rng(E * 1000 + K)
+    sf = rng.integers(0, 255, size=(E, N, K // 32)).astype(np.uint8)
+    say("pack mx scales", E, N, K)
+    got = fm.pack_mx_scales(torch.from_numpy(sf).cuda()).cpu().numpy()
+    KT, G = K // 128, -(-(K // 128) // 4)
+    assert got.size == E * (N // 16) * G * 256
+    got = got.reshape(E, N // 16, G, 64, 4)
+    e, b, m, l, j = np.meshgrid(np.arange(E), np.arange(N // 16), np.arange(G), np.arange(64), np.arange(4),
+                                indexing="ij")
+    k = 4 * m + j
+    ref = np.where(k < KT, sf[e, 16 * b + l % 16, np.minimum(4 * k + l // 16, K // 32 - 1)], 127)
+    assert np.array_equal(got, ref)
 
 
 def test_mx_edge_cases(tiny_mx):
@@ -250,9 +282,9 @@ def test_large_mx_sampled(name, T, cfg, ntok, large_weights_mx):
     assert_close_to_oracle(out[tokens], ref, f"{name} mx sampled tokens {tokens}")
     say(name, "mx determinism and packed weights")
     assert torch.equal(out, run_mx(pd))
-    p13, p2 = fm.pack_weights(pd.w13_q), fm.pack_weights(pd.w2_q)
-    assert torch.equal(out, run_mx(pd, layout=fm.WEIGHTS_MFMA_TILED, w13=p13, w2=p2))
-    del p13, p2
+    packed = pack_all(pd)
+    assert torch.equal(out, run_mx(pd, packed=packed))
+    del packed
     if name == "decode":
         for tm in TILES:
             say("decode mx tile_m", tm)
