@@ -10,5 +10,5 @@ from .ops import (  # noqa: F401
     route_capacity, route_permute, fused_workspace_size, alloc_workspace, moe_fused_fp8,
     gemm1_swiglu_quant, gemm2_weighted, combine, gated_act_fp8_quant, select_tile,
     select_tile_classes, pack_weights, WEIGHTS_ROW_MAJOR, WEIGHTS_MFMA_TILED,
-    fused_mx_workspace_size, alloc_workspace_mx, moe_fused_mxfp8, pack_mx_scales, gemm1_swiglu_quant_mx, gemm2_weighted_mx,
+    fused_mx_workspace_size, alloc_workspace_mx, moe_fused_mxfp8, pack_mx_scales, grouped_gemm_fp8, gemm1_swiglu_quant_mx, gemm2_weighted_mx,
 )

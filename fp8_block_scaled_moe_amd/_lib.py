@@ -34,6 +34,8 @@ SIGNATURES = {
                                              _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
     "moe_pack_weights": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_pack_mx_scales_bytes": (_i64, [_i64, _i32, _i32]),
+    "moe_grouped_gemm_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
+                                            _i32, _vp]),
     "moe_pack_mx_scales": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "gated_act_fp8_quant": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _vp]),

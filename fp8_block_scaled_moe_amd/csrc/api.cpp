@@ -362,6 +362,33 @@ int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out,
   return ok();
 }
 
+int moe_grouped_gemm_fp8(const void* a, const float* a_scale, const void* b, const float* b_scale,
+                         const int32_t* padded_indptr, const int32_t* sorted_src, int64_t rows, int32_t n, int32_t k,
+                         int32_t E, int32_t is_gated, float* out, int32_t tile_m, int32_t weight_layout,
+                         void* stream) {
+  if (rows < 0 || rows >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid rows %lld", (long long)rows);
+  if (n <= 0 || k <= 0) return fail(FP8MOE_ERR_SHAPE, "n and k must be positive (got %d, %d)", n, k);
+  if (k % 128 || n % 128 || (is_gated && (n / 2) % 128))
+    return fail(FP8MOE_ERR_ALIGN, "k and n (n/2 when gated) must be multiples of 128 (n=%d k=%d)", n, k);
+  if (n > (is_gated ? 2 : 1) * FP8MOE_MAX_DIM || k > FP8MOE_MAX_DIM)
+    return fail(FP8MOE_ERR_LIMIT, "n=%d or k=%d beyond the library limits", n, k);
+  if (E < 1) return fail(FP8MOE_ERR_SHAPE, "E must be >= 1 (got %d)", E);
+  if (E > FP8MOE_MAX_EXPERTS) return fail(FP8MOE_ERR_LIMIT, "E=%d exceeds %d", E, FP8MOE_MAX_EXPERTS);
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
+  if (tile_m != -1 && tile_m != 16 && tile_m != 32 && tile_m != 64 && tile_m != 128)
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128}", tile_m);
+  if (rows == 0) return ok();
+  if (!a || !a_scale || !b || !b_scale || !padded_indptr || !sorted_src || !out)
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  const int tm = tile_m == -1 ? 128 : tile_m;
+  GroupedRows g{padded_indptr, sorted_src, rows, E, 1, rows, device_num_cu()};
+  hipError_t err = launch_grouped_gemm_plain(static_cast<const uint8_t*>(a), a_scale, static_cast<const uint8_t*>(b),
+                                             b_scale, g, n, k, is_gated != 0, out, tm,
+                                             weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "grouped_gemm launch");
+  return ok();
+}
+
 int64_t moe_pack_mx_scales_bytes(int64_t E, int32_t N, int32_t K) {
   if (E < 1 || N <= 0 || K <= 0 || N % 16 || K % 128)
     return fail(FP8MOE_ERR_SHAPE, "MX scale pack needs E >= 1, N %% 16 == 0, K %% 128 == 0 (E=%lld N=%d K=%d)",

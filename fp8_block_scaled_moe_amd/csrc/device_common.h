@@ -70,11 +70,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 // silu(g) * u = g * u / (1 + exp(-g)) on the transcendental units:
 // exp(-g) = 2^(-g log2 e) with v_exp_f32 and the reciprocal with v_rcp_f32
-// (1 ulp each).  For |g| <= 88 the result is within (2|g| + 8) * 2^-24
+// (1 ulp each).  For |g| <= 87 the result is within (2|g| + 8) * 2^-24
 // relative of the correctly rounded value (the fp32 product g log2 e carries
 // |g| 2^-23 into the exponent); for g > 88 the exponential underflows and the
-// result is g * u to three roundings; for g < -88 it overflows and the result
-// is a signed zero.
+// result is g * u to three roundings; below g = -87.3, where 1 + exp(-g)
+// exceeds 2^126, the reciprocal's subnormal result is flushed and the result
+// is a signed zero (measured on gfx950: exact to -87.0, zero from -87.5).
 __device__ __forceinline__ float silu_mul(float g, float u) {
   const float ex = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);  // exp(-g)
   return g * __builtin_amdgcn_rcpf(1.0f + ex) * u;

@@ -15,7 +15,8 @@
 // activation is within (2|g| + 8) * 2^-24 relative of the correctly rounded
 // value (the fp32 product g log2 e carries |g| 2^-23 into the exponent); for
 // g > 88 the exponential underflows and the product is exact to 3 roundings,
-// for g < -88 it overflows and the activation is flushed to zero.  When the
+// below g = -87.3 the reciprocal's subnormal result is flushed and the
+// activation is a signed zero.  When the
 // block amax lies within 2^-15 (on the frexp mantissa) of a boundary
 // 448 * 2^e, or below 2^-60 (where the flushed values could matter), the
 // block is re-evaluated in fp64 and rounded once to fp32, so the decision is

@@ -732,12 +732,16 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
 // expert's segment and are treated as padding (read token 0, never stored).
 // FP8: one 1x128 block per row and N tile, fp32 scale amax / 448.  MXFP8:
 // four 1x32 blocks per row and N tile, E8M0 codes.
-template <int TM, bool PACKED, bool MX>
+// PLAIN (the plain grouped GEMM of the SM120 page's op, gated form): x rows
+// are already in the padded row space (row p0 + r, no gather) and the
+// epilogue writes act in fp32 to plain_out [rows][I] for rows whose
+// sorted_src is valid, with no requantisation.
+template <int TM, bool PACKED, bool MX, bool PLAIN = false>
 __device__ __forceinline__ void gemm1_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ x,
     const scale_t<MX>* __restrict__ x_scale, const uint8_t* __restrict__ w13,
     const scale_t<MX>* __restrict__ w13_scale, const int32_t* __restrict__ sorted_src, int K, int H, int I,
-    int NB, uint8_t* __restrict__ q, scale_t<MX>* __restrict__ q_scale) {
+    int NB, uint8_t* __restrict__ q, scale_t<MX>* __restrict__ q_scale, float* __restrict__ plain_out = nullptr) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS;
   const int NT = I / 128;
@@ -757,9 +761,13 @@ __device__ __forceinline__ void gemm1_tile(
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
     const int qc = C::block_of(tid >> 6, i) * 64 + lane;
     const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
-    const int src = r < h ? sorted_src[tc.p0 + r] : -1;
-    const size_t tok = src >= 0 ? (size_t)(src / K) : 0;  // a pad row reads token 0; never stored
-    a_src[i] = x + tok * H + c * 16;
+    if constexpr (PLAIN) {
+      a_src[i] = x + (size_t)(tc.p0 + min(r, h - 1)) * H + c * 16;   // rows past the segment re-read its last
+    } else {
+      const int src = r < h ? sorted_src[tc.p0 + r] : -1;
+      const size_t tok = src >= 0 ? (size_t)(src / K) : 0;  // a pad row reads token 0; never stored
+      a_src[i] = x + tok * H + c * 16;
+    }
   }
   // wave w owns I columns [n0 + 16w, n0 + 16w + 16) of N tile n (n0 = 128 (nt0 + n)):
   // its two operands are those columns' gate rows and up rows
@@ -786,6 +794,7 @@ __device__ __forceinline__ void gemm1_tile(
     }, tid);
     stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
       const int src = r < h ? sorted_src[tc.p0 + r] : -1;
+      if constexpr (PLAIN) return src >= 0 ? x_scale + (size_t)(tc.p0 + r) * HB : nullptr;
       return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
     }, x_scale, tid);
   }
@@ -795,6 +804,19 @@ __device__ __forceinline__ void gemm1_tile(
   // pair 2p, 2p+1 (32 columns), through LDS
   auto epi = [&](int n, v4f (&acc)[TS][2]) __attribute__((always_inline)) {
     const int n0 = 128 * (nt0 + n), c0 = n0 + 16 * wave;
+    if constexpr (PLAIN) {
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) {
+        const int row = 16 * ts + l16;
+        if (row < h && sorted_src[tc.p0 + row] >= 0) {
+          v4f a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[r] = silu_mul(acc[ts][0][r], acc[ts][1][r]);
+          *reinterpret_cast<v4f*>(plain_out + (size_t)(tc.p0 + row) * I + c0 + 4 * g) = a;
+        }
+      }
+      return;
+    }
     float act[TS][4];
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
@@ -889,12 +911,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
 // GEMM2 with the top-k weight epilogue, over a run of N tiles of 256 H
 // columns, for a tile body of TM rows; rows tc.h.. of the body are past the
 // expert's segment (they re-read the tile's last row and are never stored).
-template <int TM, bool PACKED, bool MX>
+// PLAIN (the plain grouped GEMM of the SM120 page's op): the epilogue
+// writes the fp32 accumulators to plain_out [rows][H] at the padded row
+// (rows whose sorted_src is valid), without the top-k weight.
+template <int TM, bool PACKED, bool MX, bool PLAIN = false>
 __device__ __forceinline__ void gemm2_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ q,
     const scale_t<MX>* __restrict__ q_scale, const uint8_t* __restrict__ w2,
     const scale_t<MX>* __restrict__ w2_scale, const float* __restrict__ topk_weights,
-    const int32_t* __restrict__ sorted_src, int H, int I, int NB, uint16_t* __restrict__ Y) {
+    const int32_t* __restrict__ sorted_src, int H, int I, int NB, uint16_t* __restrict__ Y,
+    float* __restrict__ plain_out = nullptr) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS;
   const int NT = (H + kTN - 1) / kTN;
@@ -951,11 +977,24 @@ __device__ __forceinline__ void gemm2_tile(
   for (int r = tid; r < TM; r += kThreads) {
     const int src = r < h ? sorted_src[tc.p0 + r] : -1;
     srow[r] = src;
-    wrow_w[r] = src >= 0 ? topk_weights[src] : 0.f;
+    if constexpr (!PLAIN) wrow_w[r] = src >= 0 ? topk_weights[src] : 0.f;
   }
 
   auto epi = [&](int n, v4f (&acc)[TS][2]) __attribute__((always_inline)) {
     const int c0 = kTN * (nt0 + n) + 32 * wave;
+    if constexpr (PLAIN) {
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) {
+        if (srow[16 * ts + l16] < 0) continue;
+        float* orow = plain_out + (size_t)(tc.p0 + 16 * ts + l16) * H;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const int col = c0 + 16 * w + 4 * g;
+          if (col < H) *reinterpret_cast<v4f*>(orow + col) = acc[ts][w];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
       const int src = srow[16 * ts + l16];
@@ -997,6 +1036,33 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   gemm2_tile<TMV, PACKED, MX>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB, Y)
   FP8MOE_BODIES(FP8MOE_G2_BODY)
 #undef FP8MOE_G2_BODY
+}
+// The plain grouped GEMM (SM120 page, section 1: a [rows, k] grouped by
+// expert segments, b [E, n, k], NT, fp32 out; gated: SwiGLU over gate+up)
+// on the same tiles and main loop as the expert GEMMs.
+template <int TMAX, bool PACKED, bool GATED>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_plain_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scale, const uint8_t* __restrict__ b,
+    const float* __restrict__ b_scale, const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src,
+    int E, int n, int k, int NB, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NT = GATED ? n / 2 / 128 : (n + kTN - 1) / kTN, NG = (NT + NB - 1) / NB;
+  TileCoord tc;
+  if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
+  FP8MOE_TOKEN_BUFFERS(TMAX);
+  if constexpr (GATED) {
+#define FP8MOE_PG_BODY(TMV) \
+  gemm1_tile<TMV, PACKED, false, true>(smem, tb, tc, a, a_scale, b, b_scale, sorted_src, 1, k, n / 2, NB, nullptr, \
+                                       nullptr, out)
+    FP8MOE_BODIES(FP8MOE_PG_BODY)
+#undef FP8MOE_PG_BODY
+  } else {
+#define FP8MOE_PP_BODY(TMV) \
+  gemm2_tile<TMV, PACKED, false, true>(smem, tb, tc, a, a_scale, b, b_scale, nullptr, sorted_src, n, k, NB, nullptr, \
+                                       out)
+    FP8MOE_BODIES(FP8MOE_PP_BODY)
+#undef FP8MOE_PP_BODY
+  }
 }
 #undef FP8MOE_TOKEN_BUFFERS
 #undef FP8MOE_BODIES

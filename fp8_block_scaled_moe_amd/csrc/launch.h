@@ -59,6 +59,13 @@ hipError_t launch_gemm2_mx(const uint8_t* q, const uint8_t* q_sf, const uint8_t*
                            const float* topk_weights, const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m,
                            int tile_n, bool packed, hipStream_t stream);
 
+// Plain grouped GEMM: out[p] = a[p] . b[e]^T (fp32) for every padded row p of
+// expert e with sorted_src[p] >= 0; gated: out[p, c] = silu(h[c]) * h[n/2 + c]
+// ([rows][n/2]).  tile_m in {16, 32, 64, 128}.
+hipError_t launch_grouped_gemm_plain(const uint8_t* a, const float* a_scale, const uint8_t* b, const float* b_scale,
+                                     const GroupedRows& g, int n, int k, bool gated, float* out, int tile_m,
+                                     bool packed, hipStream_t stream);
+
 // Row-major e4m3 [E][N][K] -> MFMA-tiled layout (N % 16 == 0, K % 128 == 0).
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);
 // Row-major E8M0 [E][N][K/32] -> MFMA-tiled MXFP8 scale layout of mx_scales_packed_bytes bytes.

@@ -174,6 +174,35 @@ def gemm2_weighted(q, q_scale, w2, w2_scale, route, topk_weights, T, K, align, t
     return Y
 
 
+# ---------------------------------------------------------------- plain grouped GEMM (checks)
+
+def grouped_gemm_fp8(a, a_scale, b, b_scale, route, is_gated=False, tile_m=-1, weight_layout=WEIGHTS_ROW_MAJOR,
+                     out=None):
+    """Plain grouped GEMM over a routing result's padded row space: a [rows, k] (rows =
+    len(sorted_src)), b [E, n, k].  Returns fp32 [rows, n] ([rows, n/2] gated: SwiGLU);
+    rows with sorted_src < 0 are not written (zero when out is allocated here)."""
+    a, b = _u8(a), _u8(b)
+    _need(a, torch.uint8, "a", 2)
+    _need(a_scale, torch.float32, "a_scale", 2)
+    _need(b, torch.uint8, "b", 3)
+    _need(b_scale, torch.float32, "b_scale", 3)
+    rows, k = a.shape
+    E, n, k2 = b.shape
+    if k2 != k or route["sorted_src"].numel() != rows:
+        raise ValueError("a / b / route shapes disagree")
+    if tuple(a_scale.shape) != (rows, k // 128) or tuple(b_scale.shape) != (E, n // 128, k // 128):
+        raise ValueError("inconsistent scale shapes")
+    cols = n // 2 if is_gated else n
+    out = torch.zeros((rows, cols), dtype=torch.float32, device=a.device) if out is None else out
+    _need(out, torch.float32, "out", 2)
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError(f"out must be [{rows}, {cols}]")
+    check(lib().moe_grouped_gemm_fp8(_p(a), _p(a_scale), _p(b), _p(b_scale), _p(route["padded_indptr"]),
+                                     _p(route["sorted_src"]), rows, n, k, E, int(bool(is_gated)), _p(out), tile_m,
+                                     weight_layout, _stream(a.device)))
+    return out
+
+
 # ---------------------------------------------------------------- MXFP8 variant
 
 def fused_mx_workspace_size(T, H, I, E, K):

@@ -186,6 +186,32 @@ int moe_gemm2_weighted(const void* q, const float* q_scale,
 int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E,
                 int32_t K, void* out, void* stream);
 
+/* ---------------------------------------------------------------- plain grouped GEMM (checks)
+ * moe_grouped_gemm_fp8: the plain grouped FP8 GEMM of the SM120 page's op
+ * (section 1: a, b, a_scale, b_scale, m_indptr, out, is_gated; NT operands),
+ * on the same tiles and main loop as the layer's GEMMs, exported so their
+ * arithmetic can be checked exactly (fp32 output, no requantisation).
+ *   a        fp8  [rows, k]          rows in the padded row space of
+ *                                    moe_route_permute (no gather)
+ *   a_scale  fp32 [rows, k/128]
+ *   b        fp8  [E, n, k]          (MFMA-tiled when weight_layout is
+ *                                    FP8MOE_WEIGHTS_MFMA_TILED)
+ *   b_scale  fp32 [E, n/128, k/128]
+ *   padded_indptr [E+1], sorted_src [rows] as moe_route_permute returns them
+ *   out      fp32 [rows, n], or [rows, n/2] when is_gated: for every row p of
+ *            expert e (padded_indptr[e] <= p < padded_indptr[e+1]) with
+ *            sorted_src[p] >= 0, h = a[p] . b[e]^T accumulated in fp32 with the
+ *            scales applied per 128-wide K step; out[p] = h, or
+ *            out[p, c] = silu(h[c]) * h[n/2 + c] (gate rows first).  Other rows
+ *            are not written.
+ * tile_m -1 (128) or 16, 32, 64, 128.  Requires k % 128 == 0 and
+ * n % 128 == 0 (n/2 when gated).  rows == 0 returns FP8MOE_OK.
+ */
+int moe_grouped_gemm_fp8(const void* a, const float* a_scale, const void* b, const float* b_scale,
+                         const int32_t* padded_indptr, const int32_t* sorted_src, int64_t rows,
+                         int32_t n, int32_t k, int32_t E, int32_t is_gated, float* out,
+                         int32_t tile_m, int32_t weight_layout, void* stream);
+
 /* ---------------------------------------------------------------- MXFP8 variant of the layer and its stages
  * The same layer with MXFP8 operands: the SM120 grouped-GEMM page lists an
  * mxfp8 grouped MoE GEMM family beside the FP8 groupwise one (its file list

@@ -60,14 +60,19 @@ MFMA_REL_BOUND = 2.0 ** -13
 def swiglu_error_bound(g, u, sg, su, rel=MFMA_REL_BOUND):
     """Bound on |act_gpu - act_ref| for act = silu(g) * u when g and u carry errors up to
     rel * sg and rel * su (sg, su = sum of |products| of each GEMM1 output); silu' <= 1.1,
-    plus fp32 SwiGLU evaluation (a few ulp of act)."""
+    plus the fp32 SwiGLU evaluation on the transcendental units: within (2|g| + 8) * 2^-24
+    relative for |g| <= 87, and a few more roundings; below g = -87.3 the device result is
+    a signed zero (the reciprocal's subnormal result is flushed), so there the whole
+    activation is allowed."""
     g = np.asarray(g, np.float64)
     u = np.asarray(u, np.float64)
     dg, du = rel * np.asarray(sg, np.float64), rel * np.asarray(su, np.float64)
     with np.errstate(over="ignore"):
         silu = g / (1.0 + np.exp(-g))
     act = silu * u
-    return 1.1 * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du + np.abs(act) * 2.0 ** -20
+    flushed = np.where(g - dg < -87.0, np.abs(act), 0.0)
+    return (1.1 * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du + np.abs(act) * (2 * np.abs(g) + 12) * 2.0 ** -24
+            + flushed)
 
 
 _E4M3_SORTED = None

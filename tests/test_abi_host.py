@@ -142,6 +142,22 @@ def test_pack_mx_scales_validation():
     assert L.moe_pack_mx_scales(FAKE, 1, 32, 128, FAKE, NULL) == E_SHAPE       # overlapping in / out
 
 
+def test_grouped_gemm_validation():
+    L = lib()
+    f = lambda **k: L.moe_grouped_gemm_fp8(k.get("a", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, k.get("rows", 64),
+                                           k.get("n", 256), k.get("k", 256), k.get("E", 4), k.get("gated", 0),
+                                           FAKE, k.get("tm", -1), k.get("layout", 0), NULL)
+    assert f(rows=-1) == E_SHAPE
+    assert f(k=200) == E_ALIGN
+    assert f(n=200) == E_ALIGN
+    assert f(n=384, gated=1) == E_ALIGN          # n/2 = 192 is not a multiple of 128
+    assert f(E=0) == E_SHAPE
+    assert f(tm=160) == E_TILE
+    assert f(layout=2) == E_SHAPE
+    assert f(a=NULL) == E_NULL
+    assert f(rows=0, a=NULL) == OK
+
+
 def test_pack_weights_validation():
     f = lib().moe_pack_weights
     assert f(FAKE, 0, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE
