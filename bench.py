@@ -60,17 +60,17 @@ CLASS128_TILE = {"gemm1": 128, "gemm2": 160}
 METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roofline"
 
 # HBM counters of the dominant kernel (GEMM1 at T=8192) and of the 2 GiB stream
-# kernel, KiB per dispatch, from two rocprofv3 --pmc passes of
-#   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --profile prefill --steps 2 --warmup 1
+# kernel, KiB per dispatch, and the GPU clock counter, from two rocprofv3 passes of
+#   rocprofv3 --pmc FETCH_SIZE GRBM_COUNT (then WRITE_SIZE GRBM_COUNT) -- python3 bench.py --profile prefill --steps 2 --warmup 1
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "d8a79bd3530b91e0c74d2e34a0ceafb037025e5510fc2f42e2812ff387fa258e",
-    "gemm1_fetch_kib": 5571007, "gemm1_write_kib": 156943,
-    # rocprofv3 --pmc GRBM_COUNT (same command): GPU clock cycles per dispatch summed over
+    "gemm_sources_sha256": "188433b8ef3f85b6d05724434f7f91451436d5cf54a939a245b8faa116bc1cf1",
+    "gemm1_fetch_kib": 5617300, "gemm1_write_kib": 157636,
+    # GRBM_COUNT (FETCH_SIZE pass): GPU clock cycles per dispatch summed over
     # the 8 XCDs, and the dispatch's average duration under that pass
-    "gemm1_grbm_count": 36129440, "gemm1_grbm_dur_us": 2681.79,
-    "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
+    "gemm1_grbm_count": 36066440, "gemm1_grbm_dur_us": 2557.78,
+    "stream_fetch_kib": 1048589, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm_kernels.h", "fp8_block_scaled_moe_amd/csrc/gemm1.hip",
                 "fp8_block_scaled_moe_amd/csrc/device_common.h", "fp8_block_scaled_moe_amd/csrc/launch.h")
