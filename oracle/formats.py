@@ -234,3 +234,87 @@ def dequant_rows_mx(q, sf, block=32):
     R, C = q.shape
     v = e4m3_decode_table(q).reshape(R, C // block, block)
     return (v * e8m0_decode(sf)[:, :, None]).reshape(R, C)
+
+
+# ---------------------------------------------------------------- MXFP4 (e2m1 codes, 1x32 E8M0 blocks)
+#
+# OCP e2m1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit; magnitudes
+# 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7, code | 8 negative.  Two codes
+# per byte along a row, the even element in the low nibble.
+
+E2M1_MAX = 6.0
+_E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes):
+    """e2m1 codes (0..15) -> float64 values."""
+    c = np.asarray(codes, dtype=np.int64)
+    v = _E2M1_MAGS[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def e2m1_encode_sat(x):
+    """Real values -> e2m1 codes: saturate |x| to 6, then the nearest of the eight
+    magnitudes, ties to the code with an even mantissa bit (even code).  The sign
+    of a value that rounds to zero is kept (code 8 for -0)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    d = np.abs(a[..., None] - _E2M1_MAGS)                     # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                           # one, or two at a tie
+    idx = np.arange(8)
+    # at a tie prefer the even code (mantissa bit 0)
+    score = np.where(cand, np.where(idx % 2 == 0, 0, 1), 2)
+    mag = np.argmin(score, axis=-1)
+    return (mag | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
+
+
+def fp4_pack(codes):
+    """e2m1 codes [..., C] (C even) -> bytes [..., C/2], element 2i in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4)
+
+
+def fp4_unpack(packed):
+    """bytes [..., C/2] -> e2m1 codes [..., C]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def e8m0_exponent_for_amax_fp4(amax):
+    """Smallest integer e with amax <= 6 * 2^e, clamped to [-127, 127] (amax == 0 -> -127):
+    the MXFP4 block scale that never makes amax / 2^e exceed the e2m1 maximum.
+    Exact float64 comparisons against 6 * 2^e."""
+    a = np.asarray(amax, dtype=np.float64)
+    pos = a > 0
+    safe = np.where(pos, a, E2M1_MAX)
+    e = np.ceil(np.log2(safe / E2M1_MAX)).astype(np.int64)
+    for _ in range(2):
+        e = np.where(safe > np.ldexp(E2M1_MAX, e), e + 1, e)
+        e = np.where(safe <= np.ldexp(E2M1_MAX, e - 1), e - 1, e)
+    e = np.where(pos, e, -127)
+    return np.clip(e, -127, 127)
+
+
+def quantize_rows_mxfp4(x, block=32):
+    """Per-row MXFP4 quantisation of a float32 matrix [R, C]: per `block` columns,
+    e = e8m0_exponent_for_amax_fp4(amax), codes = e2m1_encode_sat(x * 2^-e) (exact
+    scaling).  Returns (packed codes uint8 [R, C/2], E8M0 codes uint8 [R, C/block])."""
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    assert C % block == 0 and C % 2 == 0
+    xb = x.reshape(R, C // block, block).astype(np.float64)
+    e = e8m0_exponent_for_amax_fp4(np.max(np.abs(xb), axis=2))
+    codes = e2m1_encode_sat(np.ldexp(xb, (-e)[:, :, None])).reshape(R, C)
+    return fp4_pack(codes), e8m0_code(e)
+
+
+def dequant_rows_mxfp4(packed, sf, block=32):
+    """float64 values of packed MXFP4 codes [R, C/2] with E8M0 codes [R, C/block]."""
+    codes = fp4_unpack(packed)
+    R, C = codes.shape
+    v = e2m1_decode(codes).reshape(R, C // block, block)
+    return (v * e8m0_decode(sf)[:, :, None]).reshape(R, C)

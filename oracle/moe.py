@@ -27,8 +27,9 @@ Inputs (numpy, or anything indexable by expert for the weights):
   topk_weights f32  [T, K]
 
 moe_reference_mx is the MXFP8 variant (1x32 E8M0 scales on every operand,
-the intermediate requantised in the gated-act kernel's format); its readings
-are listed above its definition.
+the intermediate requantised in the gated-act kernel's format) and
+moe_reference_mxfp4 the MXFP4 (W4A4) one; their readings are listed above
+their definitions.
 """
 
 import numpy as np
@@ -81,13 +82,15 @@ def expert_ffn(xq_rows, xs_rows, w13_q, w13_s, w2_q, w2_s, stages=None):
     return Y
 
 
-def _layer(expert_fn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights, tokens, return_stages):
-    """Route rows to experts, run expert_fn on each expert's rows, combine."""
+def _layer(expert_fn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights, tokens, return_stages,
+           H=None):
+    """Route rows to experts, run expert_fn on each expert's rows, combine (H: output
+    width, by default the width of x_q)."""
     ids = np.asarray(topk_ids)
     wts = np.asarray(topk_weights, dtype=np.float32)
     T, K = ids.shape
     E = len(w13_q)
-    H = np.asarray(x_q).shape[1]
+    H = np.asarray(x_q).shape[1] if H is None else H
     toks = list(range(T)) if tokens is None else sorted(int(t) for t in tokens)
     pos = {t: i for i, t in enumerate(toks)}
 
@@ -170,3 +173,40 @@ def moe_reference_mx(x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weigh
     E8M0 scale codes (uint8) x_sf [T, H/32], w13_sf [E][2I, H/32], w2_sf [E][H, I/32]."""
     return _layer(expert_ffn_mx, x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
                   tokens, return_stages)
+
+
+# ---------------------------------------------------------------- MXFP4 (W4A4) variant
+#
+# The cuTile page lists NVFP4 W4A4 experts (16-element blocks with an fp8
+# scale and a per-expert global scale); on gfx950 the block-scaled MFMA takes
+# the OCP MXFP4 format instead.  Readings taken here:
+#   * every operand is e2m1 codes with one E8M0 scale per 32 consecutive
+#     elements along the contraction dimension (as in the MXFP8 variant);
+#   * the block exponent is the smallest e with amax <= 6 * 2^e (the MXFP8
+#     rule with the e2m1 maximum 6 in place of 448), codes e2m1(x * 2^-e)
+#     rounded to nearest, ties to even;
+#   * the intermediate is requantised the same way per row and 32 columns of I.
+
+def expert_ffn_mxfp4(xq_rows, xsf_rows, w13_q, w13_sf, w2_q, w2_sf, stages=None):
+    """One expert on its gathered rows, MXFP4 operands (packed e2m1 codes)."""
+    A = formats.dequant_rows_mxfp4(xq_rows, xsf_rows)                       # [n, H]
+    W13 = formats.dequant_rows_mxfp4(np.asarray(w13_q), np.asarray(w13_sf))  # [2I, H]
+    I = W13.shape[0] // 2
+    H1 = A @ W13.T
+    g, u = H1[:, :I], H1[:, I:]
+    act = silu_mul(g, u).astype(np.float32)
+    q, sf = formats.quantize_rows_mxfp4(act, 32)
+    W2 = formats.dequant_rows_mxfp4(np.asarray(w2_q), np.asarray(w2_sf))    # [H, I]
+    Y = formats.dequant_rows_mxfp4(q, sf) @ W2.T
+    if stages is not None:
+        stages.update(H1=H1, act=act, q=q, s=sf, Y=Y)
+    return Y
+
+
+def moe_reference_mxfp4(x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
+                        tokens=None, return_stages=False):
+    """Reference MXFP4 (W4A4) MoE layer: x_q uint8 [T, H/2] (two e2m1 codes per byte,
+    the even element in the low nibble), x_sf [T, H/32]; w13_q [E][2I, H/2], w13_sf
+    [E][2I, H/32]; w2_q [E][H, I/2], w2_sf [E][H, I/32]."""
+    return _layer(expert_ffn_mxfp4, x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
+                  tokens, return_stages, H=2 * np.asarray(x_q).shape[1])

@@ -102,6 +102,32 @@ def quant_rows_mx(x):
     return q.view(torch.uint8).reshape(R, C), (e + 127).to(torch.uint8).contiguous()
 
 
+def quant_rows_mxfp4(x):
+    """fp32 torch [R, C] -> (uint8 packed e2m1 codes [R, C/2], uint8 E8M0 codes [R, C/32]).
+
+    Harness MXFP4 quantisation of 1x32 blocks: with amax = m * 2^p (frexp) and
+    6 = 0.75 * 2^3, the smallest e with amax <= 6 * 2^e is p - 3 when m <= 0.75
+    and p - 2 otherwise (clamped to [-127, 127], -127 for a zero block).  The
+    e2m1 magnitude code of |v| = |x| * 2^-e is the number of rounding
+    thresholds it passes, with ties to the even code: > 0.25, >= 0.75, > 1.25,
+    >= 1.75, > 2.5, >= 3.5, > 5 (so 6 for everything above 5); the sign is the
+    value's.  Two codes per byte, the even element in the low nibble.
+    """
+    R, C = x.shape
+    xb = x.reshape(R, C // 32, 32)
+    amax = xb.abs().amax(dim=2)
+    m, p = torch.frexp(amax)
+    e = p.to(torch.int32) - 3 + (m > 0.75).to(torch.int32)
+    e = torch.where(amax == 0, torch.full_like(e, -127), e).clamp_(-127, 127)
+    v = torch.ldexp(xb, (-e).to(xb.dtype)[:, :, None])
+    a = v.abs()
+    mag = ((a > 0.25).int() + (a >= 0.75).int() + (a > 1.25).int() + (a >= 1.75).int() + (a > 2.5).int()
+           + (a >= 3.5).int() + (a > 5.0).int())
+    codes = (mag | (torch.signbit(v).int() << 3)).to(torch.uint8).reshape(R, C)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
 # ---------------------------------------------------------------- activations and weights
 
 def activations(T, H, cfg, extra=()):
@@ -151,6 +177,25 @@ def expert_weight_set_mx(E, N, K, cfg, tag, device="cpu", std=0.02):
             g.manual_seed(torch_seed(cfg, tag, e))
             w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * std
         qe, se = quant_rows_mx(w)
+        q[e].copy_(qe)
+        s[e].copy_(se)
+    return q, s
+
+
+def expert_weight_set_mxfp4(E, N, K, cfg, tag, device="cpu", std=0.02):
+    """The same fp32 weights as expert_weight_set, MXFP4-quantised along K:
+    (packed codes uint8 [E, N, K/2], E8M0 codes uint8 [E, N, K/32])."""
+    q = torch.empty((E, N, K // 2), dtype=torch.uint8, device=device)
+    s = torch.empty((E, N, K // 32), dtype=torch.uint8, device=device)
+    dev = torch.device(device)
+    for e in range(E):
+        if dev.type == "cpu":
+            w = torch.from_numpy(expert_weights_fp32(E, N, K, cfg, tag, e, std))
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(torch_seed(cfg, tag, e))
+            w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * std
+        qe, se = quant_rows_mxfp4(w)
         q[e].copy_(qe)
         s[e].copy_(se)
     return q, s
@@ -220,6 +265,33 @@ def moe_problem_mx(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weig
     w2_q, w2_sf = expert_weight_set_mx(E, H, I, wc, TAG_W2, wd)
     return MoEInputs(T, H, I, E, K, x_q, x_sf, w13_q.to(device), w13_sf.to(device),
                      w2_q.to(device), w2_sf.to(device), ids, w)
+
+
+def moe_tokens_mxfp4(T, H, E, K, cfg, extra=(), zipf_s=None, device="cpu"):
+    """Token-side MXFP4 inputs (same activations and routing as moe_tokens):
+    (x_q packed [T, H/2], x_sf E8M0 [T, H/32], topk_ids, topk_weights)."""
+    ids, w = router(T, E, K, cfg, extra, zipf_s)
+    x = torch.from_numpy(activations(T, H, cfg, extra))
+    x_q, x_sf = quant_rows_mxfp4(x)
+    return (x_q.to(device), x_sf.to(device), torch.from_numpy(ids).to(device),
+            torch.from_numpy(w).to(device))
+
+
+def moe_problem_mxfp4(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weight_cfg=None,
+                      weight_device=None):
+    """moe_problem with MXFP4 operands (packed e2m1 codes; the scale fields hold E8M0 codes)."""
+    wc = cfg if weight_cfg is None else weight_cfg
+    wd = device if weight_device is None else weight_device
+    x_q, x_sf, ids, w = moe_tokens_mxfp4(T, H, E, K, cfg, extra, zipf_s, device)
+    w13_q, w13_sf = expert_weight_set_mxfp4(E, 2 * I, H, wc, TAG_W13, wd)
+    w2_q, w2_sf = expert_weight_set_mxfp4(E, H, I, wc, TAG_W2, wd)
+    return MoEInputs(T, H, I, E, K, x_q, x_sf, w13_q.to(device), w13_sf.to(device),
+                     w2_q.to(device), w2_sf.to(device), ids, w)
+
+
+# MXFP4 needs H and I to be multiples of 256 (one 128-byte row step is 256 e2m1
+# values); its tiny problem keeps T, H, E, K of the tiny config with I = 256
+TINY_FP4 = dict(T=16, H=256, I=256, E=4, K=2)
 
 
 # named configurations (token count T, hidden H, intermediate I, experts E, top-k K)
