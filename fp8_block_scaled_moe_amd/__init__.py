@@ -1,4 +1,4 @@
-"""MI355X (gfx950) W8A8 FP8 block-scaled MoE expert path (and its MXFP8 variant).
+"""MI355X (gfx950) W8A8 FP8 block-scaled MoE expert path (and its MXFP8 and MXFP4 variants).
 
 The computation lives in libfp8moe.so (hand-written HIP kernels behind the C
 ABI of include/fp8moe.h); this package only loads it and marshals torch
@@ -10,5 +10,7 @@ from .ops import (  # noqa: F401
     route_capacity, route_permute, fused_workspace_size, alloc_workspace, moe_fused_fp8,
     gemm1_swiglu_quant, gemm2_weighted, combine, gated_act_fp8_quant, select_tile,
     select_tile_classes, pack_weights, WEIGHTS_ROW_MAJOR, WEIGHTS_MFMA_TILED,
-    fused_mx_workspace_size, alloc_workspace_mx, moe_fused_mxfp8, pack_mx_scales, grouped_gemm_fp8, gemm1_swiglu_quant_mx, gemm2_weighted_mx,
+    fused_mx_workspace_size, alloc_workspace_mx, moe_fused_mxfp8, pack_mx_scales, grouped_gemm_fp8,
+    fused_mxfp4_workspace_size, alloc_workspace_mxfp4, moe_fused_mxfp4, pack_mxfp4_scales,
+    gemm1_swiglu_quant_mxfp4, gemm2_weighted_mxfp4, gemm1_swiglu_quant_mx, gemm2_weighted_mx,
 )

@@ -34,6 +34,15 @@ SIGNATURES = {
                                              _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
     "moe_pack_weights": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "moe_pack_mx_scales_bytes": (_i64, [_i64, _i32, _i32]),
+    "moe_pack_mxfp4_scales_bytes": (_i64, [_i64, _i32, _i32]),
+    "moe_pack_mxfp4_scales": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
+    "moe_fused_mxfp4_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
+    "moe_fused_mxfp4": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                       _vp, _vp, _sz, _i32, _i32, _i32, _vp]),
+    "moe_gemm1_swiglu_quant_mxfp4": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                                    _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
+    "moe_gemm2_weighted_mxfp4": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                                _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
                                             _i32, _vp]),
     "moe_pack_mx_scales": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8moe.so")
 
-SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm1.hip", "gemm2.hip", "gemm1_mx.hip", "gemm2_mx.hip", "gemm_plain.hip",
+SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm1.hip", "gemm2.hip", "gemm1_mx.hip", "gemm2_mx.hip", "gemm1_mxfp4.hip",
+           "gemm2_mxfp4.hip", "gemm_plain.hip",
            "combine.hip", "gated_act.hip", "pack.hip"]
 
 ARCH = "gfx950"

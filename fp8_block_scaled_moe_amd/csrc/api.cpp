@@ -54,8 +54,13 @@ struct WsLayout {
   size_t counts, m_indptr, padded, sorted_src, src_to_sorted, q, q_scale, Y, total;
 };
 
-// MXFP8: q_scale holds one E8M0 byte per 32 columns instead of a float per 128.
-WsLayout ws_layout(int64_t T, int H, int I, int E, int K, bool mx) {
+// Operand formats of the layer: FP8 with fp32 block scales, MXFP8 and MXFP4
+// (W4A4), both with E8M0 scales per 32 elements.
+enum Fmt { kFmtFp8 = 0, kFmtMx8 = 1, kFmtMx4 = 2 };
+
+// MX: q_scale holds one E8M0 byte per 32 columns instead of a float per 128;
+// MXFP4: q holds two e2m1 codes per byte.
+WsLayout ws_layout(int64_t T, int H, int I, int E, int K, int fmt) {
   const int64_t R = T * K;
   const int64_t cap = R + (int64_t)E * (128 - 1);  // worst case: align 128
   WsLayout w{};
@@ -66,8 +71,8 @@ WsLayout ws_layout(int64_t T, int H, int I, int E, int K, bool mx) {
   w.padded = take(sizeof(int32_t) * (E + 1));
   w.sorted_src = take(sizeof(int32_t) * cap);
   w.src_to_sorted = take(sizeof(int32_t) * (R > 0 ? R : 1));
-  w.q = take((size_t)cap * I);
-  w.q_scale = take(mx ? (size_t)cap * (I / 32) : sizeof(float) * (size_t)cap * (I / 128));
+  w.q = take((size_t)cap * (fmt == kFmtMx4 ? I / 2 : I));
+  w.q_scale = take(fmt != kFmtFp8 ? (size_t)cap * (I / 32) : sizeof(float) * (size_t)cap * (I / 128));
   w.Y = take(sizeof(uint16_t) * (size_t)(R > 0 ? R : 1) * H);
   w.total = off;
   return w;
@@ -111,36 +116,44 @@ int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
   return cls == 128 ? (gated ? kClass128TileGemm1 : kClass128TileGemm2) : cls;
 }
 
-// Scale pointer type of each format: fp32 block scales (FP8) or E8M0 codes
-// (MXFP8); the launchers are chosen by overload on it.
-template <bool MX>
-using scale_ptr_t = std::conditional_t<MX, uint8_t, float>;
+// Scale pointer type of each format: fp32 block scales (FP8) or E8M0 codes (MX).
+template <int F>
+using scale_ptr_t = std::conditional_t<F == kFmtFp8, float, uint8_t>;
 
-hipError_t gemm1_launch(const uint8_t* x, const float* xs, const uint8_t* w, const float* ws, const GroupedRows& g,
-                        int H, int I, uint8_t* q, float* qs, int tm, bool packed, hipStream_t st) {
-  return launch_gemm1(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+// MXFP4 rows are 256-element K steps: H and I multiples of 256
+template <int F>
+int check_format_dims(int H, int I) {
+  if (F == kFmtMx4 && (H % 256 || I % 256))
+    return fail(FP8MOE_ERR_ALIGN, "MXFP4 needs H and I multiples of 256 (got %d, %d)", H, I);
+  return FP8MOE_OK;
 }
-hipError_t gemm1_launch(const uint8_t* x, const uint8_t* xs, const uint8_t* w, const uint8_t* ws,
-                        const GroupedRows& g, int H, int I, uint8_t* q, uint8_t* qs, int tm, bool packed,
+
+template <int F>
+hipError_t gemm1_launch(const uint8_t* x, const scale_ptr_t<F>* xs, const uint8_t* w, const scale_ptr_t<F>* ws,
+                        const GroupedRows& g, int H, int I, uint8_t* q, scale_ptr_t<F>* qs, int tm, bool packed,
                         hipStream_t st) {
-  return launch_gemm1_mx(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
-}
-hipError_t gemm2_launch(const uint8_t* q, const float* qs, const uint8_t* w, const float* ws, const float* tw,
-                        const GroupedRows& g, int H, int I, uint16_t* Y, int tm, bool packed, hipStream_t st) {
-  return launch_gemm2(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
-}
-hipError_t gemm2_launch(const uint8_t* q, const uint8_t* qs, const uint8_t* w, const uint8_t* ws, const float* tw,
-                        const GroupedRows& g, int H, int I, uint16_t* Y, int tm, bool packed, hipStream_t st) {
-  return launch_gemm2_mx(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+  if constexpr (F == kFmtFp8) return launch_gemm1(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+  else if constexpr (F == kFmtMx8) return launch_gemm1_mx(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+  else return launch_gemm1_mxfp4(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
 }
 
-template <bool MX>
-int fused_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, const scale_ptr_t<MX>* w13_scale,
-               const void* w2, const scale_ptr_t<MX>* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+template <int F>
+hipError_t gemm2_launch(const uint8_t* q, const scale_ptr_t<F>* qs, const uint8_t* w, const scale_ptr_t<F>* ws,
+                        const float* tw, const GroupedRows& g, int H, int I, uint16_t* Y, int tm, bool packed,
+                        hipStream_t st) {
+  if constexpr (F == kFmtFp8) return launch_gemm2(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+  else if constexpr (F == kFmtMx8) return launch_gemm2_mx(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+  else return launch_gemm2_mxfp4(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+}
+
+template <int F>
+int fused_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, const scale_ptr_t<F>* w13_scale,
+               const void* w2, const scale_ptr_t<F>* w2_scale, const int32_t* topk_ids, const float* topk_weights,
                int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, void* workspace,
                size_t workspace_bytes, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
+  if ((st = check_format_dims<F>(H, I))) return st;
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   const bool packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
   if (tile_m != -1 && !valid_tile_m(tile_m))
@@ -149,7 +162,7 @@ int fused_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, c
   if (T == 0) return ok();
   if (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out)
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
-  const WsLayout L = ws_layout(T, H, I, E, K, MX);
+  const WsLayout L = ws_layout(T, H, I, E, K, F);
   if (!workspace) return fail(FP8MOE_ERR_WORKSPACE, "workspace is null");
   if ((uintptr_t)workspace % kAlignWs) return fail(FP8MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -170,7 +183,7 @@ int fused_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, c
   int32_t* sorted_src = reinterpret_cast<int32_t*>(ws + L.sorted_src);
   int32_t* src_to_sorted = reinterpret_cast<int32_t*>(ws + L.src_to_sorted);
   uint8_t* q = ws + L.q;
-  scale_ptr_t<MX>* q_scale = reinterpret_cast<scale_ptr_t<MX>*>(ws + L.q_scale);
+  scale_ptr_t<F>* q_scale = reinterpret_cast<scale_ptr_t<F>*>(ws + L.q_scale);
   uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
   hipStream_t s = (hipStream_t)stream;
 
@@ -178,24 +191,25 @@ int fused_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, c
                                         sorted_src, src_to_sorted, s);
   if (err != hipSuccess) return hip_fail(err, "route_permute launch");
   GroupedRows g{padded, sorted_src, cap, E, K, R, device_num_cu()};
-  err = gemm1_launch(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale, g, H,
-                     I, q, q_scale, tm1, packed, s);
+  err = gemm1_launch<F>(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale, g, H,
+                        I, q, q_scale, tm1, packed, s);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
-  err = gemm2_launch(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2, packed,
-                     s);
+  err = gemm2_launch<F>(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2,
+                        packed, s);
   if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
   err = launch_combine(Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
   return ok();
 }
 
-template <bool MX>
-int gemm1_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, const scale_ptr_t<MX>* w13_scale,
+template <int F>
+int gemm1_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, const scale_ptr_t<F>* w13_scale,
                const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H, int32_t I, int32_t E,
-               int32_t K, int32_t align, void* q, scale_ptr_t<MX>* q_scale, int64_t cap, int32_t tile_m,
+               int32_t K, int32_t align, void* q, scale_ptr_t<F>* q_scale, int64_t cap, int32_t tile_m,
                int32_t weight_layout, void* stream) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
+  if ((st = check_format_dims<F>(H, I))) return st;
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   if (tile_m != -1 && !valid_tile_m(tile_m))
@@ -206,20 +220,21 @@ int gemm1_impl(const void* x, const scale_ptr_t<MX>* x_scale, const void* w13, c
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
-  hipError_t err = gemm1_launch(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
-                                w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
+  hipError_t err = gemm1_launch<F>(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
+                                   w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
                                 weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
   return ok();
 }
 
-template <bool MX>
-int gemm2_impl(const void* q, const scale_ptr_t<MX>* q_scale, const void* w2, const scale_ptr_t<MX>* w2_scale,
+template <int F>
+int gemm2_impl(const void* q, const scale_ptr_t<F>* q_scale, const void* w2, const scale_ptr_t<F>* w2_scale,
                const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights, int64_t T,
                int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y, int64_t cap, int32_t tile_m,
                int32_t tile_n, int32_t weight_layout, void* stream) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
+  if ((st = check_format_dims<F>(H, I))) return st;
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   if (tile_m != -1 && !valid_tile_m(tile_m))
@@ -231,8 +246,8 @@ int gemm2_impl(const void* q, const scale_ptr_t<MX>* q_scale, const void* w2, co
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
-  hipError_t err = gemm2_launch(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2), w2_scale,
-                                topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm,
+  hipError_t err = gemm2_launch<F>(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2), w2_scale,
+                                   topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm,
                                 weight_layout == FP8MOE_WEIGHTS_MFMA_TILED, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
   return ok();
@@ -288,7 +303,7 @@ int moe_fused_fp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
   if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
-  *bytes = ws_layout(T, H, I, E, K, false).total;
+  *bytes = ws_layout(T, H, I, E, K, kFmtFp8).total;
   return ok();
 }
 
@@ -296,7 +311,7 @@ int moe_fused_mxfp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, i
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
   if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
-  *bytes = ws_layout(T, H, I, E, K, true).total;
+  *bytes = ws_layout(T, H, I, E, K, kFmtMx8).total;
   return ok();
 }
 
@@ -305,7 +320,7 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
                   const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                   void* out, void* workspace, size_t workspace_bytes, int32_t tile_m, int32_t tile_n,
                   int32_t weight_layout, void* stream) {
-  return fused_impl<false>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, out,
+  return fused_impl<kFmtFp8>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, out,
                            workspace, workspace_bytes, tile_m, tile_n, weight_layout, stream);
 }
 
@@ -313,7 +328,7 @@ int moe_fused_mxfp8(const void* x, const uint8_t* x_sf, const void* w13, const u
                     const uint8_t* w2_sf, const int32_t* topk_ids, const float* topk_weights, int64_t T, int32_t H,
                     int32_t I, int32_t E, int32_t K, void* out, void* workspace, size_t workspace_bytes,
                     int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
-  return fused_impl<true>(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, T, H, I, E, K, out, workspace,
+  return fused_impl<kFmtMx8>(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, T, H, I, E, K, out, workspace,
                           workspace_bytes, tile_m, tile_n, weight_layout, stream);
 }
 
@@ -321,7 +336,7 @@ int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13,
                            const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
                            int32_t I, int32_t E, int32_t K, int32_t align, void* q, float* q_scale,
                            int64_t cap, int32_t tile_m, int32_t weight_layout, void* stream) {
-  return gemm1_impl<false>(x, x_scale, w13, w13_scale, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_scale,
+  return gemm1_impl<kFmtFp8>(x, x_scale, w13, w13_scale, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_scale,
                            cap, tile_m, weight_layout, stream);
 }
 
@@ -329,7 +344,7 @@ int moe_gemm1_swiglu_quant_mx(const void* x, const uint8_t* x_sf, const void* w1
                               const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
                               int32_t I, int32_t E, int32_t K, int32_t align, void* q, uint8_t* q_sf, int64_t cap,
                               int32_t tile_m, int32_t weight_layout, void* stream) {
-  return gemm1_impl<true>(x, x_sf, w13, w13_sf, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_sf, cap,
+  return gemm1_impl<kFmtMx8>(x, x_sf, w13, w13_sf, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_sf, cap,
                           tile_m, weight_layout, stream);
 }
 
@@ -337,7 +352,7 @@ int moe_gemm2_weighted(const void* q, const float* q_scale, const void* w2, cons
                        const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
                        int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y,
                        int64_t cap, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
-  return gemm2_impl<false>(q, q_scale, w2, w2_scale, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align,
+  return gemm2_impl<kFmtFp8>(q, q_scale, w2, w2_scale, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align,
                            Y, cap, tile_m, tile_n, weight_layout, stream);
 }
 
@@ -345,7 +360,7 @@ int moe_gemm2_weighted_mx(const void* q, const uint8_t* q_sf, const void* w2, co
                           const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
                           int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y, int64_t cap,
                           int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
-  return gemm2_impl<true>(q, q_sf, w2, w2_sf, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align, Y, cap,
+  return gemm2_impl<kFmtMx8>(q, q_sf, w2, w2_sf, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align, Y, cap,
                           tile_m, tile_n, weight_layout, stream);
 }
 
@@ -394,18 +409,74 @@ int64_t moe_pack_mx_scales_bytes(int64_t E, int32_t N, int32_t K) {
     return fail(FP8MOE_ERR_SHAPE, "MX scale pack needs E >= 1, N %% 16 == 0, K %% 128 == 0 (E=%lld N=%d K=%d)",
                 (long long)E, N, K);
   ok();
-  return mx_scales_packed_bytes(E, N, K);
+  return mx_scales_packed_bytes(E, N, K, 1);
 }
 
-int moe_pack_mx_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {
-  const int64_t n = moe_pack_mx_scales_bytes(E, N, K);
+int64_t moe_pack_mxfp4_scales_bytes(int64_t E, int32_t N, int32_t K) {
+  if (E < 1 || N <= 0 || K <= 0 || N % 16 || K % 256)
+    return fail(FP8MOE_ERR_SHAPE, "MXFP4 scale pack needs E >= 1, N %% 16 == 0, K %% 256 == 0 (E=%lld N=%d K=%d)",
+                (long long)E, N, K);
+  ok();
+  return mx_scales_packed_bytes(E, N, K, 2);
+}
+
+}  // extern "C"
+
+namespace {
+
+int pack_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, int spb, int64_t n, void* out, void* stream) {
   if (n < 0) return (int)n;
   if (!in || !out) return fail(FP8MOE_ERR_NULL, "null tensor argument");
   const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out, na = (uintptr_t)(E * (int64_t)N * (K / 32));
   if (a < b + (uintptr_t)n && b < a + na) return fail(FP8MOE_ERR_SHAPE, "pack in and out overlap");
-  hipError_t err = launch_pack_mx_scales(in, E, N, K, static_cast<uint8_t*>(out), (hipStream_t)stream);
+  hipError_t err = launch_pack_mx_scales(in, E, N, K, spb, static_cast<uint8_t*>(out), (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "pack_mx_scales launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_pack_mx_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {
+  return pack_scales(in, E, N, K, 1, moe_pack_mx_scales_bytes(E, N, K), out, stream);
+}
+
+int moe_pack_mxfp4_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {
+  return pack_scales(in, E, N, K, 2, moe_pack_mxfp4_scales_bytes(E, N, K), out, stream);
+}
+
+int moe_fused_mxfp4_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, size_t* bytes) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if ((st = check_format_dims<kFmtMx4>(H, I))) return st;
+  if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
+  *bytes = ws_layout(T, H, I, E, K, kFmtMx4).total;
+  return ok();
+}
+
+int moe_fused_mxfp4(const void* x, const uint8_t* x_sf, const void* w13, const uint8_t* w13_sf, const void* w2,
+                    const uint8_t* w2_sf, const int32_t* topk_ids, const float* topk_weights, int64_t T, int32_t H,
+                    int32_t I, int32_t E, int32_t K, void* out, void* workspace, size_t workspace_bytes,
+                    int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+  return fused_impl<kFmtMx4>(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, T, H, I, E, K, out, workspace,
+                             workspace_bytes, tile_m, tile_n, weight_layout, stream);
+}
+
+int moe_gemm1_swiglu_quant_mxfp4(const void* x, const uint8_t* x_sf, const void* w13, const uint8_t* w13_sf,
+                                 const int32_t* padded_indptr, const int32_t* sorted_src, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t K, int32_t align, void* q, uint8_t* q_sf, int64_t cap,
+                                 int32_t tile_m, int32_t weight_layout, void* stream) {
+  return gemm1_impl<kFmtMx4>(x, x_sf, w13, w13_sf, padded_indptr, sorted_src, T, H, I, E, K, align, q, q_sf, cap,
+                             tile_m, weight_layout, stream);
+}
+
+int moe_gemm2_weighted_mxfp4(const void* q, const uint8_t* q_sf, const void* w2, const uint8_t* w2_sf,
+                             const int32_t* padded_indptr, const int32_t* sorted_src, const float* topk_weights,
+                             int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* Y, int64_t cap,
+                             int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+  return gemm2_impl<kFmtMx4>(q, q_sf, w2, w2_sf, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align, Y,
+                             cap, tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_combine(const void* Y, const int32_t* topk_ids, int64_t T, int32_t H, int32_t E, int32_t K, void* out,

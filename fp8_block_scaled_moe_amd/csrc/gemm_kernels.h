@@ -110,37 +110,66 @@ using scale_t = std::conditional_t<MX, uint8_t, float>;
 // order), so the 32-K block k of the step is bytes 0..15 of lane groups
 // 2(k%2), 2(k%2)+1 for k < 2 and bytes 16..31 of them for k >= 2 -- exactly
 // the elements lane 16k + row's scale covers.
-template <int SA, int SB>
+// FMT: operand format code of both operands (0 = e4m3, 4 = e2m1; an e2m1
+// operand is the first 16 bytes of each lane: 32 values, all of the lane's
+// 32-K block l / 16 -- measured like the e4m3 layout)
+template <int SA, int SB, int FMT>
 __device__ __forceinline__ v4f mfma16x16x128_mx(const v8i& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, SA, (int)sa, SB, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, SA, (int)sa, SB, (int)sb);
 }
 // byte sela of sa and byte selb of sb; both are constants of the unrolled loops
+template <int FMT = 0>
 __device__ __forceinline__ v4f mfma16x16x128_mx_sel(int sela, int selb, const v8i& a, const v8i& b, const v4f& c,
                                                     uint32_t sa, uint32_t sb) {
 #define FP8MOE_MX_CASE(A, B) \
-  case 4 * A + B: return mfma16x16x128_mx<A, B>(a, b, c, sa, sb);
+  case 4 * A + B: return mfma16x16x128_mx<A, B, FMT>(a, b, c, sa, sb);
   switch (4 * sela + selb) {
     FP8MOE_MX_CASE(0, 0) FP8MOE_MX_CASE(0, 1) FP8MOE_MX_CASE(0, 2) FP8MOE_MX_CASE(0, 3)
     FP8MOE_MX_CASE(1, 0) FP8MOE_MX_CASE(1, 1) FP8MOE_MX_CASE(1, 2) FP8MOE_MX_CASE(1, 3)
     FP8MOE_MX_CASE(2, 0) FP8MOE_MX_CASE(2, 1) FP8MOE_MX_CASE(2, 2) FP8MOE_MX_CASE(2, 3)
     FP8MOE_MX_CASE(3, 0) FP8MOE_MX_CASE(3, 1) FP8MOE_MX_CASE(3, 2)
-    default: return mfma16x16x128_mx<3, 3>(a, b, c, sa, sb);
+    default: return mfma16x16x128_mx<3, 3, FMT>(a, b, c, sa, sb);
   }
 #undef FP8MOE_MX_CASE
 }
 
-// MXFP8 weight scales in the MFMA-tiled layout (moe_pack_mx_scales): per
-// 16-row band, groups of 4 K steps of 256 bytes, lane l's dword holding its
-// scale code of each of the 4 steps, so a wave reads the scales of a whole
-// round of the operand ring with one contiguous dword load per band.
-constexpr int kMxScaleGroup = 4;     // K steps per packed scale dword
+// MX weight scales in the MFMA-tiled layout (moe_pack_mx_scales,
+// moe_pack_mxfp4_scales): per 16-row band, groups of 4 K steps of 256 * SPB
+// bytes, lane l's SPB dwords holding its scale code of each MFMA of the 4
+// steps (SPB = MFMAs per operand pair and step: 1 for e4m3, whose 128-byte
+// step is 128 K; 2 for e2m1, whose 128-byte step is 256 K), so a wave reads
+// the scales of a whole round of the operand ring with one contiguous load
+// per band.
+constexpr int kMxScaleGroup = 4;     // K steps per packed scale group
 __host__ __device__ constexpr int mx_scale_groups(int KT) { return (KT + kMxScaleGroup - 1) / kMxScaleGroup; }
 
-// Bytes of one expert's MXFP8 weight scales for N rows and a K extent of kdim:
-// row-major [N][kdim/32], or MFMA-tiled [N/16][groups][64 lanes][4].
-template <bool PACKED>
+// Bytes of one expert's MX weight scales for N rows of kdim bytes (SPB = 2
+// for e2m1 rows, whose bytes hold two elements): row-major [N][SPB*kdim/32],
+// or MFMA-tiled [N/16][groups][64 lanes][4 * SPB].
+template <bool PACKED, int SPB = 1>
 __host__ __device__ constexpr int mx_weight_scale_bytes(int N, int kdim) {
-  return PACKED ? N / 16 * mx_scale_groups(kdim / kKB) * 256 : N * (kdim / 32);
+  return PACKED ? N / 16 * mx_scale_groups(kdim / kKB) * 256 * SPB : N * (SPB * kdim / 32);
+}
+
+// MXFP4 block exponent: the smallest e with amax <= 6 * 2^e (frexp: amax =
+// m * 2^x, 6 = 0.75 * 2^3, so e = x - 3 if m <= 0.75 else x - 2), clamped to
+// [-127, 127]; -127 for amax == 0.  Codes e2m1(v * 2^-e) never saturate.
+__device__ __forceinline__ int e8m0_exponent_fp4(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int x;
+  const float m = frexpf(amax, &x);
+  const int e = m <= 0.75f ? x - 3 : x - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// e2m1 code of v (|v| <= 6 after the block scaling): round to nearest, ties
+// to the even code, as the number of rounding thresholds |v| passes (> 0.25,
+// >= 0.75, > 1.25, >= 1.75, > 2.5, >= 3.5, > 5); sign bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return mag | (__builtin_signbit(v) ? 8u : 0u);
 }
 
 __device__ __forceinline__ int swz_key(int r) { return ((r >> 1) & 7) ^ (((r >> 2) ^ (r >> 3)) & 1); }
@@ -445,15 +474,16 @@ __device__ __forceinline__ void stage_token_scales_mx(uint8_t* SX, int KT, RowSf
 }
 
 // Dynamic LDS layout (the four token buffers [TM][128] are static arrays of
-// the main loop): the M tile's token scales (FP8: fp32 [KT][TSLOT]; MXFP8:
-// E8M0 [KT][4][16][4*TSW]), the run's weight block scales (FP8 only: fp32
+// the main loop): the M tile's token scales (FP8: fp32 [KT][TSLOT]; MX:
+// E8M0 [SPB*KT][4][16][4*TSW]), the run's weight block scales (FP8 only: fp32
 // [NB][KT][2]; MXFP8 weight scales stream from global memory with the
 // weights), the epilogue scratch (GEMM1: per-wave row max [8][TM]; GEMM2:
 // source row and top-k weight [2][TM]).
-template <int TM, bool MX>
+template <int TM, bool MX, bool FP4 = false>
 struct Lds {
+  // MX: SPB scale bytes per row, 32-K block group and K step (2 for e2m1)
   __host__ __device__ static constexpr size_t token_bytes(int KT) {
-    return MX ? 256 * (size_t)Cfg<TM>::TSW * KT : 4 * (size_t)Cfg<TM>::TSLOT * KT;
+    return MX ? 256 * (size_t)Cfg<TM>::TSW * (FP4 ? 2 : 1) * KT : 4 * (size_t)Cfg<TM>::TSLOT * KT;
   }
   __host__ __device__ static constexpr size_t weight_bytes(int KT, int NB) { return MX ? 0 : 8 * (size_t)NB * KT; }
   __host__ __device__ static constexpr size_t bytes(int KT, int NB) {
@@ -493,7 +523,7 @@ struct Lds {
 // steps 4m..4m+3 of an N tile) loads the dword of scale group m for the next
 // round, which becomes the current one when the round ends; step s of a
 // round selects byte s (op_sel of the A operand).
-template <int TM, bool GATED, bool PACKED, bool MX, typename WBand, typename Epi>
+template <int TM, bool GATED, bool PACKED, bool MX, bool FP4, typename WBand, typename Epi>
 __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& tb,
                                             const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
                                             __amdgpu_buffer_rsrc_t wrsrc, __amdgpu_buffer_rsrc_t srsrc, int kdim,
@@ -501,8 +531,14 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
                                             v4f (&acc)[Cfg<TM>::TS][2], WBand wband, Epi epi) {
   using C = Cfg<TM>;
   constexpr int TS = C::TS, D = C::D, APW = C::A_PER_WAVE, TSW = C::TSW;
-  const float* SAs = Lds<TM, MX>::token_scales(smem);
-  const float* SBs = Lds<TM, MX>::weight_scales(smem, KT);
+  // MX: MFMAs per operand pair and K step (= scale bytes per lane and step):
+  // an e2m1 step of 128 bytes is 256 K, two MFMAs on the halves of each
+  // 32-byte fragment (bytes {16g..} for K 0..127, {64+16g..} for 128..255)
+  constexpr int SPB = FP4 ? 2 : 1;
+  constexpr int FMT = FP4 ? 4 : 0;
+  static_assert(!FP4 || MX, "e2m1 operands carry E8M0 scales");
+  const float* SAs = Lds<TM, MX, FP4>::token_scales(smem);
+  const float* SBs = Lds<TM, MX, FP4>::weight_scales(smem, KT);
   const uint8_t* SXs = reinterpret_cast<const uint8_t*>(SAs);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const int S = nn * KT;
@@ -520,15 +556,15 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   };
 
   v8i wr[D][2];        // weight ring: slot s holds step j with j % D == s
-  uint32_t wsc[D][2];  // MXFP8, row-major scales: the lane's weight scale code of each ring slot
-  uint32_t wsg[2], wsg_next[2];   // MXFP8, MFMA-tiled scales: this round's and the next round's dwords
+  uint32_t wsc[D][2][SPB];  // MX, row-major scales: the lane's weight scale codes of each ring slot
+  uint32_t wsg[2][SPB], wsg_next[2][SPB];   // MX, MFMA-tiled scales: this round's and the next round's dwords
   constexpr bool MXT = MX && PACKED;
 
   const int wvoff = weight_lane_offset<PACKED>(lane, kdim);
-  // MXFP8: the lane's scale byte within a band's K step (row-major), or its
-  // dword within a band's scale group (MFMA-tiled)
-  const int svoff = MXT ? 4 * lane : r0 * (kdim >> 5) + g;
-  const int sgroup = mx_scale_groups(kdim / kKB) * 256;   // bytes per band of MFMA-tiled scales
+  // MX: the lane's scale byte within a band's K step (row-major), or its
+  // SPB dwords within a band's scale group (MFMA-tiled)
+  const int svoff = MXT ? 4 * SPB * lane : r0 * (SPB * kdim >> 5) + g;
+  const int sgroup = mx_scale_groups(kdim / kKB) * 256 * SPB;   // bytes per band of MFMA-tiled scales
   constexpr int kKStep = PACKED ? 2048 : kKB;   // bytes between K steps within a band
   int nw = 0, kw = 0;
   int wb[2], sb[2];
@@ -537,7 +573,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     for (int w = 0; w < 2; ++w) {
       const int row = wband(n, w);
       wb[w] = row * kdim;
-      sb[w] = MXT ? (row >> 4) * sgroup : row * (kdim >> 5);
+      sb[w] = MXT ? (row >> 4) * sgroup : row * (SPB * kdim >> 5);
     }
   };
   set_bands(0);
@@ -546,14 +582,25 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     for (int w = 0; w < 2; ++w) wr[s][w] = weight_frag<PACKED>(wrsrc, wvoff, wb[w] + kw * kKStep);
     if constexpr (MXT) {
       if (s == 0) {   // kw is the first step of a scale group here
+        const int goff = (kw / kMxScaleGroup) * 256 * SPB;
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
-          wsg_next[w] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, svoff, sb[w] + (kw / kMxScaleGroup) * 256, 0);
+        for (int w = 0; w < 2; ++w) {
+          if constexpr (SPB == 1) {
+            wsg_next[w][0] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, svoff, sb[w] + goff, 0);
+          } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(srsrc, svoff, sb[w] + goff, 0);
+            wsg_next[w][0] = v[0];
+            wsg_next[w][1] = v[1];
+          }
+        }
       }
     } else if constexpr (MX) {
-      // 4 blocks of 32 per K step
+      // 4 * SPB blocks of 32 per K step; the lane's are 4 apart
 #pragma unroll
-      for (int w = 0; w < 2; ++w) wsc[s][w] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, svoff, sb[w] + 4 * kw, 0);
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int hf = 0; hf < SPB; ++hf)
+          wsc[s][w][hf] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, svoff, sb[w] + 4 * (SPB * kw + hf), 0);
     }
     if (kw + 1 < KT) {
       ++kw;
@@ -584,11 +631,11 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   // other waves.  Vector memory operations complete in issue order for the
   // counter, and younger than those loads are that step's weight loads and
   // this step's APW + weight loads: step s issues WL(s) = 4 weight fragment
-  // loads, plus 2 scale bytes (MXFP8, row-major scales) or, at s == 0, 2 scale
-  // dwords (MXFP8, MFMA-tiled scales), so the wait at step s is
+  // loads, plus 2 * SPB scale bytes (MX, row-major scales) or, at s == 0, one
+  // scale load per band (MX, MFMA-tiled scales), so the wait at step s is
   // vmcnt(WL(s-1) + APW + WL(s)).  Every step issues all of them (the
   // producers never skip), so the count holds.
-  auto wl = [](int st) constexpr -> int { return 4 + (MXT ? (st == 0 ? 2 : 0) : (MX ? 2 : 0)); };
+  auto wl = [](int st) constexpr -> int { return 4 + (MXT ? (st == 0 ? 2 : 0) : (MX ? 2 * SPB : 0)); };
   auto publish_wait = [&](int s) __attribute__((always_inline)) {
     switch (s) {   // s is a constant of the unrolled round
       case 0: vmcnt_wait<wl(3) + APW + wl(0)>(); break;
@@ -602,12 +649,16 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   v8i af[3];
   float sa[TS];
   float sb0, sb1;
-  uint32_t sx[TSW];   // MXFP8 token scale codes
+  uint32_t sx[SPB][TSW];   // MX token scale codes (per MFMA of the step)
   auto read_scales = [&](int n, int k) __attribute__((always_inline)) {
     if constexpr (MX) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(SXs + ((4 * k + g) * 16 + r0) * 4 * TSW);
 #pragma unroll
-      for (int i = 0; i < TSW; ++i) sx[i] = p[i];
+      for (int hf = 0; hf < SPB; ++hf) {
+        const uint32_t* p =
+            reinterpret_cast<const uint32_t*>(SXs + ((4 * (SPB * k + hf) + g) * 16 + r0) * 4 * TSW);
+#pragma unroll
+        for (int i = 0; i < TSW; ++i) sx[hf][i] = p[i];
+      }
     } else {
       read_token_scales<TS>(SAs + (size_t)k * C::TSLOT + scale_slot<TS>(r0, 0), sa);
       const float* b = SBs + 2 * ((size_t)n * KT + k);
@@ -633,13 +684,26 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     dma_a((s + 3) & 3);        // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
     __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
     if constexpr (MX) {
-      const uint32_t ws0 = MXT ? wsg[0] : wsc[s][0], ws1 = MXT ? wsg[1] : wsc[s][1];
-      const int sela = MXT ? s : 0;
+      // the hf-th MFMA of the step takes the hf-th 16 bytes of each operand
+      // (the whole 32 bytes for e4m3) and scale byte SPB*s + hf of the round
+      auto half = [](const v8i& v, int hf) __attribute__((always_inline)) -> v8i {
+        if (hf == 0) return v;
+        return v8i{v[4], v[5], v[6], v[7], v[4], v[5], v[6], v[7]};
+      };
 #pragma unroll
       for (int ts = 0; ts < TS; ++ts) {
         if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
-        acc[ts][0] = mfma16x16x128_mx_sel(sela, ts & 3, wr[s][0], af[ts % 3], acc[ts][0], ws0, sx[ts >> 2]);
-        acc[ts][1] = mfma16x16x128_mx_sel(sela, ts & 3, wr[s][1], af[ts % 3], acc[ts][1], ws1, sx[ts >> 2]);
+#pragma unroll
+        for (int hf = 0; hf < SPB; ++hf) {
+          const int sb_i = SPB * s + hf;
+          const int sela = MXT ? sb_i % 4 : 0;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t ws = MXT ? wsg[w][sb_i / 4] : wsc[s][w][hf];
+            acc[ts][w] = mfma16x16x128_mx_sel<FMT>(sela, ts & 3, half(wr[s][w], hf), half(af[ts % 3], hf), acc[ts][w],
+                                                   ws, sx[hf][ts >> 2]);
+          }
+        }
       }
     } else {
       v4f pr[2][2];
@@ -669,8 +733,10 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   // MXFP8, MFMA-tiled scales: the next round's scale dwords become current
   auto next_round = [&]() __attribute__((always_inline)) {
     if constexpr (MXT) {
-      wsg[0] = wsg_next[0];
-      wsg[1] = wsg_next[1];
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int i = 0; i < SPB; ++i) wsg[w][i] = wsg_next[w][i];
     }
   };
   auto finish_tile = [&](int n) __attribute__((always_inline)) {
@@ -736,7 +802,9 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
 // are already in the padded row space (row p0 + r, no gather) and the
 // epilogue writes act in fp32 to plain_out [rows][I] for rows whose
 // sorted_src is valid, with no requantisation.
-template <int TM, bool PACKED, bool MX, bool PLAIN = false>
+// FP4 (MXFP4, e2m1 operands): rows of x and w13 are H/2 bytes, the
+// intermediate is requantised to 1x32 E8M0 + e2m1 (I/2 bytes per q row).
+template <int TM, bool PACKED, bool MX, bool PLAIN = false, bool FP4 = false>
 __device__ __forceinline__ void gemm1_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ x,
     const scale_t<MX>* __restrict__ x_scale, const uint8_t* __restrict__ w13,
@@ -751,8 +819,10 @@ __device__ __forceinline__ void gemm1_tile(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int KT = H / kKB, HB = H / kKB, IB = I / 128;
-  float* red = Lds<TM, MX>::scratch(smem, KT, NB);
+  constexpr int SPB = FP4 ? 2 : 1;
+  const int HR = H / SPB;                      // bytes per x / w13 row
+  const int KT = HR / kKB, HB = H / kKB, IB = I / 128;
+  float* red = Lds<TM, MX, FP4>::scratch(smem, KT, NB);
 
   // source of this lane's 16-byte chunk of each direct-to-LDS block: LDS
   // chunk qc holds row qc / 8, logical chunk (qc % 8) XOR the row's key
@@ -762,37 +832,38 @@ __device__ __forceinline__ void gemm1_tile(
     const int qc = C::block_of(tid >> 6, i) * 64 + lane;
     const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
     if constexpr (PLAIN) {
-      a_src[i] = x + (size_t)(tc.p0 + min(r, h - 1)) * H + c * 16;   // rows past the segment re-read its last
+      a_src[i] = x + (size_t)(tc.p0 + min(r, h - 1)) * HR + c * 16;   // rows past the segment re-read its last
     } else {
       const int src = r < h ? sorted_src[tc.p0 + r] : -1;
       const size_t tok = src >= 0 ? (size_t)(src / K) : 0;  // a pad row reads token 0; never stored
-      a_src[i] = x + tok * H + c * 16;
+      a_src[i] = x + tok * HR + c * 16;
     }
   }
   // wave w owns I columns [n0 + 16w, n0 + 16w + 16) of N tile n (n0 = 128 (nt0 + n)):
   // its two operands are those columns' gate rows and up rows
-  const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * H;
+  const uint8_t* wexp = w13 + (size_t)tc.e * (2 * (size_t)I) * HR;
   const __amdgpu_buffer_rsrc_t wrsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, 2 * I * H, kWeightRsrcFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, 2 * I * HR, kWeightRsrcFlags);
   auto wband = [&](int n, int w) -> int {
     const int c = 128 * (nt0 + n) + 16 * wave;   // first row of the 16-row band
     return w ? I + c : c;
   };
   __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
   if constexpr (MX) {
-    const int sbytes = mx_weight_scale_bytes<PACKED>(2 * I, H);
+    const int sbytes = mx_weight_scale_bytes<PACKED, SPB>(2 * I, HR);
     const uint8_t* sexp = w13_scale + (size_t)tc.e * sbytes;
     srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, sbytes, kWeightRsrcFlags);
-    stage_token_scales_mx<TM>(smem, KT, [&](int r) -> const uint8_t* {
+    // SPB dwords of codes per row and K step, staged as SPB * KT steps
+    stage_token_scales_mx<TM>(smem, SPB * KT, [&](int r) -> const uint8_t* {
       const int src = r < h ? sorted_src[tc.p0 + r] : -1;
       return src >= 0 ? x_scale + (size_t)(src / K) * (H / 32) : nullptr;
     }, x_scale, tid);
   } else {
     const float* sexp = w13_scale + (size_t)tc.e * (2 * IB) * HB;
-    stage_weight_scales(Lds<TM, MX>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
+    stage_weight_scales(Lds<TM, MX, FP4>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
       return sexp + (size_t)(which ? IB + nt0 + n : nt0 + n) * HB;
     }, tid);
-    stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
+    stage_token_scales<TM>(Lds<TM, MX, FP4>::token_scales(smem), KT, [&](int r) -> const float* {
       const int src = r < h ? sorted_src[tc.p0 + r] : -1;
       if constexpr (PLAIN) return src >= 0 ? x_scale + (size_t)(tc.p0 + r) * HB : nullptr;
       return src >= 0 ? x_scale + (size_t)(src / K) * HB : nullptr;
@@ -839,6 +910,17 @@ __device__ __forceinline__ void gemm1_tile(
       if (16 * ts >= h) break;   // sub-tiles past the segment (h is a multiple of 16)
       const int row = 16 * ts + l16;
       const size_t prow = (size_t)(tc.p0 + row);
+      if constexpr (FP4) {
+        const float amax = fmaxf(red[wave * TM + row], red[(wave ^ 1) * TM + row]);
+        const int e = e8m0_exponent_fp4(amax);
+        uint32_t v = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v |= e2m1_code(ldexpf(act[ts][r], -e)) << (4 * r);
+        // columns c0 + 4g .. +3: two bytes, the even column in the low nibble
+        *reinterpret_cast<uint16_t*>(q + prow * (I / 2) + (c0 + 4 * g) / 2) = (uint16_t)v;
+        if ((wave & 1) == 0 && g == 0) q_scale[prow * (I / 32) + c0 / 32] = (uint8_t)(e + 127);
+        continue;
+      }
       uint32_t* qd = reinterpret_cast<uint32_t*>(q + prow * I + c0 + 4 * g);
       if constexpr (MX) {
         const float amax = fmaxf(red[wave * TM + row], red[(wave ^ 1) * TM + row]);
@@ -863,7 +945,7 @@ __device__ __forceinline__ void gemm1_tile(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, true, PACKED, MX>(smem, tb, a_src, wrsrc, srsrc, H, 0, KT, nn, tid, lane, acc, wband, epi);
+  ws_mainloop<TM, true, PACKED, MX, FP4>(smem, tb, a_src, wrsrc, srsrc, HR, 0, KT, nn, tid, lane, acc, wband, epi);
 }
 
 // The token buffers are the kernel's; each workgroup runs the tile body of
@@ -890,7 +972,7 @@ __device__ __forceinline__ void gemm1_tile(
     default: if constexpr (TMAX >= 160) { BODY(160); } break;                      \
   }
 
-template <int TMAX, bool PACKED, bool MX>
+template <int TMAX, bool PACKED, bool MX, bool FP4 = false>
 __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
     const uint8_t* __restrict__ x, const scale_t<MX>* __restrict__ x_scale, const uint8_t* __restrict__ w13,
     const scale_t<MX>* __restrict__ w13_scale, const int32_t* __restrict__ padded,
@@ -902,7 +984,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
   if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
   FP8MOE_TOKEN_BUFFERS(TMAX);
 #define FP8MOE_G1_BODY(TMV) \
-  gemm1_tile<TMV, PACKED, MX>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB, q, q_scale)
+  gemm1_tile<TMV, PACKED, MX, false, FP4>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB, q, \
+                                          q_scale)
   FP8MOE_BODIES(FP8MOE_G1_BODY)
 #undef FP8MOE_G1_BODY
 }
@@ -914,7 +997,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
 // PLAIN (the plain grouped GEMM of the SM120 page's op): the epilogue
 // writes the fp32 accumulators to plain_out [rows][H] at the padded row
 // (rows whose sorted_src is valid), without the top-k weight.
-template <int TM, bool PACKED, bool MX, bool PLAIN = false>
+// FP4 (MXFP4): q and w2 rows are I/2 bytes of e2m1 codes.
+template <int TM, bool PACKED, bool MX, bool PLAIN = false, bool FP4 = false>
 __device__ __forceinline__ void gemm2_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ q,
     const scale_t<MX>* __restrict__ q_scale, const uint8_t* __restrict__ w2,
@@ -930,8 +1014,10 @@ __device__ __forceinline__ void gemm2_tile(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int KT = I / kKB, IB = I / kKB, HB = H / 128;
-  int* srow = reinterpret_cast<int*>(Lds<TM, MX>::scratch(smem, KT, NB));
+  constexpr int SPB = FP4 ? 2 : 1;
+  const int IR = I / SPB;                      // bytes per q / w2 row
+  const int KT = IR / kKB, IB = I / kKB, HB = H / 128;
+  int* srow = reinterpret_cast<int*>(Lds<TM, MX, FP4>::scratch(smem, KT, NB));
   float* wrow_w = reinterpret_cast<float*>(srow + TM);
 
   // token rows: q rows p0.. (a pad row holds whatever is there; its outputs are never stored)
@@ -940,12 +1026,12 @@ __device__ __forceinline__ void gemm2_tile(
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
     const int qc = C::block_of(tid >> 6, i) * 64 + lane;
     const int r = qc >> 3, c = (qc & 7) ^ swz_key(r);
-    a_src[i] = q + (size_t)(tc.p0 + min(r, h - 1)) * I + c * 16;
+    a_src[i] = q + (size_t)(tc.p0 + min(r, h - 1)) * IR + c * 16;
   }
   // wave w owns H columns [n0 + 32w, n0 + 32w + 32) of N tile n (n0 = 256 (nt0 + n)),
   // its two operands 16 columns each; rows past H read a valid row, outputs masked
-  const uint8_t* wexp = w2 + (size_t)tc.e * H * (size_t)I;
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, H * I,
+  const uint8_t* wexp = w2 + (size_t)tc.e * H * (size_t)IR;
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)wexp, (short)0, H * IR,
                                                                          kWeightRsrcFlags);
   auto wband = [&](int n, int w) -> int {
     // bands past H (the last N tile when H % 256 == 128) read the last band
@@ -953,10 +1039,10 @@ __device__ __forceinline__ void gemm2_tile(
   };
   __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
   if constexpr (MX) {
-    const int sbytes = mx_weight_scale_bytes<PACKED>(H, I);
+    const int sbytes = mx_weight_scale_bytes<PACKED, SPB>(H, IR);
     const uint8_t* sexp = w2_scale + (size_t)tc.e * sbytes;
     srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, sbytes, kWeightRsrcFlags);
-    stage_token_scales_mx<TM>(smem, KT, [&](int r) -> const uint8_t* {
+    stage_token_scales_mx<TM>(smem, SPB * KT, [&](int r) -> const uint8_t* {
       const int p = tc.p0 + r;
       return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * (I / 32) : nullptr;
     }, q_scale + (size_t)tc.p0 * (I / 32), tid);
@@ -964,11 +1050,11 @@ __device__ __forceinline__ void gemm2_tile(
     // N tile n spans scale blocks 2(nt0+n) and 2(nt0+n)+1 (the second clamped
     // at the last block; only columns < H are stored); waves 4..7 use the second
     const float* sexp = w2_scale + (size_t)tc.e * HB * IB;
-    stage_weight_scales(Lds<TM, MX>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
+    stage_weight_scales(Lds<TM, MX, FP4>::weight_scales(smem, KT), KT, nn, [&](int n, int which) -> const float* {
       const int nb = min(2 * (nt0 + n) + which, HB - 1);
       return sexp + (size_t)nb * IB;
     }, tid);
-    stage_token_scales<TM>(Lds<TM, MX>::token_scales(smem), KT, [&](int r) -> const float* {
+    stage_token_scales<TM>(Lds<TM, MX, FP4>::token_scales(smem), KT, [&](int r) -> const float* {
       const int p = tc.p0 + r;
       return r < h && sorted_src[p] >= 0 ? q_scale + (size_t)p * IB : nullptr;
     }, q_scale + (size_t)tc.p0 * IB, tid);
@@ -1017,11 +1103,11 @@ __device__ __forceinline__ void gemm2_tile(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, false, PACKED, MX>(smem, tb, a_src, wrsrc, srsrc, I, wave >> 2, KT, nn, tid, lane, acc, wband,
+  ws_mainloop<TM, false, PACKED, MX, FP4>(smem, tb, a_src, wrsrc, srsrc, IR, wave >> 2, KT, nn, tid, lane, acc, wband,
                                      epi);
 }
 
-template <int TMAX, bool PACKED, bool MX>
+template <int TMAX, bool PACKED, bool MX, bool FP4 = false>
 __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
     const uint8_t* __restrict__ q, const scale_t<MX>* __restrict__ q_scale, const uint8_t* __restrict__ w2,
     const scale_t<MX>* __restrict__ w2_scale, const float* __restrict__ topk_weights,
@@ -1033,7 +1119,8 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
   FP8MOE_TOKEN_BUFFERS(TMAX);
 #define FP8MOE_G2_BODY(TMV) \
-  gemm2_tile<TMV, PACKED, MX>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB, Y)
+  gemm2_tile<TMV, PACKED, MX, false, FP4>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, \
+                                          NB, Y)
   FP8MOE_BODIES(FP8MOE_G2_BODY)
 #undef FP8MOE_G2_BODY
 }
@@ -1089,15 +1176,15 @@ static inline int run_length(const GroupedRows& g, int tm, int NT, int KT) {
   return (int)((NT + ng - 1) / ng);
 }
 
-template <bool MX>
+template <bool MX, bool FP4 = false>
 static inline size_t gemm_lds_bytes(int tile_m, int KT, int NB) {
   switch (tile_m) {
-    case 16: return Lds<16, MX>::bytes(KT, NB);
-    case 32: return Lds<32, MX>::bytes(KT, NB);
-    case 64: return Lds<64, MX>::bytes(KT, NB);
-    case 128: return Lds<128, MX>::bytes(KT, NB);
-    case 144: return Lds<144, MX>::bytes(KT, NB);
-    default: return Lds<160, MX>::bytes(KT, NB);
+    case 16: return Lds<16, MX, FP4>::bytes(KT, NB);
+    case 32: return Lds<32, MX, FP4>::bytes(KT, NB);
+    case 64: return Lds<64, MX, FP4>::bytes(KT, NB);
+    case 128: return Lds<128, MX, FP4>::bytes(KT, NB);
+    case 144: return Lds<144, MX, FP4>::bytes(KT, NB);
+    default: return Lds<160, MX, FP4>::bytes(KT, NB);
   }
 }
 
@@ -1110,11 +1197,11 @@ static_assert(Cfg<128>::D == kRing && Cfg<160>::D == kRing, "one ring depth");
 
 // run_length, shortened until the run's weight scales fit in LDS; one N tile
 // per workgroup unless the K steps fill whole rounds of the weight ring
-template <bool MX>
+template <bool MX, bool FP4 = false>
 static inline int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
   if (KT % kRing != 0) return 1;
   int nb = run_length(g, tm, NT, KT);
-  while (nb > 1 && gemm_lds_bytes<MX>(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
+  while (nb > 1 && gemm_lds_bytes<MX, FP4>(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
   const int ng = (NT + nb - 1) / nb;
   return (NT + ng - 1) / ng;
 }
@@ -1134,31 +1221,33 @@ static hipError_t allow_lds(Kern k) {
   return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_dyn_lds(TMAX));
 }
 
-template <bool MX>
+// KT counts 128-byte K steps: H / 128 for e4m3, H / 256 for e2m1 (FP4)
+template <bool MX, bool FP4 = false>
 static hipError_t launch_gemm1_t(const uint8_t* x, const scale_t<MX>* x_scale, const uint8_t* w13,
                                  const scale_t<MX>* w13_scale, const GroupedRows& g, int H, int I, uint8_t* q,
                                  scale_t<MX>* q_scale, int tile_m, bool packed, hipStream_t stream) {
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
-#define FP8MOE_ATTR(TMV)                                                            \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, false, MX>); \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, true, MX>)
+#define FP8MOE_ATTR(TMV)                                                                 \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, false, MX, FP4>); \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_quant_kernel<TMV, true, MX, FP4>)
     FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128);
 #undef FP8MOE_ATTR
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (tile_m > kMaxTileGemm1) return hipErrorInvalidValue;
-  const int NT = I / 128, NB = fit_run<MX>(g, tile_m, NT, H / kKB), NG = (NT + NB - 1) / NB;
-  const size_t lds = gemm_lds_bytes<MX>(tile_m, H / kKB, NB);
+  const int KT = H / (FP4 ? 2 : 1) / kKB;
+  const int NT = I / 128, NB = fit_run<MX, FP4>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
+  const size_t lds = gemm_lds_bytes<MX, FP4>(tile_m, KT, NB);
   if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
 #define FP8MOE_G1(TMV)                                                                                     \
   if (packed)                                                                                              \
-    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, true, MX>), grid, block, lds, stream, x, x_scale, w13, \
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, true, MX, FP4>), grid, block, lds, stream, x, x_scale, w13, \
                        w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale);           \
   else                                                                                                     \
-    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, false, MX>), grid, block, lds, stream, x, x_scale, w13, \
+    hipLaunchKernelGGL((gemm1_swiglu_quant_kernel<TMV, false, MX, FP4>), grid, block, lds, stream, x, x_scale, w13, \
                        w13_scale, g.padded_indptr, g.sorted_src, g.E, g.K, H, I, NB, q, q_scale)
   switch (tile_m) {
     case 16: FP8MOE_G1(16); break;
@@ -1171,7 +1260,7 @@ static hipError_t launch_gemm1_t(const uint8_t* x, const scale_t<MX>* x_scale, c
   return hipGetLastError();
 }
 
-template <bool MX>
+template <bool MX, bool FP4 = false>
 static hipError_t launch_gemm2_t(const uint8_t* q, const scale_t<MX>* q_scale, const uint8_t* w2,
                                  const scale_t<MX>* w2_scale, const float* topk_weights, const GroupedRows& g,
                                  int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed,
@@ -1179,25 +1268,26 @@ static hipError_t launch_gemm2_t(const uint8_t* q, const scale_t<MX>* q_scale, c
   if (tile_n != kTN) return hipErrorInvalidValue;
   static const hipError_t attr = [] {
     hipError_t e = hipSuccess;
-#define FP8MOE_ATTR(TMV)                                                        \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, false, MX>); \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, true, MX>)
+#define FP8MOE_ATTR(TMV)                                                             \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, false, MX, FP4>); \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_kernel<TMV, true, MX, FP4>)
     FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144); FP8MOE_ATTR(160);
 #undef FP8MOE_ATTR
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (tile_m > kMaxTileGemm2) return hipErrorInvalidValue;
-  const int NT = (H + kTN - 1) / kTN, NB = fit_run<MX>(g, tile_m, NT, I / kKB), NG = (NT + NB - 1) / NB;
-  const size_t lds = gemm_lds_bytes<MX>(tile_m, I / kKB, NB);
+  const int KT = I / (FP4 ? 2 : 1) / kKB;
+  const int NT = (H + kTN - 1) / kTN, NB = fit_run<MX, FP4>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
+  const size_t lds = gemm_lds_bytes<MX, FP4>(tile_m, KT, NB);
   if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
   const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
 #define FP8MOE_G2(TMV)                                                                                        \
   if (packed)                                                                                                 \
-    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, true, MX>), grid, block, lds, stream, q, q_scale, w2,        \
+    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, true, MX, FP4>), grid, block, lds, stream, q, q_scale, w2,   \
                        w2_scale, topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y);              \
   else                                                                                                        \
-    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, false, MX>), grid, block, lds, stream, q, q_scale, w2,       \
+    hipLaunchKernelGGL((gemm2_weighted_kernel<TMV, false, MX, FP4>), grid, block, lds, stream, q, q_scale, w2,  \
                        w2_scale, topk_weights, g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y)
   switch (tile_m) {
     case 16: FP8MOE_G2(16); break;

@@ -59,6 +59,18 @@ hipError_t launch_gemm2_mx(const uint8_t* q, const uint8_t* q_sf, const uint8_t*
                            const float* topk_weights, const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m,
                            int tile_n, bool packed, hipStream_t stream);
 
+// MXFP4 (W4A4) variants: e2m1 codes two per byte (the even element in the low
+// nibble) with E8M0 scales per 32 K elements (x [T][H/2], x_sf [T][H/32],
+// w13 [E][2I][H/2], w13_sf [E][2I][H/32] or packed, q [cap][I/2], q_sf
+// [cap][I/32], w2 [E][H][I/2], w2_sf [E][H][I/32] or packed); H and I
+// multiples of 256.  GEMM1 requantises the intermediate to 1x32 E8M0 + e2m1.
+hipError_t launch_gemm1_mxfp4(const uint8_t* x, const uint8_t* x_sf, const uint8_t* w13, const uint8_t* w13_sf,
+                              const GroupedRows& g, int H, int I, uint8_t* q, uint8_t* q_sf, int tile_m, bool packed,
+                              hipStream_t stream);
+hipError_t launch_gemm2_mxfp4(const uint8_t* q, const uint8_t* q_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                              const float* topk_weights, const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m,
+                              int tile_n, bool packed, hipStream_t stream);
+
 // Plain grouped GEMM: out[p] = a[p] . b[e]^T (fp32) for every padded row p of
 // expert e with sorted_src[p] >= 0; gated: out[p, c] = silu(h[c]) * h[n/2 + c]
 // ([rows][n/2]).  tile_m in {16, 32, 64, 128}.
@@ -68,9 +80,11 @@ hipError_t launch_grouped_gemm_plain(const uint8_t* a, const float* a_scale, con
 
 // Row-major e4m3 [E][N][K] -> MFMA-tiled layout (N % 16 == 0, K % 128 == 0).
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);
-// Row-major E8M0 [E][N][K/32] -> MFMA-tiled MXFP8 scale layout of mx_scales_packed_bytes bytes.
-int64_t mx_scales_packed_bytes(int64_t E, int N, int K);
-hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream);
+// Row-major E8M0 [E][N][K/32] (K in elements) -> MFMA-tiled MX scale layout
+// of mx_scales_packed_bytes bytes; SPB = 1 for e4m3 weights, 2 for e2m1.
+int64_t mx_scales_packed_bytes(int64_t E, int N, int K, int SPB);
+hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t E, int N, int K, int SPB, uint8_t* out,
+                                 hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* Y, const int32_t* topk_ids, int T, int H, int E, int K,
                           uint16_t* out, hipStream_t stream);

@@ -44,22 +44,25 @@ hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int N, int K, uint8
   return hipGetLastError();
 }
 
-// MXFP8 weight scales (E8M0 codes, row-major [E][N][K/32]) -> the MFMA-tiled
-// scale layout the MXFP8 GEMMs read with one contiguous dword load per wave,
-// band and round of four K steps:
-//   out[e][b][m][l][j] = in[e][16b + l%16][4(4m + j) + l/16]
-// for 16-row band b, group m of K steps 4m..4m+3 (K steps of 128), lane l in
-// [0, 64) and byte j in [0, 4); bytes of steps past K/128 hold 127 (2^0).
-// Lane l's byte j is the scale of its MFMA operand row (l % 16) for the 32-K
-// block l / 16 of K step 4m + j.
+// MX weight scales (E8M0 codes, row-major [E][N][K/32]) -> the MFMA-tiled
+// scale layout the MX GEMMs read with one contiguous load per wave, band and
+// round of four 128-byte K steps.  SPB = MFMAs per operand pair and K step
+// (1 for e4m3 rows, whose 128-byte step is 128 K; 2 for e2m1 rows, 256 K):
+//   out[e][b][m][l][SPB*j + hf] = in[e][16b + l%16][4*SPB*(4m + j) + 4hf + l/16]
+// for 16-row band b, group m of K steps 4m..4m+3, lane l in [0, 64), step j
+// in [0, 4) and MFMA hf in [0, SPB); bytes of steps past the last hold 127
+// (2^0).  Lane l's byte is the scale of its MFMA operand row (l % 16) for the
+// 32-K block l / 16 of that MFMA.
 __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ in, int64_t E, int N, int K,
-                                                             uint32_t* __restrict__ out) {
-  const int KT = K / 128, G = (KT + 3) / 4, SB = K / 32;
+                                                             int SPB, uint32_t* __restrict__ out) {
+  const int KT = K / (128 * SPB), G = (KT + 3) / 4, SB = K / 32;
   const int64_t NB = N / 16;
-  const int64_t dwords = E * NB * G * 64;
+  const int64_t dwords = E * NB * G * 64 * SPB;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < dwords; c += stride) {
     int64_t t = c;
+    const int d = (int)(t % SPB);     // dword of the lane's SPB
+    t /= SPB;
     const int l = (int)(t & 63);
     t >>= 6;
     const int m = (int)(t % G);
@@ -69,23 +72,27 @@ __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __re
     const uint8_t* src = in + (e * N + 16 * b + (l & 15)) * SB + (l >> 4);
     uint32_t v = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < 4; ++i) {
+      const int byte = 4 * d + i, j = byte / SPB, hf = byte % SPB;
       const int k = 4 * m + j;
-      const uint32_t code = k < KT ? src[4 * k] : 127u;
-      v |= code << (8 * j);
+      const uint32_t code = k < KT ? src[4 * (SPB * k + hf)] : 127u;
+      v |= code << (8 * i);
     }
     out[c] = v;
   }
 }
 
-int64_t mx_scales_packed_bytes(int64_t E, int N, int K) { return E * (N / 16) * ((K / 128 + 3) / 4) * 256; }
+int64_t mx_scales_packed_bytes(int64_t E, int N, int K, int SPB) {
+  return E * (N / 16) * ((K / (128 * SPB) + 3) / 4) * 256 * SPB;
+}
 
-hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t E, int N, int K, uint8_t* out, hipStream_t stream) {
-  const int64_t dwords = mx_scales_packed_bytes(E, N, K) / 4;
+hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t E, int N, int K, int SPB, uint8_t* out,
+                                 hipStream_t stream) {
+  const int64_t dwords = mx_scales_packed_bytes(E, N, K, SPB) / 4;
   if (dwords == 0) return hipSuccess;
   int64_t blocks = (dwords + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(pack_mx_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, E, N, K,
+  hipLaunchKernelGGL(pack_mx_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, E, N, K, SPB,
                      reinterpret_cast<uint32_t*>(out));
   return hipGetLastError();
 }

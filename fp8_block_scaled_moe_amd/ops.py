@@ -203,11 +203,21 @@ def grouped_gemm_fp8(a, a_scale, b, b_scale, route, is_gated=False, tile_m=-1, w
     return out
 
 
-# ---------------------------------------------------------------- MXFP8 variant
+# ---------------------------------------------------------------- MX variants (MXFP8, MXFP4)
+#
+# Both take E8M0 scale codes (uint8, one per 32 contraction elements) on every
+# operand; MXFP4 operands are e2m1 codes two per byte (the even element in the
+# low nibble), so their code tensors have half the columns.
 
 def fused_mx_workspace_size(T, H, I, E, K):
     n = ctypes.c_size_t(0)
     check(lib().moe_fused_mxfp8_workspace_size(T, H, I, E, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def fused_mxfp4_workspace_size(T, H, I, E, K):
+    n = ctypes.c_size_t(0)
+    check(lib().moe_fused_mxfp4_workspace_size(T, H, I, E, K, ctypes.byref(n)))
     return int(n.value)
 
 
@@ -216,37 +226,50 @@ def alloc_workspace_mx(T, H, I, E, K, device):
     return torch.empty(fused_mx_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
 
 
-def pack_mx_scales(sf, out=None):
-    """MXFP8 weight scales, E8M0 codes [E, N, K/32] row-major -> the MFMA-tiled scale layout
-    (a flat uint8 tensor of moe_pack_mx_scales_bytes bytes; see moe_pack_mx_scales in
-    include/fp8moe.h).  Use with weights packed by pack_weights."""
+def alloc_workspace_mxfp4(T, H, I, E, K, device):
+    """A device workspace for moe_fused_mxfp4."""
+    return torch.empty(fused_mxfp4_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
+
+
+def _pack_scales(fn_bytes, fn, sf):
     sf = _u8(sf)
     _need(sf, torch.uint8, "sf", 3)
     E, N, KB = sf.shape
     K = KB * 32
-    n = lib().moe_pack_mx_scales_bytes(E, N, K)
+    n = fn_bytes(E, N, K)
     if n < 0:
         check(int(n))
-    if out is None:
-        out = torch.empty(int(n), dtype=torch.uint8, device=sf.device)
-    _need(out, torch.uint8, "out")
-    if out.numel() != n:
-        raise ValueError(f"out must hold {n} bytes")
-    check(lib().moe_pack_mx_scales(_p(sf), E, N, K, _p(out), _stream(sf.device)))
+    out = torch.empty(int(n), dtype=torch.uint8, device=sf.device)
+    check(fn(_p(sf), E, N, K, _p(out), _stream(sf.device)))
     return out
 
 
-def _mx_weight_scales_ok(sf, E, N, K, layout):
-    """Row-major scales are [E, N, K/32]; MFMA-tiled ones the flat output of pack_mx_scales."""
+def pack_mx_scales(sf):
+    """MXFP8 weight scales, E8M0 codes [E, N, K/32] row-major -> the MFMA-tiled scale layout
+    (a flat uint8 tensor of moe_pack_mx_scales_bytes bytes; see moe_pack_mx_scales in
+    include/fp8moe.h).  Use with weights packed by pack_weights."""
+    L = lib()
+    return _pack_scales(L.moe_pack_mx_scales_bytes, L.moe_pack_mx_scales, sf)
+
+
+def pack_mxfp4_scales(sf):
+    """MXFP4 weight scales, E8M0 codes [E, N, K/32] -> the MFMA-tiled scale layout of the
+    MXFP4 GEMMs (moe_pack_mxfp4_scales).  Use with codes packed by pack_weights."""
+    L = lib()
+    return _pack_scales(L.moe_pack_mxfp4_scales_bytes, L.moe_pack_mxfp4_scales, sf)
+
+
+def _mx_weight_scales_ok(sf, E, N, K, layout, fp4):
+    """Row-major scales are [E, N, K/32]; MFMA-tiled ones the flat output of the scale packer."""
     if layout == WEIGHTS_MFMA_TILED:
-        return sf.numel() == lib().moe_pack_mx_scales_bytes(E, N, K)
+        L = lib()
+        n = (L.moe_pack_mxfp4_scales_bytes if fp4 else L.moe_pack_mx_scales_bytes)(E, N, K)
+        return sf.numel() == n
     return tuple(sf.shape) == (E, N, K // 32)
 
 
-def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
-                    out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
-    """MXFP8 MoE layer (1x32 E8M0 scales on every operand; E8M0 codes as uint8).
-    x_sf [T, H/32], w13_sf [E, 2I, H/32], w2_sf [E, H, I/32].  Returns bf16 [T, H]."""
+def _fused_mx(fp4, x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, out, workspace, tile_m, tile_n,
+              weight_layout):
     x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
     x_sf, w13_sf, w2_sf = _u8(x_sf), _u8(w13_sf), _u8(w2_sf)
     _need(x, torch.uint8, "x", 2)
@@ -257,15 +280,16 @@ def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
     _need(w2_sf, torch.uint8, "w2_sf")
     _need(topk_ids, torch.int32, "topk_ids", 2)
     _need(topk_weights, torch.float32, "topk_weights", 2)
-    T, H = x.shape
-    E, I2, H2 = w13.shape
+    epb = 2 if fp4 else 1                      # elements per byte of the code tensors
+    T, H = x.shape[0], x.shape[1] * epb
+    E, I2 = w13.shape[0], w13.shape[1]
     I = I2 // 2
     K = topk_ids.shape[1]
-    if H2 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
+    if tuple(w13.shape) != (E, 2 * I, H // epb) or tuple(w2.shape) != (E, H, I // epb) or I2 != 2 * I:
         raise ValueError("inconsistent x / w13 / w2 shapes")
-    if tuple(x_sf.shape) != (T, H // 32) or not _mx_weight_scales_ok(w13_sf, E, 2 * I, H, weight_layout) \
-            or not _mx_weight_scales_ok(w2_sf, E, H, I, weight_layout):
-        raise ValueError("inconsistent E8M0 scale shapes (MFMA-tiled weights need pack_mx_scales scales)")
+    if tuple(x_sf.shape) != (T, H // 32) or not _mx_weight_scales_ok(w13_sf, E, 2 * I, H, weight_layout, fp4) \
+            or not _mx_weight_scales_ok(w2_sf, E, H, I, weight_layout, fp4):
+        raise ValueError("inconsistent E8M0 scale shapes (MFMA-tiled weights need packed scales)")
     if tuple(topk_ids.shape) != (T, K) or tuple(topk_weights.shape) != (T, K):
         raise ValueError("topk_ids / topk_weights must be [T, K]")
     dev = x.device
@@ -273,64 +297,103 @@ def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, torch.bfloat16, "out", 2)
     if workspace is None:
-        workspace = alloc_workspace_mx(T, H, I, E, K, dev)
-    check(lib().moe_fused_mxfp8(_p(x), _p(x_sf), _p(w13), _p(w13_sf), _p(w2), _p(w2_sf),
-                                _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
-                                workspace.numel() * workspace.element_size(), tile_m, tile_n, weight_layout,
-                                _stream(dev)))
+        workspace = (alloc_workspace_mxfp4 if fp4 else alloc_workspace_mx)(T, H, I, E, K, dev)
+    fn = lib().moe_fused_mxfp4 if fp4 else lib().moe_fused_mxfp8
+    check(fn(_p(x), _p(x_sf), _p(w13), _p(w13_sf), _p(w2), _p(w2_sf), _p(topk_ids), _p(topk_weights), T, H, I, E,
+             K, _p(out), _p(workspace), workspace.numel() * workspace.element_size(), tile_m, tile_n, weight_layout,
+             _stream(dev)))
     return out
+
+
+def moe_fused_mxfp8(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
+                    out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
+    """MXFP8 MoE layer (1x32 E8M0 scales on every operand; E8M0 codes as uint8).
+    x_sf [T, H/32], w13_sf [E, 2I, H/32], w2_sf [E, H, I/32].  Returns bf16 [T, H]."""
+    return _fused_mx(False, x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, out, workspace, tile_m,
+                     tile_n, weight_layout)
+
+
+def moe_fused_mxfp4(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights,
+                    out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
+    """MXFP4 (W4A4) MoE layer: x [T, H/2], w13 [E, 2I, H/2], w2 [E, H, I/2] packed e2m1 codes,
+    E8M0 scales as for MXFP8.  Returns bf16 [T, H]."""
+    return _fused_mx(True, x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, out, workspace, tile_m,
+                     tile_n, weight_layout)
+
+
+def _gemm1_mx(fp4, x, x_sf, w13, w13_sf, route, T, K, align, tile_m, weight_layout, q, q_sf):
+    x, w13, x_sf, w13_sf = _u8(x), _u8(w13), _u8(x_sf), _u8(w13_sf)
+    _need(x, torch.uint8, "x", 2)
+    _need(x_sf, torch.uint8, "x_sf", 2)
+    _need(w13, torch.uint8, "w13", 3)
+    _need(w13_sf, torch.uint8, "w13_sf")
+    epb = 2 if fp4 else 1
+    E, I2, H = w13.shape[0], w13.shape[1], w13.shape[2] * epb
+    I = I2 // 2
+    if tuple(x_sf.shape) != (x.shape[0], H // 32) or not _mx_weight_scales_ok(w13_sf, E, I2, H, weight_layout, fp4):
+        raise ValueError("inconsistent E8M0 scale shapes (MFMA-tiled weights need packed scales)")
+    cap = route["sorted_src"].numel()
+    dev = x.device
+    q = torch.zeros((cap, I // epb), dtype=torch.uint8, device=dev) if q is None else q
+    qs = torch.zeros((cap, I // 32), dtype=torch.uint8, device=dev) if q_sf is None else _u8(q_sf)
+    _need(q, torch.uint8, "q", 2)
+    _need(qs, torch.uint8, "q_sf", 2)
+    if tuple(q.shape) != (cap, I // epb) or tuple(qs.shape) != (cap, I // 32):
+        raise ValueError(f"q / q_sf must be [cap, {I // epb}] / [cap, I/32]")
+    fn = lib().moe_gemm1_swiglu_quant_mxfp4 if fp4 else lib().moe_gemm1_swiglu_quant_mx
+    check(fn(_p(x), _p(x_sf), _p(w13), _p(w13_sf), _p(route["padded_indptr"]), _p(route["sorted_src"]), T, H, I, E,
+             K, align, _p(q), _p(qs), cap, tile_m, weight_layout, _stream(dev)))
+    return q, qs
 
 
 def gemm1_swiglu_quant_mx(x, x_sf, w13, w13_sf, route, T, K, align, tile_m=-1,
                           weight_layout=WEIGHTS_ROW_MAJOR, q=None, q_sf=None):
     """MXFP8 GEMM1 + SwiGLU + 1x32 E8M0 requant stage.  Returns (q uint8 [cap, I], q_sf uint8
     [cap, I/32]); q / q_sf given: written in place (rows the stage does not write keep their contents)."""
-    x, w13, x_sf, w13_sf = _u8(x), _u8(w13), _u8(x_sf), _u8(w13_sf)
-    _need(x, torch.uint8, "x", 2)
-    _need(x_sf, torch.uint8, "x_sf", 2)
-    _need(w13, torch.uint8, "w13", 3)
-    _need(w13_sf, torch.uint8, "w13_sf")
-    E, I2, H = w13.shape
-    I = I2 // 2
-    if tuple(x_sf.shape) != (x.shape[0], H // 32) or not _mx_weight_scales_ok(w13_sf, E, I2, H, weight_layout):
-        raise ValueError("inconsistent E8M0 scale shapes (MFMA-tiled weights need pack_mx_scales scales)")
-    cap = route["sorted_src"].numel()
-    dev = x.device
-    q = torch.zeros((cap, I), dtype=torch.uint8, device=dev) if q is None else q
-    qs = torch.zeros((cap, I // 32), dtype=torch.uint8, device=dev) if q_sf is None else _u8(q_sf)
-    _need(q, torch.uint8, "q", 2)
-    _need(qs, torch.uint8, "q_sf", 2)
-    if tuple(q.shape) != (cap, I) or tuple(qs.shape) != (cap, I // 32):
-        raise ValueError("q / q_sf must be [cap, I] / [cap, I/32]")
-    check(lib().moe_gemm1_swiglu_quant_mx(_p(x), _p(x_sf), _p(w13), _p(w13_sf), _p(route["padded_indptr"]),
-                                          _p(route["sorted_src"]), T, H, I, E, K, align, _p(q), _p(qs), cap,
-                                          tile_m, weight_layout, _stream(dev)))
-    return q, qs
+    return _gemm1_mx(False, x, x_sf, w13, w13_sf, route, T, K, align, tile_m, weight_layout, q, q_sf)
 
 
-def gemm2_weighted_mx(q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
-                      weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
-    """MXFP8 GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H]; rows of dropped slots are not
-    written (zero when Y is allocated here)."""
+def gemm1_swiglu_quant_mxfp4(x, x_sf, w13, w13_sf, route, T, K, align, tile_m=-1,
+                             weight_layout=WEIGHTS_ROW_MAJOR, q=None, q_sf=None):
+    """MXFP4 GEMM1 + SwiGLU + 1x32 E8M0 / e2m1 requant stage.  Returns (q uint8 [cap, I/2],
+    q_sf uint8 [cap, I/32])."""
+    return _gemm1_mx(True, x, x_sf, w13, w13_sf, route, T, K, align, tile_m, weight_layout, q, q_sf)
+
+
+def _gemm2_mx(fp4, q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m, tile_n, weight_layout, Y):
     q, q_sf, w2, w2_sf = _u8(q), _u8(q_sf), _u8(w2), _u8(w2_sf)
     _need(q, torch.uint8, "q", 2)
     _need(q_sf, torch.uint8, "q_sf", 2)
     _need(w2, torch.uint8, "w2", 3)
     _need(w2_sf, torch.uint8, "w2_sf")
-    E, H, I = w2.shape
+    epb = 2 if fp4 else 1
+    E, H, I = w2.shape[0], w2.shape[1], w2.shape[2] * epb
     cap = route["sorted_src"].numel()
-    if tuple(q.shape) != (cap, I) or tuple(q_sf.shape) != (cap, I // 32) \
-            or not _mx_weight_scales_ok(w2_sf, E, H, I, weight_layout):
+    if tuple(q.shape) != (cap, I // epb) or tuple(q_sf.shape) != (cap, I // 32) \
+            or not _mx_weight_scales_ok(w2_sf, E, H, I, weight_layout, fp4):
         raise ValueError("inconsistent q / q_sf / w2_sf shapes")
     dev = q.device
     Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev) if Y is None else Y
     _need(Y, torch.bfloat16, "Y", 2)
     if tuple(Y.shape) != (T * K, H):
         raise ValueError("Y must be [T*K, H]")
-    check(lib().moe_gemm2_weighted_mx(_p(q), _p(q_sf), _p(w2), _p(w2_sf), _p(route["padded_indptr"]),
-                                      _p(route["sorted_src"]), _p(topk_weights), T, H, I, E, K, align, _p(Y),
-                                      cap, tile_m, tile_n, weight_layout, _stream(dev)))
+    fn = lib().moe_gemm2_weighted_mxfp4 if fp4 else lib().moe_gemm2_weighted_mx
+    check(fn(_p(q), _p(q_sf), _p(w2), _p(w2_sf), _p(route["padded_indptr"]), _p(route["sorted_src"]),
+             _p(topk_weights), T, H, I, E, K, align, _p(Y), cap, tile_m, tile_n, weight_layout, _stream(dev)))
     return Y
+
+
+def gemm2_weighted_mx(q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
+                      weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
+    """MXFP8 GEMM2 + routing-weight stage.  Returns Y bf16 [T*K, H]; rows of dropped slots are not
+    written (zero when Y is allocated here)."""
+    return _gemm2_mx(False, q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m, tile_n, weight_layout, Y)
+
+
+def gemm2_weighted_mxfp4(q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
+                         weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
+    """MXFP4 GEMM2 + routing-weight stage (q [cap, I/2] packed e2m1 codes)."""
+    return _gemm2_mx(True, q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m, tile_n, weight_layout, Y)
 
 
 def combine(Y, topk_ids, E):

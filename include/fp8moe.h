@@ -257,6 +257,47 @@ int moe_gemm2_weighted_mx(const void* q, const uint8_t* q_sf,
                           void* Y, int64_t cap, int32_t tile_m, int32_t tile_n,
                           int32_t weight_layout, void* stream);
 
+/* ---------------------------------------------------------------- MXFP4 (W4A4) variant of the layer and its stages
+ * The layer with MXFP4 operands: the cuTile page's W4A4 experts (NVFP4 on its
+ * hardware) in the OCP MXFP4 format that gfx950's block-scaled MFMA takes.
+ * Every operand is e2m1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3
+ * the sign), two per byte with the even element in the low nibble, and one
+ * E8M0 scale code per 32 consecutive contraction elements:
+ *   x      uint8 [T, H/2]       x_sf    uint8 [T, H/32]
+ *   w13    uint8 [E, 2I, H/2]   w13_sf  uint8 [E, 2I, H/32]  (gate rows first)
+ *   w2     uint8 [E, H, I/2]    w2_sf   uint8 [E, H, I/32]
+ * GEMM1 requantises the intermediate per row and 32 columns of I: e = the
+ * smallest exponent with amax <= 6 * 2^e (clamped to [-127, 127], -127 for
+ * an all-zero block), q = e2m1(act * 2^-e) rounded to nearest, ties to even:
+ *   q      uint8 [cap, I/2]     q_sf    uint8 [cap, I/32].
+ * Requires H % 256 == 0 and I % 256 == 0 (FP8MOE_ERR_ALIGN otherwise); all
+ * else as for the MXFP8 entry points.  With FP8MOE_WEIGHTS_MFMA_TILED the
+ * codes are packed by moe_pack_weights (as bytes: K = H/2 or I/2) and the
+ * scales by moe_pack_mxfp4_scales.
+ */
+int moe_fused_mxfp4_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                   size_t* bytes);
+int moe_fused_mxfp4(const void* x, const uint8_t* x_sf,
+                    const void* w13, const uint8_t* w13_sf,
+                    const void* w2, const uint8_t* w2_sf,
+                    const int32_t* topk_ids, const float* topk_weights,
+                    int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream);
+int moe_gemm1_swiglu_quant_mxfp4(const void* x, const uint8_t* x_sf,
+                                 const void* w13, const uint8_t* w13_sf,
+                                 const int32_t* padded_indptr, const int32_t* sorted_src,
+                                 int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                                 void* q, uint8_t* q_sf, int64_t cap,
+                                 int32_t tile_m, int32_t weight_layout, void* stream);
+int moe_gemm2_weighted_mxfp4(const void* q, const uint8_t* q_sf,
+                             const void* w2, const uint8_t* w2_sf,
+                             const int32_t* padded_indptr, const int32_t* sorted_src,
+                             const float* topk_weights,
+                             int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                             void* Y, int64_t cap, int32_t tile_m, int32_t tile_n,
+                             int32_t weight_layout, void* stream);
+
 /* ---------------------------------------------------------------- weight packing
  * moe_pack_weights: expert weights e4m3 [E, N, K] row-major (w13 with N = 2I,
  * K = H, or w2 with N = H, K = I) -> FP8MOE_WEIGHTS_MFMA_TILED, the layout
@@ -286,6 +327,16 @@ int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out,
  */
 int64_t moe_pack_mx_scales_bytes(int64_t E, int32_t N, int32_t K);
 int moe_pack_mx_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream);
+
+/* moe_pack_mxfp4_scales: the same for MXFP4 weights (K elements, K % 256 == 0;
+ * a 128-byte K step of e2m1 codes is 256 elements, two MFMAs of 128):
+ *   out[e][b][m][l][2j + hf] = in[e][16b + l%16][8(4m + j) + 4hf + l/16]
+ * for band b, group m of K steps 4m..4m+3 (of 256 elements), lane l, step j
+ * and MFMA hf in {0, 1}; 127 past the last step.  Size
+ * moe_pack_mxfp4_scales_bytes(E, N, K) = E * (N/16) * ceil(K/1024) * 512.
+ */
+int64_t moe_pack_mxfp4_scales_bytes(int64_t E, int32_t N, int32_t K);
+int moe_pack_mxfp4_scales(const uint8_t* in, int64_t E, int32_t N, int32_t K, void* out, void* stream);
 
 /* ---------------------------------------------------------------- gated activation + MXFP8
  * SwiGLU + MXFP8 quantisation (PR 8023 page, title and section 1):
