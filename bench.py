@@ -26,14 +26,17 @@ The line also carries:
   mxfp8         the MXFP8 variant of the layer (1x32 E8M0 scales on every
                 operand, intermediate requantised to 1x32 E8M0) on the same
                 prefill and decode shapes: us, TFLOP/s, GB/s and stage times.
+  mxfp4         the same for the MXFP4 (W4A4: e2m1 codes, 1x32 E8M0 scales)
+                variant, priced against the dense fp4 MFMA peak (10.1 PFLOP/s).
   cpu_baseline  the CPU oracle timed on a bounded sample of prefill tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                      [--no-extras] [--profile {prefill,decode,gated,mx}] [--traffic-kib F,W,SF,SW]
+                      [--no-extras] [--profile {prefill,decode,gated,mx,mxfp4}] [--traffic-kib F,W,SF,SW]
 
 --profile runs one workload only, for rocprofv3 passes: prefill (the layer,
 its stages and the 2 GiB stream kernel), decode (prefill, then the decode
-layer), gated (the gated-act sweep) or mx (the MXFP8 layer).  --traffic-kib takes GEMM1's
+layer), gated (the gated-act sweep), mx (the MXFP8 layer) or mxfp4 (the MXFP4
+layer).  --traffic-kib takes GEMM1's
 FETCH_SIZE and WRITE_SIZE per dispatch and the stream kernel's (KiB, as
 rocprofv3 --pmc reports them) and fills roofline.traffic from them instead of
 the readings recorded in TRAFFIC_COUNTERS.
@@ -65,12 +68,12 @@ METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roof
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "188433b8ef3f85b6d05724434f7f91451436d5cf54a939a245b8faa116bc1cf1",
-    "gemm1_fetch_kib": 5617300, "gemm1_write_kib": 157636,
+    "gemm_sources_sha256": "37ecebad71241c3e259cfca277a181e0283c9eb814eb36c65221538518c5550f",
+    "gemm1_fetch_kib": 5638232, "gemm1_write_kib": 157863,
     # GRBM_COUNT (FETCH_SIZE pass): GPU clock cycles per dispatch summed over
     # the 8 XCDs, and the dispatch's average duration under that pass
-    "gemm1_grbm_count": 36066440, "gemm1_grbm_dur_us": 2557.78,
-    "stream_fetch_kib": 1048589, "stream_write_kib": 2097152,
+    "gemm1_grbm_count": 35763830, "gemm1_grbm_dur_us": 2601.48,
+    "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm_kernels.h", "fp8_block_scaled_moe_amd/csrc/gemm1.hip",
                 "fp8_block_scaled_moe_amd/csrc/device_common.h", "fp8_block_scaled_moe_amd/csrc/launch.h")
@@ -94,6 +97,7 @@ def traffic_from(g1f, g1w, sf, sw):
             f"{write_scale:.4f} (scales: the 2 GiB stream kernel's known bytes / its counter readings)")
     return traffic, note
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published (2.4 GHz)
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 MFMA, published
 PEAK_CLOCK_GHZ = 2.4
 NUM_XCD = 8
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
@@ -302,9 +306,21 @@ def stage_times(p, steps, warmup):
     return out
 
 
-def mx_problem(T, cfg, weights, packed):
+MX_FORMATS = {
+    # name: (element bytes per value, tokens generator, weight-set generator, scale packer,
+    #        workspace allocator, fused layer, GEMM1 stage, GEMM2 stage, peak TFLOP/s, label)
+    "mxfp8": (1.0, synth.moe_tokens_mx, synth.expert_weight_set_mx, "pack_mx_scales", "alloc_workspace_mx",
+              "moe_fused_mxfp8", "gemm1_swiglu_quant_mx", "gemm2_weighted_mx", PEAK_FP8_TFLOPS,
+              "MXFP8 (e4m3, 1x32 E8M0) operands"),
+    "mxfp4": (0.5, synth.moe_tokens_mxfp4, synth.expert_weight_set_mxfp4, "pack_mxfp4_scales",
+              "alloc_workspace_mxfp4", "moe_fused_mxfp4", "gemm1_swiglu_quant_mxfp4", "gemm2_weighted_mxfp4",
+              PEAK_FP4_TFLOPS, "MXFP4 (e2m1, 1x32 E8M0) operands"),
+}
+
+
+def mx_problem(tokens_fn, T, cfg, weights, packed):
     d = synth.LARGE_DIMS
-    x_q, x_sf, ids, w = synth.moe_tokens_mx(T, d["H"], d["E"], d["K"], cfg)
+    x_q, x_sf, ids, w = tokens_fn(T, d["H"], d["E"], d["K"], cfg)
     w13_q, w13_sf, w2_q, w2_sf = weights
     p = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_sf.cuda(), w13_q, w13_sf, w2_q, w2_sf,
                         ids.cuda(), w.cuda())
@@ -312,54 +328,60 @@ def mx_problem(T, cfg, weights, packed):
     return p
 
 
-def mx_algorithmic_bytes(p):
-    """As algorithmic_bytes, with one E8M0 byte per 32 elements for every scale."""
+def mx_algorithmic_bytes(p, elem_bytes):
+    """As algorithmic_bytes, with elem_bytes per weight and token element and one E8M0 byte
+    per 32 elements for every scale."""
     ids = p.topk_ids.cpu().numpy()
     active = np.unique(ids[(ids >= 0) & (ids < p.E)]).size
     H, I = p.H, p.I
-    per_expert = 3 * H * I + 3 * H * I // 32
-    io = p.T * H + p.T * (H // 32) + 8 * p.T * p.K + 2 * p.T * H
+    per_expert = int(3 * H * I * elem_bytes) + 3 * H * I // 32
+    io = int(p.T * H * elem_bytes) + p.T * (H // 32) + 8 * p.T * p.K + 2 * p.T * H
     return active * per_expert + io, active
 
 
-def mx_bench(steps, warmup):
-    """The MXFP8 layer on the prefill and decode shapes (packed weights, auto tiles)."""
+def mx_bench(fmt, steps, warmup):
+    """An MX variant of the layer on the prefill and decode shapes (packed weights and scales,
+    auto tiles)."""
+    eb, tokens_fn, weights_fn, pack_sf, alloc_ws, fused_fn, g1_fn, g2_fn, peak, label = MX_FORMATS[fmt]
+    pack_sf, alloc_ws = getattr(fm, pack_sf), getattr(fm, alloc_ws)
+    fused_fn, g1_fn, g2_fn = getattr(fm, fused_fn), getattr(fm, g1_fn), getattr(fm, g2_fn)
     d = synth.LARGE_DIMS
-    log("generating 256-expert MXFP8 weights on the device")
-    w13 = synth.expert_weight_set_mx(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
-    w2 = synth.expert_weight_set_mx(d["E"], d["H"], d["I"], synth.CFG_LARGE, synth.TAG_W2, "cuda")
-    # the production layouts: e4m3 weights and their E8M0 scales packed once per weight set
-    packed = (fm.pack_weights(w13[0]), fm.pack_mx_scales(w13[1]), fm.pack_weights(w2[0]), fm.pack_mx_scales(w2[1]))
+    log(f"generating 256-expert {fmt} weights on the device")
+    w13 = weights_fn(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
+    w2 = weights_fn(d["E"], d["H"], d["I"], synth.CFG_LARGE, synth.TAG_W2, "cuda")
+    # the production layouts: weight codes and their E8M0 scales packed once per weight set
+    packed = (fm.pack_weights(w13[0]), pack_sf(w13[1]), fm.pack_weights(w2[0]), pack_sf(w2[1]))
     weights = (*w13, *w2)
     res = {}
     for name, T, cfg in (("prefill", 8192, synth.CFG_PREFILL), ("decode", 64, synth.CFG_LARGE)):
-        p = mx_problem(T, cfg, weights, packed)
-        ws = fm.alloc_workspace_mx(p.T, p.H, p.I, p.E, p.K, "cuda")
+        p = mx_problem(tokens_fn, T, cfg, weights, packed)
+        ws = alloc_ws(p.T, p.H, p.I, p.E, p.K, "cuda")
         out = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
         L = fm.WEIGHTS_MFMA_TILED
-        ms = event_time_ms(lambda: fm.moe_fused_mxfp8(p.x_q, p.x_s, p.w13_p, p.w13_sp, p.w2_p, p.w2_sp, p.topk_ids,
-                                                      p.topk_weights, out=out, workspace=ws, weight_layout=L),
+        ms = event_time_ms(lambda: fused_fn(p.x_q, p.x_s, p.w13_p, p.w13_sp, p.w2_p, p.w2_sp, p.topk_ids,
+                                            p.topk_weights, out=out, workspace=ws, weight_layout=L),
                            steps if name == "prefill" else max(steps, 10), warmup)
         align = 16
         route = fm.route_permute(p.topk_ids, p.E, align)
-        q, qs = fm.gemm1_swiglu_quant_mx(p.x_q, p.x_s, p.w13_p, p.w13_sp, route, p.T, p.K, align, weight_layout=L)
-        Y = fm.gemm2_weighted_mx(q, qs, p.w2_p, p.w2_sp, route, p.topk_weights, p.T, p.K, align, weight_layout=L)
+        q, qs = g1_fn(p.x_q, p.x_s, p.w13_p, p.w13_sp, route, p.T, p.K, align, weight_layout=L)
+        Y = g2_fn(q, qs, p.w2_p, p.w2_sp, route, p.topk_weights, p.T, p.K, align, weight_layout=L)
         n = max(3, steps // 2)
-        g1 = event_time_ms(lambda: fm.gemm1_swiglu_quant_mx(p.x_q, p.x_s, p.w13_p, p.w13_sp, route, p.T, p.K, align,
-                                                            weight_layout=L, q=q, q_sf=qs), n, 1)
-        g2 = event_time_ms(lambda: fm.gemm2_weighted_mx(q, qs, p.w2_p, p.w2_sp, route, p.topk_weights, p.T, p.K,
-                                                        align, weight_layout=L, Y=Y), n, 1)
-        nbytes, active = mx_algorithmic_bytes(p)
+        g1 = event_time_ms(lambda: g1_fn(p.x_q, p.x_s, p.w13_p, p.w13_sp, route, p.T, p.K, align,
+                                         weight_layout=L, q=q, q_sf=qs), n, 1)
+        g2 = event_time_ms(lambda: g2_fn(q, qs, p.w2_p, p.w2_sp, route, p.topk_weights, p.T, p.K,
+                                         align, weight_layout=L, Y=Y), n, 1)
+        nbytes, active = mx_algorithmic_bytes(p, eb)
         flops = layer_flops(p)
         g1_tflops = 4.0 * p.T * p.K * p.H * p.I / (g1 * 1e-3) / 1e12
         res[name] = {"us_per_layer": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
                      "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                     "peak_TFLOPs": peak,
+                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
                      "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4), "gemm1_TFLOPs": round(g1_tflops, 1),
                      "algorithmic_bytes": int(nbytes), "active_experts": int(active),
-                     "workload": f"{name} T={T} H=7168 I=2048 E=256 top-8, MXFP8 (1x32 E8M0) operands"}
-        log(f"mxfp8 {name}", res[name])
+                     "workload": f"{name} T={T} H=7168 I=2048 E=256 top-8, {label}"}
+        log(f"{fmt} {name}", res[name])
         del ws, out, q, qs, Y
     del packed, w13, w2
     torch.cuda.empty_cache()
@@ -396,9 +418,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the gated-act and skewed sweeps")
-    ap.add_argument("--profile", choices=("prefill", "decode", "gated", "mx"), default=None,
+    ap.add_argument("--profile", choices=("prefill", "decode", "gated", "mx", "mxfp4"), default=None,
                     help="one workload only, for rocprofv3 passes: prefill (+ stages, stream kernel), "
-                         "decode (+ stages) or gated (the gated-act sweep)")
+                         "decode (+ stages), gated (the gated-act sweep), mx (the MXFP8 layer) or "
+                         "mxfp4 (the MXFP4 layer)")
     ap.add_argument("--traffic-kib", default=None,
                     help="gemm1_fetch,gemm1_write,stream_fetch,stream_write (KiB per dispatch, rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -410,8 +433,9 @@ def main():
     if args.profile == "gated":
         print(json.dumps({"profile": "gated", "gated_act": gated_act_bench(iters=5)}), flush=True)
         return
-    if args.profile == "mx":
-        print(json.dumps({"profile": "mx", "mxfp8": mx_bench(args.steps, args.warmup)}), flush=True)
+    if args.profile in ("mx", "mxfp4"):
+        fmt = "mxfp8" if args.profile == "mx" else "mxfp4"
+        print(json.dumps({"profile": args.profile, fmt: mx_bench(fmt, args.steps, args.warmup)}), flush=True)
         return
     d = synth.LARGE_DIMS
     log("generating 256-expert fp8 weights on the device")
@@ -527,8 +551,9 @@ def main():
         result["gated_act"] = gated_act_bench()
         log("skewed-routing sweep")
         result["skewed"] = skewed_bench()
-        log("MXFP8 layer")
-        result["mxfp8"] = mx_bench(max(3, args.steps // 2), 1)
+        for fmt in ("mxfp8", "mxfp4"):
+            log(f"{fmt} layer")
+            result[fmt] = mx_bench(fmt, max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = cpu_baseline(pre)

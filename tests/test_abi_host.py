@@ -64,12 +64,13 @@ def test_route_permute_validation():
     assert "top-k" in lib().moe_last_error().decode() or lib().moe_last_error().decode()
 
 
-FUSED = ("moe_fused_fp8", "moe_fused_mxfp8")
+# entry point and the smallest valid intermediate size (MXFP4 needs H and I multiples of 256)
+FUSED = (("moe_fused_fp8", 128), ("moe_fused_mxfp8", 128), ("moe_fused_mxfp4", 256))
 
 
-@pytest.mark.parametrize("fn", FUSED)
-def test_fused_validation(fn):
-    def _fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE, layout=0):
+@pytest.mark.parametrize("fn,I0", FUSED)
+def test_fused_validation(fn, I0):
+    def _fused(T=16, H=256, I=I0, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE, layout=0):
         return getattr(lib(), fn)(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn,
                                   layout, NULL)
     assert _fused(T=-1) == E_SHAPE
@@ -93,6 +94,12 @@ def test_fused_validation(fn):
     # T == 0: nothing to do, no launch, null pointers allowed
     assert _fused(T=0, ptr=NULL, ws=NULL, out=NULL) == OK
     assert lib().moe_last_error().decode() == ""
+    if fn == "moe_fused_mxfp4":
+        # one 128-byte K step of e2m1 codes is 256 elements
+        assert _fused(I=128) == E_ALIGN
+        assert _fused(H=384) == E_ALIGN
+        assert "256" in lib().moe_last_error().decode()
+        assert _fused(T=0, H=384, ptr=NULL, ws=NULL, out=NULL) == E_ALIGN
 
 
 @pytest.mark.parametrize("size", [fm.fused_workspace_size, fm.fused_mx_workspace_size])
@@ -107,23 +114,41 @@ def test_workspace_size(size):
         size(16, 100, 128, 4, 2)
 
 
-@pytest.mark.parametrize("mx", [False, True])
-def test_stage_validation(mx):
+def test_workspace_size_mxfp4():
+    n4 = fm.fused_mxfp4_workspace_size(16, 256, 256, 4, 2)
+    n8 = fm.fused_mx_workspace_size(16, 256, 256, 4, 2)
+    R, cap = 32, 32 + 4 * 127
+    # q holds I/2 bytes a row (two e2m1 codes a byte), its scales I/32; Y and sorted_src as for MXFP8
+    assert n4 >= cap * 128 + cap * 8 + R * 256 * 2 + cap * 4
+    assert n4 < n8
+    assert fm.fused_mxfp4_workspace_size(8192, 7168, 2048, 256, 8) < 2 ** 31
+    with pytest.raises(fm.Fp8MoeError):
+        fm.fused_mxfp4_workspace_size(16, 256, 128, 4, 2)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
+def test_stage_validation(fmt):
     L = lib()
-    f1 = L.moe_gemm1_swiglu_quant_mx if mx else L.moe_gemm1_swiglu_quant
-    f2 = L.moe_gemm2_weighted_mx if mx else L.moe_gemm2_weighted
-    g1 = lambda **k: f1(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("T", 16), 256, 128, 4, 2, k.get("align", 16),
-                        FAKE, FAKE, k.get("cap", 100), k.get("tm", -1), k.get("layout", 0), NULL)
+    suffix = {"fp8": "", "mxfp8": "_mx", "mxfp4": "_mxfp4"}[fmt]
+    f1 = getattr(L, "moe_gemm1_swiglu_quant" + suffix)
+    f2 = getattr(L, "moe_gemm2_weighted" + suffix)
+    I = 256 if fmt == "mxfp4" else 128
+    g1 = lambda **k: f1(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("T", 16), 256, k.get("I", I), 4, 2,
+                        k.get("align", 16), FAKE, FAKE, k.get("cap", 100), k.get("tm", -1), k.get("layout", 0),
+                        NULL)
     assert g1(align=24) == E_ALIGN
     assert g1(align=16, tm=48) == E_TILE          # tile heights 16/32/64/128/144/160 only
     assert g1(cap=-1) == E_SHAPE
     assert g1(T=0) == OK
     assert g1(layout=3) == E_SHAPE
-    g2 = lambda **k: f2(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 256, 128, 4, 2, k.get("align", 16), FAKE,
-                        100, k.get("tm", -1), k.get("tn", -1), k.get("layout", 0), NULL)
+    g2 = lambda **k: f2(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, k.get("H", 256), I, 4, 2, k.get("align", 16),
+                        FAKE, 100, k.get("tm", -1), k.get("tn", -1), k.get("layout", 0), NULL)
     assert g2(tn=64) == E_TILE
     assert g2(align=32, tm=96) == E_TILE
     assert g2(layout=2) == E_SHAPE
+    if fmt == "mxfp4":
+        assert g1(I=128) == E_ALIGN
+        assert g2(H=384) == E_ALIGN
     assert L.moe_combine(FAKE, FAKE, 4, 100, 4, 2, FAKE, NULL) == E_ALIGN
     assert L.moe_combine(FAKE, FAKE, 4, 128, 4, 9, FAKE, NULL) == E_TOPK
     assert L.moe_combine(NULL, FAKE, 4, 128, 4, 2, FAKE, NULL) == E_NULL
@@ -140,6 +165,19 @@ def test_pack_mx_scales_validation():
     assert L.moe_pack_mx_scales(FAKE, 0, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE
     assert L.moe_pack_mx_scales(NULL, 1, 32, 128, ctypes.c_void_p(1 << 40), NULL) == E_NULL
     assert L.moe_pack_mx_scales(FAKE, 1, 32, 128, FAKE, NULL) == E_SHAPE       # overlapping in / out
+
+
+def test_pack_mxfp4_scales_validation():
+    L = lib()
+    # no padding when the K steps (256 elements each) fill whole groups of 4: one byte per 32 elements
+    assert L.moe_pack_mxfp4_scales_bytes(256, 4096, 7168) == 256 * 4096 * 7168 // 32
+    assert L.moe_pack_mxfp4_scales_bytes(2, 32, 768) == 2 * 2 * 1 * 512        # 3 K steps -> one group of 4
+    assert L.moe_pack_mxfp4_scales_bytes(2, 32, 1280) == 2 * 2 * 2 * 512
+    assert L.moe_pack_mxfp4_scales_bytes(2, 32, 384) == E_SHAPE                # K % 256 != 0
+    assert L.moe_pack_mxfp4_scales_bytes(2, 24, 512) == E_SHAPE
+    assert L.moe_pack_mxfp4_scales(FAKE, 0, 32, 256, ctypes.c_void_p(1 << 40), NULL) == E_SHAPE
+    assert L.moe_pack_mxfp4_scales(NULL, 1, 32, 256, ctypes.c_void_p(1 << 40), NULL) == E_NULL
+    assert L.moe_pack_mxfp4_scales(FAKE, 1, 32, 256, FAKE, NULL) == E_SHAPE     # overlapping in / out
 
 
 def test_grouped_gemm_validation():
