@@ -27,9 +27,9 @@ Inputs (numpy, or anything indexable by expert for the weights):
   topk_weights f32  [T, K]
 
 moe_reference_mx is the MXFP8 variant (1x32 E8M0 scales on every operand,
-the intermediate requantised in the gated-act kernel's format) and
-moe_reference_mxfp4 the MXFP4 (W4A4) one; their readings are listed above
-their definitions.
+the intermediate requantised in the gated-act kernel's format),
+moe_reference_mxfp4 the MXFP4 (W4A4) one and moe_reference_bf16 the
+unquantised bf16 one; their readings are listed above their definitions.
 """
 
 import numpy as np
@@ -210,3 +210,40 @@ def moe_reference_mxfp4(x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_we
     [E][2I, H/32]; w2_q [E][H, I/2], w2_sf [E][H, I/32]."""
     return _layer(expert_ffn_mxfp4, x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
                   tokens, return_stages, H=2 * np.asarray(x_q).shape[1])
+
+
+# ---------------------------------------------------------------- bf16 experts
+#
+# The cuTile page lists unquantised bf16 MoE configurations beside the FP8 and
+# FP4 ones (its unified-API section) without fixing their arithmetic.
+# Readings taken here:
+#   * x [T, H], w13 [E][2I, H] and w2 [E][H, I] are bfloat16, given as their
+#     uint16 bit patterns, with no scales;
+#   * both GEMMs and SwiGLU run in float64; the activation is rounded once to
+#     float32 and then to bfloat16 (round to nearest, ties to even): the
+#     intermediate between the GEMMs is bf16, as the layer's input and output;
+#   * routing, the combine and the output rounding are those of the FP8 layer.
+
+def expert_ffn_bf16(x_rows, _xs_rows, w13, _w13_s, w2, _w2_s, stages=None):
+    """One expert on its gathered rows, bf16 operands (uint16 bit patterns)."""
+    A = formats.bf16_decode(x_rows)                                  # [n, H]
+    W13 = formats.bf16_decode(np.asarray(w13))                       # [2I, H]
+    I = W13.shape[0] // 2
+    H1 = A @ W13.T                                                   # GEMM1, [n, 2I]
+    g, u = H1[:, :I], H1[:, I:]
+    act = silu_mul(g, u).astype(np.float32)                          # SwiGLU, one fp32 rounding
+    q = formats.bf16_bits(act)                                       # bf16 intermediate
+    W2 = formats.bf16_decode(np.asarray(w2))                         # [H, I]
+    Y = formats.bf16_decode(q) @ W2.T                                # GEMM2, [n, H]
+    if stages is not None:
+        stages.update(H1=H1, act=act, q=q, Y=Y)
+    return Y
+
+
+def moe_reference_bf16(x, w13, w2, topk_ids, topk_weights, tokens=None, return_stages=False):
+    """Reference bf16 MoE layer: x uint16 [T, H], w13 [E][2I, H], w2 [E][H, I] bf16 bit
+    patterns; results as moe_reference."""
+    T = np.asarray(x).shape[0]
+    no_scales = [None] * len(w13)
+    return _layer(expert_ffn_bf16, x, np.zeros((T, 0), np.float32), w13, no_scales, w2, no_scales, topk_ids,
+                  topk_weights, tokens, return_stages)

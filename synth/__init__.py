@@ -7,7 +7,9 @@ harness quantisation of those fp32 values into the fp8 e4m3 codes plus fp32
 block scales that the expert path takes as input (1x128 for activations,
 128x128 for weights; scale = amax/448, codes from torch's own float8_e4m3fn
 cast after clamping to +-448; or, for the MXFP8 variant, 1x32 blocks along
-the contraction dimension with power-of-two E8M0 scales).  None of the expert computation (GEMMs,
+the contraction dimension with power-of-two E8M0 scales; or e2m1 codes with
+E8M0 scales for MXFP4; or torch's bf16 cast for the unquantised variant).
+None of the expert computation (GEMMs,
 SwiGLU, requantisation, combine) is here.
 
 Seeds: numpy streams come from SeedSequence([cfg, tag, idx, *extra]); torch
@@ -212,7 +214,7 @@ class MoEInputs:
         self.topk_ids, self.topk_weights = topk_ids, topk_weights
 
     def to(self, device):
-        f = lambda t: t.to(device)
+        f = lambda t: None if t is None else t.to(device)
         return MoEInputs(self.T, self.H, self.I, self.E, self.K, f(self.x_q), f(self.x_s),
                          f(self.w13_q), f(self.w13_s), f(self.w2_q), f(self.w2_s),
                          f(self.topk_ids), f(self.topk_weights))
@@ -287,6 +289,47 @@ def moe_problem_mxfp4(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", w
     w2_q, w2_sf = expert_weight_set_mxfp4(E, H, I, wc, TAG_W2, wd)
     return MoEInputs(T, H, I, E, K, x_q, x_sf, w13_q.to(device), w13_sf.to(device),
                      w2_q.to(device), w2_sf.to(device), ids, w)
+
+
+def expert_weight_set_bf16(E, N, K, cfg, tag, device="cpu", std=0.02):
+    """The same fp32 weights as expert_weight_set, rounded to bfloat16 by torch's cast
+    (nearest, ties to even): bf16 [E, N, K]."""
+    q = torch.empty((E, N, K), dtype=torch.bfloat16, device=device)
+    dev = torch.device(device)
+    for e in range(E):
+        if dev.type == "cpu":
+            w = torch.from_numpy(expert_weights_fp32(E, N, K, cfg, tag, e, std))
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(torch_seed(cfg, tag, e))
+            w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * std
+        q[e].copy_(w.to(torch.bfloat16))
+    return q
+
+
+def moe_tokens_bf16(T, H, E, K, cfg, extra=(), zipf_s=None, device="cpu"):
+    """Token-side bf16 inputs (same activations and routing as moe_tokens):
+    (x bf16 [T, H], topk_ids, topk_weights)."""
+    ids, w = router(T, E, K, cfg, extra, zipf_s)
+    x = torch.from_numpy(activations(T, H, cfg, extra)).to(torch.bfloat16)
+    return x.to(device), torch.from_numpy(ids).to(device), torch.from_numpy(w).to(device)
+
+
+def moe_problem_bf16(T, H, I, E, K, cfg, extra=(), zipf_s=None, device="cpu", weight_cfg=None,
+                     weight_device=None):
+    """moe_problem with unquantised bf16 operands: x_q, w13_q and w2_q hold bf16 tensors and
+    the scale fields are None."""
+    wc = cfg if weight_cfg is None else weight_cfg
+    wd = device if weight_device is None else weight_device
+    x, ids, w = moe_tokens_bf16(T, H, E, K, cfg, extra, zipf_s, device)
+    w13 = expert_weight_set_bf16(E, 2 * I, H, wc, TAG_W13, wd)
+    w2 = expert_weight_set_bf16(E, H, I, wc, TAG_W2, wd)
+    return MoEInputs(T, H, I, E, K, x, None, w13.to(device), None, w2.to(device), None, ids, w)
+
+
+def bf16_bits(t):
+    """A bf16 torch tensor -> its uint16 bit patterns as a numpy array (host copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
 # MXFP4 needs H and I to be multiples of 256 (one 128-byte row step is 256 e2m1
