@@ -1,4 +1,4 @@
-"""MI355X (gfx950) W8A8 FP8 block-scaled MoE expert path (and its MXFP8 and MXFP4 variants).
+"""MI355X (gfx950) W8A8 FP8 block-scaled MoE expert path (and its MXFP8, MXFP4 and bf16 variants).
 
 The computation lives in libfp8moe.so (hand-written HIP kernels behind the C
 ABI of include/fp8moe.h); this package only loads it and marshals torch
@@ -13,4 +13,5 @@ from .ops import (  # noqa: F401
     fused_mx_workspace_size, alloc_workspace_mx, moe_fused_mxfp8, pack_mx_scales, grouped_gemm_fp8,
     fused_mxfp4_workspace_size, alloc_workspace_mxfp4, moe_fused_mxfp4, pack_mxfp4_scales,
     gemm1_swiglu_quant_mxfp4, gemm2_weighted_mxfp4, gemm1_swiglu_quant_mx, gemm2_weighted_mx,
+    fused_bf16_workspace_size, alloc_workspace_bf16, moe_fused_bf16, gemm1_swiglu_bf16, gemm2_weighted_bf16,
 )

@@ -43,6 +43,16 @@ SIGNATURES = {
                                                     _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
     "moe_gemm2_weighted_mxfp4": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                                 _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "moe_fused_bf16_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
+    # x, w13, w2, topk_ids, topk_weights, T, H, I, E, K, out, workspace, bytes, tile_m, tile_n, layout, stream
+    "moe_fused_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _i32,
+                                      _i32, _i32, _vp]),
+    # x, w13, padded_indptr, sorted_src, T, H, I, E, K, align, q, cap, tile_m, layout, stream
+    "moe_gemm1_swiglu_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _i64,
+                                             _i32, _i32, _vp]),
+    # q, w2, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align, Y, cap, tile_m, tile_n, layout, stream
+    "moe_gemm2_weighted_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp,
+                                               _i64, _i32, _i32, _i32, _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _i32,
                                             _i32, _vp]),
     "moe_pack_mx_scales": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),

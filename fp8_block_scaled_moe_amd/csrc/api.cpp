@@ -55,11 +55,12 @@ struct WsLayout {
 };
 
 // Operand formats of the layer: FP8 with fp32 block scales, MXFP8 and MXFP4
-// (W4A4), both with E8M0 scales per 32 elements.
-enum Fmt { kFmtFp8 = 0, kFmtMx8 = 1, kFmtMx4 = 2 };
+// (W4A4), both with E8M0 scales per 32 elements, and unquantised bf16.
+enum Fmt { kFmtFp8 = 0, kFmtMx8 = 1, kFmtMx4 = 2, kFmtBf16 = 3 };
 
 // MX: q_scale holds one E8M0 byte per 32 columns instead of a float per 128;
-// MXFP4: q holds two e2m1 codes per byte.
+// MXFP4: q holds two e2m1 codes per byte; bf16: q holds 2 bytes per element
+// and there is no q_scale.
 WsLayout ws_layout(int64_t T, int H, int I, int E, int K, int fmt) {
   const int64_t R = T * K;
   const int64_t cap = R + (int64_t)E * (128 - 1);  // worst case: align 128
@@ -71,8 +72,10 @@ WsLayout ws_layout(int64_t T, int H, int I, int E, int K, int fmt) {
   w.padded = take(sizeof(int32_t) * (E + 1));
   w.sorted_src = take(sizeof(int32_t) * cap);
   w.src_to_sorted = take(sizeof(int32_t) * (R > 0 ? R : 1));
-  w.q = take((size_t)cap * (fmt == kFmtMx4 ? I / 2 : I));
-  w.q_scale = take(fmt != kFmtFp8 ? (size_t)cap * (I / 32) : sizeof(float) * (size_t)cap * (I / 128));
+  w.q = take((size_t)cap * (fmt == kFmtMx4 ? I / 2 : fmt == kFmtBf16 ? 2 * (size_t)I : I));
+  w.q_scale = take(fmt == kFmtBf16  ? 0
+                   : fmt != kFmtFp8 ? (size_t)cap * (I / 32)
+                                    : sizeof(float) * (size_t)cap * (I / 128));
   w.Y = take(sizeof(uint16_t) * (size_t)(R > 0 ? R : 1) * H);
   w.total = off;
   return w;
@@ -116,7 +119,8 @@ int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
   return cls == 128 ? (gated ? kClass128TileGemm1 : kClass128TileGemm2) : cls;
 }
 
-// Scale pointer type of each format: fp32 block scales (FP8) or E8M0 codes (MX).
+// Scale pointer type of each format: fp32 block scales (FP8) or E8M0 codes
+// (MX; bf16 passes null scale pointers of this type).
 template <int F>
 using scale_ptr_t = std::conditional_t<F == kFmtFp8, float, uint8_t>;
 
@@ -134,7 +138,9 @@ hipError_t gemm1_launch(const uint8_t* x, const scale_ptr_t<F>* xs, const uint8_
                         hipStream_t st) {
   if constexpr (F == kFmtFp8) return launch_gemm1(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
   else if constexpr (F == kFmtMx8) return launch_gemm1_mx(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
-  else return launch_gemm1_mxfp4(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+  else if constexpr (F == kFmtMx4) return launch_gemm1_mxfp4(x, xs, w, ws, g, H, I, q, qs, tm, packed, st);
+  else return launch_gemm1_bf16(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), g, H, I,
+                                reinterpret_cast<uint16_t*>(q), tm, packed, st);
 }
 
 template <int F>
@@ -143,7 +149,9 @@ hipError_t gemm2_launch(const uint8_t* q, const scale_ptr_t<F>* qs, const uint8_
                         hipStream_t st) {
   if constexpr (F == kFmtFp8) return launch_gemm2(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
   else if constexpr (F == kFmtMx8) return launch_gemm2_mx(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
-  else return launch_gemm2_mxfp4(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+  else if constexpr (F == kFmtMx4) return launch_gemm2_mxfp4(q, qs, w, ws, tw, g, H, I, Y, tm, 256, packed, st);
+  else return launch_gemm2_bf16(reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(w), tw, g, H,
+                                I, Y, tm, 256, packed, st);
 }
 
 template <int F>
@@ -160,7 +168,8 @@ int fused_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, co
     return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
   if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
   if (T == 0) return ok();
-  if (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out)
+  if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !out ||
+      (F != kFmtBf16 && (!x_scale || !w13_scale || !w2_scale)))
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   const WsLayout L = ws_layout(T, H, I, E, K, F);
   if (!workspace) return fail(FP8MOE_ERR_WORKSPACE, "workspace is null");
@@ -216,7 +225,7 @@ int gemm1_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, co
     return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
   if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
   if (T == 0 || cap == 0) return ok();
-  if (!x || !x_scale || !w13 || !w13_scale || !padded_indptr || !sorted_src || !q || !q_scale)
+  if (!x || !w13 || !padded_indptr || !sorted_src || !q || (F != kFmtBf16 && (!x_scale || !w13_scale || !q_scale)))
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
@@ -242,7 +251,8 @@ int gemm2_impl(const void* q, const scale_ptr_t<F>* q_scale, const void* w2, con
   if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
   if (cap < 0 || cap >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "invalid cap %lld", (long long)cap);
   if (T == 0 || cap == 0) return ok();
-  if (!q || !q_scale || !w2 || !w2_scale || !padded_indptr || !sorted_src || !topk_weights || !Y)
+  if (!q || !w2 || !padded_indptr || !sorted_src || !topk_weights || !Y ||
+      (F != kFmtBf16 && (!q_scale || !w2_scale)))
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
@@ -362,6 +372,36 @@ int moe_gemm2_weighted_mx(const void* q, const uint8_t* q_sf, const void* w2, co
                           int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
   return gemm2_impl<kFmtMx8>(q, q_sf, w2, w2_sf, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align, Y, cap,
                           tile_m, tile_n, weight_layout, stream);
+}
+
+int moe_fused_bf16_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, size_t* bytes) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
+  *bytes = ws_layout(T, H, I, E, K, kFmtBf16).total;
+  return ok();
+}
+
+int moe_fused_bf16(const void* x, const void* w13, const void* w2, const int32_t* topk_ids, const float* topk_weights,
+                   int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, void* workspace,
+                   size_t workspace_bytes, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+  return fused_impl<kFmtBf16>(x, nullptr, w13, nullptr, w2, nullptr, topk_ids, topk_weights, T, H, I, E, K, out,
+                              workspace, workspace_bytes, tile_m, tile_n, weight_layout, stream);
+}
+
+int moe_gemm1_swiglu_bf16(const void* x, const void* w13, const int32_t* padded_indptr, const int32_t* sorted_src,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align, void* q, int64_t cap,
+                          int32_t tile_m, int32_t weight_layout, void* stream) {
+  return gemm1_impl<kFmtBf16>(x, nullptr, w13, nullptr, padded_indptr, sorted_src, T, H, I, E, K, align, q, nullptr,
+                              cap, tile_m, weight_layout, stream);
+}
+
+int moe_gemm2_weighted_bf16(const void* q, const void* w2, const int32_t* padded_indptr, const int32_t* sorted_src,
+                            const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                            int32_t align, void* Y, int64_t cap, int32_t tile_m, int32_t tile_n, int32_t weight_layout,
+                            void* stream) {
+  return gemm2_impl<kFmtBf16>(q, nullptr, w2, nullptr, padded_indptr, sorted_src, topk_weights, T, H, I, E, K, align,
+                              Y, cap, tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out, void* stream) {

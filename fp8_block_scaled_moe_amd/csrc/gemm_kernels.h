@@ -1,6 +1,8 @@
-// Grouped FP8 (e4m3) GEMMs of the MoE expert path on gfx950 (CDNA4): the
-// kernels and their launch logic, instantiated by gemm1.hip / gemm2.hip (FP8
-// block-scaled operands) and gemm1_mx.hip / gemm2_mx.hip (MXFP8 operands).
+// Grouped GEMMs of the MoE expert path on gfx950 (CDNA4): the kernels and
+// their launch logic, instantiated by gemm1.hip / gemm2.hip (FP8 block-scaled
+// operands), gemm1_mx.hip / gemm2_mx.hip (MXFP8), gemm1_mxfp4.hip /
+// gemm2_mxfp4.hip (MXFP4) and gemm1_bf16.hip / gemm2_bf16.hip (unquantised
+// bf16 operands).
 //
 //   GEMM1: h = x[token] . w13[e]^T over gate+up, then SwiGLU and the FP8
 //          requantisation in the epilogue (AlphaMoE page, section "Problem":
@@ -25,6 +27,12 @@
 // op_sel), so the MFMA accumulates straight into acc and no VALU fold
 // remains.  The intermediate is requantised per 1x32 block to E8M0 + e4m3 as
 // in the gated-act kernel.
+//
+// bf16 variant (the unquantised experts of the cuTile page's unified API):
+// the same byte path with rows of 2 bytes per element and no scales.  A
+// 128-byte K step holds 64 elements; each 16-byte half of a lane's operand
+// fragment is 8 elements and feeds one 16x16x32 bf16 MFMA, two per step.
+// GEMM1 stores the activation as bf16.
 //
 // Weight streaming.  For these shapes the layer is a stream of expert
 // weights (every active expert's weights are read once, ~256 routed rows
@@ -131,6 +139,17 @@ __device__ __forceinline__ v4f mfma16x16x128_mx_sel(int sela, int selb, const v8
     default: return mfma16x16x128_mx<3, 3, FMT>(a, b, c, sa, sb);
   }
 #undef FP8MOE_MX_CASE
+}
+
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+// One 16x16x32 bf16 MFMA, c += a . b, on the hf-th 16 bytes (8 elements) of
+// each lane's 32-byte operand fragment.  Both operands take the same bytes,
+// so the hardware's K order within the lane leaves the sum unchanged.
+__device__ __forceinline__ v4f mfma16x16x32_bf16_half(const v8i& a, const v8i& b, const v4f& c, int hf) {
+  const v4i ah = hf ? v4i{a[4], a[5], a[6], a[7]} : v4i{a[0], a[1], a[2], a[3]};
+  const v4i bh = hf ? v4i{b[4], b[5], b[6], b[7]} : v4i{b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, ah), __builtin_bit_cast(v8bf16, bh), c,
+                                                 0, 0, 0);
 }
 
 // MX weight scales in the MFMA-tiled layout (moe_pack_mx_scales,
@@ -479,13 +498,16 @@ __device__ __forceinline__ void stage_token_scales_mx(uint8_t* SX, int KT, RowSf
 // [NB][KT][2]; MXFP8 weight scales stream from global memory with the
 // weights), the epilogue scratch (GEMM1: per-wave row max [8][TM]; GEMM2:
 // source row and top-k weight [2][TM]).
-template <int TM, bool MX, bool FP4 = false>
+template <int TM, bool MX, bool FP4 = false, bool BF = false>
 struct Lds {
-  // MX: SPB scale bytes per row, 32-K block group and K step (2 for e2m1)
+  // MX: SPB scale bytes per row, 32-K block group and K step (2 for e2m1);
+  // BF (bf16 operands): no scales at all
   __host__ __device__ static constexpr size_t token_bytes(int KT) {
-    return MX ? 256 * (size_t)Cfg<TM>::TSW * (FP4 ? 2 : 1) * KT : 4 * (size_t)Cfg<TM>::TSLOT * KT;
+    return BF ? 0 : MX ? 256 * (size_t)Cfg<TM>::TSW * (FP4 ? 2 : 1) * KT : 4 * (size_t)Cfg<TM>::TSLOT * KT;
   }
-  __host__ __device__ static constexpr size_t weight_bytes(int KT, int NB) { return MX ? 0 : 8 * (size_t)NB * KT; }
+  __host__ __device__ static constexpr size_t weight_bytes(int KT, int NB) {
+    return MX || BF ? 0 : 8 * (size_t)NB * KT;
+  }
   __host__ __device__ static constexpr size_t bytes(int KT, int NB) {
     return token_bytes(KT) + weight_bytes(KT, NB) + 4 * (size_t)kWaves * TM;
   }
@@ -523,7 +545,7 @@ struct Lds {
 // steps 4m..4m+3 of an N tile) loads the dword of scale group m for the next
 // round, which becomes the current one when the round ends; step s of a
 // round selects byte s (op_sel of the A operand).
-template <int TM, bool GATED, bool PACKED, bool MX, bool FP4, typename WBand, typename Epi>
+template <int TM, bool GATED, bool PACKED, bool MX, bool FP4, bool BF = false, typename WBand, typename Epi>
 __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& tb,
                                             const uint8_t* const (&a_src)[Cfg<TM>::A_PER_WAVE],
                                             __amdgpu_buffer_rsrc_t wrsrc, __amdgpu_buffer_rsrc_t srsrc, int kdim,
@@ -537,8 +559,9 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   constexpr int SPB = FP4 ? 2 : 1;
   constexpr int FMT = FP4 ? 4 : 0;
   static_assert(!FP4 || MX, "e2m1 operands carry E8M0 scales");
-  const float* SAs = Lds<TM, MX, FP4>::token_scales(smem);
-  const float* SBs = Lds<TM, MX, FP4>::weight_scales(smem, KT);
+  static_assert(!BF || !MX, "bf16 operands carry no scales");
+  const float* SAs = Lds<TM, MX, FP4, BF>::token_scales(smem);
+  const float* SBs = Lds<TM, MX, FP4, BF>::weight_scales(smem, KT);
   const uint8_t* SXs = reinterpret_cast<const uint8_t*>(SAs);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const int S = nn * KT;
@@ -651,7 +674,10 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   float sb0, sb1;
   uint32_t sx[SPB][TSW];   // MX token scale codes (per MFMA of the step)
   auto read_scales = [&](int n, int k) __attribute__((always_inline)) {
-    if constexpr (MX) {
+    if constexpr (BF) {
+      (void)n;
+      (void)k;
+    } else if constexpr (MX) {
 #pragma unroll
       for (int hf = 0; hf < SPB; ++hf) {
         const uint32_t* p =
@@ -683,7 +709,17 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   auto step = [&](int s, int nx, int kx) __attribute__((always_inline)) {
     dma_a((s + 3) & 3);        // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
     __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
-    if constexpr (MX) {
+    if constexpr (BF) {
+      // 64 bf16 elements per step: one 16x16x32 MFMA per 16-byte half
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) {
+        if (ts + 2 < TS) af[(ts + 2) % 3] = frag(s, ts + 2);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int w = 0; w < 2; ++w) acc[ts][w] = mfma16x16x32_bf16_half(wr[s][w], af[ts % 3], acc[ts][w], hf);
+      }
+    } else if constexpr (MX) {
       // the hf-th MFMA of the step takes the hf-th 16 bytes of each operand
       // (the whole 32 bytes for e4m3) and scale byte SPB*s + hf of the round
       auto half = [](const v8i& v, int hf) __attribute__((always_inline)) -> v8i {
@@ -804,7 +840,9 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
 // sorted_src is valid, with no requantisation.
 // FP4 (MXFP4, e2m1 operands): rows of x and w13 are H/2 bytes, the
 // intermediate is requantised to 1x32 E8M0 + e2m1 (I/2 bytes per q row).
-template <int TM, bool PACKED, bool MX, bool PLAIN = false, bool FP4 = false>
+// BF (bf16 operands, no scales): rows of x and w13 are 2H bytes and q holds
+// the activation as bf16 [rows][I] (round to nearest even).
+template <int TM, bool PACKED, bool MX, bool PLAIN = false, bool FP4 = false, bool BF = false>
 __device__ __forceinline__ void gemm1_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ x,
     const scale_t<MX>* __restrict__ x_scale, const uint8_t* __restrict__ w13,
@@ -820,9 +858,9 @@ __device__ __forceinline__ void gemm1_tile(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   constexpr int SPB = FP4 ? 2 : 1;
-  const int HR = H / SPB;                      // bytes per x / w13 row
+  const int HR = BF ? 2 * H : H / SPB;         // bytes per x / w13 row
   const int KT = HR / kKB, HB = H / kKB, IB = I / 128;
-  float* red = Lds<TM, MX, FP4>::scratch(smem, KT, NB);
+  float* red = Lds<TM, MX, FP4, BF>::scratch(smem, KT, NB);
 
   // source of this lane's 16-byte chunk of each direct-to-LDS block: LDS
   // chunk qc holds row qc / 8, logical chunk (qc % 8) XOR the row's key
@@ -848,8 +886,10 @@ __device__ __forceinline__ void gemm1_tile(
     const int c = 128 * (nt0 + n) + 16 * wave;   // first row of the 16-row band
     return w ? I + c : c;
   };
-  __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
-  if constexpr (MX) {
+  __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MX weight scales; unused by the other variants
+  if constexpr (BF) {
+    // no scales
+  } else if constexpr (MX) {
     const int sbytes = mx_weight_scale_bytes<PACKED, SPB>(2 * I, HR);
     const uint8_t* sexp = w13_scale + (size_t)tc.e * sbytes;
     srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, sbytes, kWeightRsrcFlags);
@@ -875,6 +915,20 @@ __device__ __forceinline__ void gemm1_tile(
   // pair 2p, 2p+1 (32 columns), through LDS
   auto epi = [&](int n, v4f (&acc)[TS][2]) __attribute__((always_inline)) {
     const int n0 = 128 * (nt0 + n), c0 = n0 + 16 * wave;
+    if constexpr (BF) {
+      // four consecutive columns per lane as bf16, no requantisation
+      uint16_t* q16 = reinterpret_cast<uint16_t*>(q);
+#pragma unroll
+      for (int ts = 0; ts < TS; ++ts) {
+        if (16 * ts >= h) break;   // sub-tiles past the segment (h is a multiple of 16)
+        const int row = 16 * ts + l16;
+        uint2 v;
+        v.x = pack2_bf16(silu_mul(acc[ts][0][0], acc[ts][1][0]), silu_mul(acc[ts][0][1], acc[ts][1][1]));
+        v.y = pack2_bf16(silu_mul(acc[ts][0][2], acc[ts][1][2]), silu_mul(acc[ts][0][3], acc[ts][1][3]));
+        *reinterpret_cast<uint2*>(q16 + (size_t)(tc.p0 + row) * I + c0 + 4 * g) = v;
+      }
+      return;
+    }
     if constexpr (PLAIN) {
 #pragma unroll
       for (int ts = 0; ts < TS; ++ts) {
@@ -945,7 +999,8 @@ __device__ __forceinline__ void gemm1_tile(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, true, PACKED, MX, FP4>(smem, tb, a_src, wrsrc, srsrc, HR, 0, KT, nn, tid, lane, acc, wband, epi);
+  ws_mainloop<TM, true, PACKED, MX, FP4, BF>(smem, tb, a_src, wrsrc, srsrc, HR, 0, KT, nn, tid, lane, acc, wband,
+                                             epi);
 }
 
 // The token buffers are the kernel's; each workgroup runs the tile body of
@@ -998,7 +1053,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_swiglu_quant_kernel(
 // writes the fp32 accumulators to plain_out [rows][H] at the padded row
 // (rows whose sorted_src is valid), without the top-k weight.
 // FP4 (MXFP4): q and w2 rows are I/2 bytes of e2m1 codes.
-template <int TM, bool PACKED, bool MX, bool PLAIN = false, bool FP4 = false>
+// BF (bf16 operands, no scales): q and w2 rows are 2I bytes of bf16.
+template <int TM, bool PACKED, bool MX, bool PLAIN = false, bool FP4 = false, bool BF = false>
 __device__ __forceinline__ void gemm2_tile(
     uint8_t* smem, const TokenBuffers& tb, const TileCoord& tc, const uint8_t* __restrict__ q,
     const scale_t<MX>* __restrict__ q_scale, const uint8_t* __restrict__ w2,
@@ -1015,9 +1071,9 @@ __device__ __forceinline__ void gemm2_tile(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   constexpr int SPB = FP4 ? 2 : 1;
-  const int IR = I / SPB;                      // bytes per q / w2 row
+  const int IR = BF ? 2 * I : I / SPB;         // bytes per q / w2 row
   const int KT = IR / kKB, IB = I / kKB, HB = H / 128;
-  int* srow = reinterpret_cast<int*>(Lds<TM, MX, FP4>::scratch(smem, KT, NB));
+  int* srow = reinterpret_cast<int*>(Lds<TM, MX, FP4, BF>::scratch(smem, KT, NB));
   float* wrow_w = reinterpret_cast<float*>(srow + TM);
 
   // token rows: q rows p0.. (a pad row holds whatever is there; its outputs are never stored)
@@ -1037,8 +1093,10 @@ __device__ __forceinline__ void gemm2_tile(
     // bands past H (the last N tile when H % 256 == 128) read the last band
     return min(kTN * (nt0 + n) + 32 * wave + 16 * w, H - 16);
   };
-  __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MXFP8 weight scales; unused by the FP8 variant
-  if constexpr (MX) {
+  __amdgpu_buffer_rsrc_t srsrc = wrsrc;   // MX weight scales; unused by the other variants
+  if constexpr (BF) {
+    // no scales
+  } else if constexpr (MX) {
     const int sbytes = mx_weight_scale_bytes<PACKED, SPB>(H, IR);
     const uint8_t* sexp = w2_scale + (size_t)tc.e * sbytes;
     srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)sexp, (short)0, sbytes, kWeightRsrcFlags);
@@ -1103,8 +1161,8 @@ __device__ __forceinline__ void gemm2_tile(
   v4f acc[TS][2];
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) acc[ts][0] = acc[ts][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  ws_mainloop<TM, false, PACKED, MX, FP4>(smem, tb, a_src, wrsrc, srsrc, IR, wave >> 2, KT, nn, tid, lane, acc, wband,
-                                     epi);
+  ws_mainloop<TM, false, PACKED, MX, FP4, BF>(smem, tb, a_src, wrsrc, srsrc, IR, wave >> 2, KT, nn, tid, lane, acc,
+                                              wband, epi);
 }
 
 template <int TMAX, bool PACKED, bool MX, bool FP4 = false>
@@ -1124,6 +1182,41 @@ __global__ __launch_bounds__(kThreads) void gemm2_weighted_kernel(
   FP8MOE_BODIES(FP8MOE_G2_BODY)
 #undef FP8MOE_G2_BODY
 }
+// bf16 kernels: the same tile bodies with BF = true and no scale arguments;
+// q is bf16 [cap][I].
+template <int TMAX, bool PACKED>
+__global__ __launch_bounds__(kThreads) void gemm1_swiglu_bf16_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w13, const int32_t* __restrict__ padded,
+    const int32_t* __restrict__ sorted_src, int E, int K, int H, int I, int NB, uint16_t* __restrict__ q) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NT = I / 128, NG = (NT + NB - 1) / NB;
+  TileCoord tc;
+  if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
+  FP8MOE_TOKEN_BUFFERS(TMAX);
+#define FP8MOE_B1_BODY(TMV)                                                                                \
+  gemm1_tile<TMV, PACKED, false, false, false, true>(smem, tb, tc, x, nullptr, w13, nullptr, sorted_src, K, H, I, \
+                                                     NB, reinterpret_cast<uint8_t*>(q), nullptr)
+  FP8MOE_BODIES(FP8MOE_B1_BODY)
+#undef FP8MOE_B1_BODY
+}
+
+template <int TMAX, bool PACKED>
+__global__ __launch_bounds__(kThreads) void gemm2_weighted_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ w2, const float* __restrict__ topk_weights,
+    const int32_t* __restrict__ padded, const int32_t* __restrict__ sorted_src, int E, int H, int I, int NB,
+    uint16_t* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int NT = (H + kTN - 1) / kTN, NG = (NT + NB - 1) / NB;
+  TileCoord tc;
+  if (!tile_coord<TMAX>(padded, sorted_src, E, NG, tc)) return;
+  FP8MOE_TOKEN_BUFFERS(TMAX);
+#define FP8MOE_B2_BODY(TMV)                                                                                         \
+  gemm2_tile<TMV, PACKED, false, false, false, true>(smem, tb, tc, reinterpret_cast<const uint8_t*>(q), nullptr, w2, \
+                                                     nullptr, topk_weights, sorted_src, H, I, NB, Y)
+  FP8MOE_BODIES(FP8MOE_B2_BODY)
+#undef FP8MOE_B2_BODY
+}
+
 // The plain grouped GEMM (SM120 page, section 1: a [rows, k] grouped by
 // expert segments, b [E, n, k], NT, fp32 out; gated: SwiGLU over gate+up)
 // on the same tiles and main loop as the expert GEMMs.
@@ -1176,15 +1269,15 @@ static inline int run_length(const GroupedRows& g, int tm, int NT, int KT) {
   return (int)((NT + ng - 1) / ng);
 }
 
-template <bool MX, bool FP4 = false>
+template <bool MX, bool FP4 = false, bool BF = false>
 static inline size_t gemm_lds_bytes(int tile_m, int KT, int NB) {
   switch (tile_m) {
-    case 16: return Lds<16, MX, FP4>::bytes(KT, NB);
-    case 32: return Lds<32, MX, FP4>::bytes(KT, NB);
-    case 64: return Lds<64, MX, FP4>::bytes(KT, NB);
-    case 128: return Lds<128, MX, FP4>::bytes(KT, NB);
-    case 144: return Lds<144, MX, FP4>::bytes(KT, NB);
-    default: return Lds<160, MX, FP4>::bytes(KT, NB);
+    case 16: return Lds<16, MX, FP4, BF>::bytes(KT, NB);
+    case 32: return Lds<32, MX, FP4, BF>::bytes(KT, NB);
+    case 64: return Lds<64, MX, FP4, BF>::bytes(KT, NB);
+    case 128: return Lds<128, MX, FP4, BF>::bytes(KT, NB);
+    case 144: return Lds<144, MX, FP4, BF>::bytes(KT, NB);
+    default: return Lds<160, MX, FP4, BF>::bytes(KT, NB);
   }
 }
 
@@ -1197,11 +1290,11 @@ static_assert(Cfg<128>::D == kRing && Cfg<160>::D == kRing, "one ring depth");
 
 // run_length, shortened until the run's weight scales fit in LDS; one N tile
 // per workgroup unless the K steps fill whole rounds of the weight ring
-template <bool MX, bool FP4 = false>
+template <bool MX, bool FP4 = false, bool BF = false>
 static inline int fit_run(const GroupedRows& g, int tm, int NT, int KT) {
   if (KT % kRing != 0) return 1;
   int nb = run_length(g, tm, NT, KT);
-  while (nb > 1 && gemm_lds_bytes<MX, FP4>(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
+  while (nb > 1 && gemm_lds_bytes<MX, FP4, BF>(tm, KT, nb) > max_dyn_lds(tm)) nb = (nb + 1) / 2;
   const int ng = (NT + nb - 1) / nb;
   return (NT + ng - 1) / ng;
 }
@@ -1299,6 +1392,84 @@ static hipError_t launch_gemm2_t(const uint8_t* q, const scale_t<MX>* q_scale, c
     default: return hipErrorInvalidValue;
   }
 #undef FP8MOE_G2
+  return hipGetLastError();
+}
+
+// bf16 launchers: KT = 2H / 128 (GEMM1) and 2I / 128 (GEMM2) 128-byte K
+// steps; same tiles, runs and grids as the quantised variants.
+static hipError_t launch_gemm1_bf16_t(const uint8_t* x, const uint8_t* w13, const GroupedRows& g, int H, int I,
+                                      uint16_t* q, int tile_m, bool packed, hipStream_t stream) {
+  static const hipError_t attr = [] {
+    hipError_t e = hipSuccess;
+#define FP8MOE_ATTR(TMV)                                                              \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_bf16_kernel<TMV, false>);    \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_bf16_kernel<TMV, true>)
+    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128);
+#undef FP8MOE_ATTR
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (tile_m > kMaxTileGemm1) return hipErrorInvalidValue;
+  const int KT = 2 * H / kKB;
+  const int NT = I / 128, NB = fit_run<false, false, true>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
+  const size_t lds = gemm_lds_bytes<false, false, true>(tile_m, KT, NB);
+  if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
+  const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
+#define FP8MOE_B1(TMV)                                                                                          \
+  if (packed)                                                                                                   \
+    hipLaunchKernelGGL((gemm1_swiglu_bf16_kernel<TMV, true>), grid, block, lds, stream, x, w13, g.padded_indptr, \
+                       g.sorted_src, g.E, g.K, H, I, NB, q);                                                     \
+  else                                                                                                          \
+    hipLaunchKernelGGL((gemm1_swiglu_bf16_kernel<TMV, false>), grid, block, lds, stream, x, w13, g.padded_indptr, \
+                       g.sorted_src, g.E, g.K, H, I, NB, q)
+  switch (tile_m) {
+    case 16: FP8MOE_B1(16); break;
+    case 32: FP8MOE_B1(32); break;
+    case 64: FP8MOE_B1(64); break;
+    case 128: FP8MOE_B1(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FP8MOE_B1
+  return hipGetLastError();
+}
+
+static hipError_t launch_gemm2_bf16_t(const uint16_t* q, const uint8_t* w2, const float* topk_weights,
+                                      const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m, int tile_n,
+                                      bool packed, hipStream_t stream) {
+  if (tile_n != kTN) return hipErrorInvalidValue;
+  static const hipError_t attr = [] {
+    hipError_t e = hipSuccess;
+#define FP8MOE_ATTR(TMV)                                                               \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_bf16_kernel<TMV, false>);   \
+    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_bf16_kernel<TMV, true>)
+    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144); FP8MOE_ATTR(160);
+#undef FP8MOE_ATTR
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (tile_m > kMaxTileGemm2) return hipErrorInvalidValue;
+  const int KT = 2 * I / kKB;
+  const int NT = (H + kTN - 1) / kTN, NB = fit_run<false, false, true>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
+  const size_t lds = gemm_lds_bytes<false, false, true>(tile_m, KT, NB);
+  if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
+  const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
+#define FP8MOE_B2(TMV)                                                                                            \
+  if (packed)                                                                                                     \
+    hipLaunchKernelGGL((gemm2_weighted_bf16_kernel<TMV, true>), grid, block, lds, stream, q, w2, topk_weights,     \
+                       g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y);                                           \
+  else                                                                                                            \
+    hipLaunchKernelGGL((gemm2_weighted_bf16_kernel<TMV, false>), grid, block, lds, stream, q, w2, topk_weights,    \
+                       g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y)
+  switch (tile_m) {
+    case 16: FP8MOE_B2(16); break;
+    case 32: FP8MOE_B2(32); break;
+    case 64: FP8MOE_B2(64); break;
+    case 128: FP8MOE_B2(128); break;
+    case 144: FP8MOE_B2(144); break;
+    case 160: FP8MOE_B2(160); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef FP8MOE_B2
   return hipGetLastError();
 }
 

@@ -71,6 +71,15 @@ hipError_t launch_gemm2_mxfp4(const uint8_t* q, const uint8_t* q_sf, const uint8
                               const float* topk_weights, const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m,
                               int tile_n, bool packed, hipStream_t stream);
 
+// Unquantised bf16 variants: x [T][H], w13 [E][2I][H] (row-major, or packed
+// by launch_pack_weights as bytes with K = 2H), q [cap][I], w2 [E][H][I], all
+// bf16; GEMM1 stores the SwiGLU output as bf16 (nearest even).  Same tiles,
+// layouts and limits as the FP8 launchers.
+hipError_t launch_gemm1_bf16(const uint16_t* x, const uint16_t* w13, const GroupedRows& g, int H, int I, uint16_t* q,
+                             int tile_m, bool packed, hipStream_t stream);
+hipError_t launch_gemm2_bf16(const uint16_t* q, const uint16_t* w2, const float* topk_weights, const GroupedRows& g,
+                             int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream);
+
 // Plain grouped GEMM: out[p] = a[p] . b[e]^T (fp32) for every padded row p of
 // expert e with sorted_src[p] >= 0; gated: out[p, c] = silu(h[c]) * h[n/2 + c]
 // ([rows][n/2]).  tile_m in {16, 32, 64, 128}.

@@ -85,7 +85,15 @@ WEIGHTS_ROW_MAJOR, WEIGHTS_MFMA_TILED = 0, 1
 
 def pack_weights(w, out=None):
     """Expert weights e4m3 [E, N, K] row-major -> the MFMA-tiled layout (same shape and byte
-    count, bytes permuted; see moe_pack_weights in include/fp8moe.h)."""
+    count, bytes permuted; see moe_pack_weights in include/fp8moe.h).  bf16 weights are packed
+    as their bytes and returned as bf16 of the same shape."""
+    if w.dtype == torch.bfloat16:
+        if out is not None:
+            _need(out, torch.bfloat16, "out", 3)
+            if tuple(out.shape) != tuple(w.shape):
+                raise ValueError("out must have the shape of w")
+        packed = pack_weights(w.view(torch.uint8), None if out is None else out.view(torch.uint8))
+        return packed.view(torch.bfloat16)
     w = _u8(w)
     _need(w, torch.uint8, "w", 3)
     E, N, K = w.shape
@@ -394,6 +402,83 @@ def gemm2_weighted_mxfp4(q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, t
                          weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
     """MXFP4 GEMM2 + routing-weight stage (q [cap, I/2] packed e2m1 codes)."""
     return _gemm2_mx(True, q, q_sf, w2, w2_sf, route, topk_weights, T, K, align, tile_m, tile_n, weight_layout, Y)
+
+
+# ---------------------------------------------------------------- bf16 variant
+
+def fused_bf16_workspace_size(T, H, I, E, K):
+    n = ctypes.c_size_t(0)
+    check(lib().moe_fused_bf16_workspace_size(T, H, I, E, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace_bf16(T, H, I, E, K, device):
+    """A device workspace for moe_fused_bf16."""
+    return torch.empty(fused_bf16_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=device)
+
+
+def moe_fused_bf16(x, w13, w2, topk_ids, topk_weights, out=None, workspace=None, tile_m=-1, tile_n=-1,
+                   weight_layout=WEIGHTS_ROW_MAJOR):
+    """Unquantised bf16 MoE layer: x [T, H], w13 [E, 2I, H], w2 [E, H, I] bf16, no scales.
+    Returns bf16 [T, H].  weight_layout 1: w13 and w2 packed by pack_weights."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w13, torch.bfloat16, "w13", 3)
+    _need(w2, torch.bfloat16, "w2", 3)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    K = topk_ids.shape[1]
+    if H2 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
+        raise ValueError("inconsistent x / w13 / w2 shapes")
+    if tuple(topk_ids.shape) != (T, K) or tuple(topk_weights.shape) != (T, K):
+        raise ValueError("topk_ids / topk_weights must be [T, K]")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", 2)
+    if workspace is None:
+        workspace = alloc_workspace_bf16(T, H, I, E, K, dev)
+    check(lib().moe_fused_bf16(_p(x), _p(w13), _p(w2), _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out),
+                               _p(workspace), workspace.numel() * workspace.element_size(), tile_m, tile_n,
+                               weight_layout, _stream(dev)))
+    return out
+
+
+def gemm1_swiglu_bf16(x, w13, route, T, K, align, tile_m=-1, weight_layout=WEIGHTS_ROW_MAJOR, q=None):
+    """bf16 GEMM1 + SwiGLU stage.  Returns q bf16 [cap, I] (the activation rounded to bf16)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w13, torch.bfloat16, "w13", 3)
+    E, I2, H = w13.shape
+    I = I2 // 2
+    cap = route["sorted_src"].numel()
+    dev = x.device
+    q = torch.zeros((cap, I), dtype=torch.bfloat16, device=dev) if q is None else q
+    _need(q, torch.bfloat16, "q", 2)
+    if tuple(q.shape) != (cap, I):
+        raise ValueError("q must be [cap, I]")
+    check(lib().moe_gemm1_swiglu_bf16(_p(x), _p(w13), _p(route["padded_indptr"]), _p(route["sorted_src"]), T, H, I,
+                                      E, K, align, _p(q), cap, tile_m, weight_layout, _stream(dev)))
+    return q
+
+
+def gemm2_weighted_bf16(q, w2, route, topk_weights, T, K, align, tile_m=-1, tile_n=-1,
+                        weight_layout=WEIGHTS_ROW_MAJOR, Y=None):
+    """bf16 GEMM2 + routing-weight stage (q bf16 [cap, I]).  Returns Y bf16 [T*K, H]."""
+    _need(q, torch.bfloat16, "q", 2)
+    _need(w2, torch.bfloat16, "w2", 3)
+    E, H, I = w2.shape
+    cap = route["sorted_src"].numel()
+    dev = q.device
+    Y = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev) if Y is None else Y
+    _need(Y, torch.bfloat16, "Y", 2)
+    if tuple(Y.shape) != (T * K, H):
+        raise ValueError("Y must be [T*K, H]")
+    check(lib().moe_gemm2_weighted_bf16(_p(q), _p(w2), _p(route["padded_indptr"]), _p(route["sorted_src"]),
+                                        _p(topk_weights), T, H, I, E, K, align, _p(Y), cap, tile_m, tile_n,
+                                        weight_layout, _stream(dev)))
+    return Y
 
 
 def combine(Y, topk_ids, E):

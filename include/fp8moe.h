@@ -298,6 +298,40 @@ int moe_gemm2_weighted_mxfp4(const void* q, const uint8_t* q_sf,
                              void* Y, int64_t cap, int32_t tile_m, int32_t tile_n,
                              int32_t weight_layout, void* stream);
 
+/* ---------------------------------------------------------------- bf16 variant of the layer and its stages
+ * The layer with unquantised bf16 experts (the cuTile page lists bf16 MoE
+ * configurations beside the FP8 and FP4 ones, unified-API section).  Every
+ * operand is bfloat16 (uint16 storage), with no scales:
+ *   x      bf16 [T, H]
+ *   w13    bf16 [E, 2I, H]   (gate rows first)
+ *   w2     bf16 [E, H, I]
+ * Both GEMMs accumulate in fp32; GEMM1 stores the SwiGLU output rounded to
+ * bf16 (nearest, ties to even) as the intermediate:
+ *   q      bf16 [cap, I]     (no scales)
+ * GEMM2's epilogue and the combine are those of moe_fused_fp8.  Arguments
+ * mean what they mean there; H and I multiples of 128.  With
+ * FP8MOE_WEIGHTS_MFMA_TILED the weights are packed by moe_pack_weights as
+ * bytes (K = 2H for w13, 2I for w2).  Workspace: moe_fused_bf16_workspace_size
+ * (q takes 2 bytes per element).  Errors as for moe_fused_fp8.
+ */
+int moe_fused_bf16_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                  size_t* bytes);
+int moe_fused_bf16(const void* x, const void* w13, const void* w2,
+                   const int32_t* topk_ids, const float* topk_weights,
+                   int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                   void* out, void* workspace, size_t workspace_bytes,
+                   int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream);
+int moe_gemm1_swiglu_bf16(const void* x, const void* w13,
+                          const int32_t* padded_indptr, const int32_t* sorted_src,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                          void* q, int64_t cap, int32_t tile_m, int32_t weight_layout, void* stream);
+int moe_gemm2_weighted_bf16(const void* q, const void* w2,
+                            const int32_t* padded_indptr, const int32_t* sorted_src,
+                            const float* topk_weights,
+                            int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t align,
+                            void* Y, int64_t cap, int32_t tile_m, int32_t tile_n,
+                            int32_t weight_layout, void* stream);
+
 /* ---------------------------------------------------------------- weight packing
  * moe_pack_weights: expert weights e4m3 [E, N, K] row-major (w13 with N = 2I,
  * K = H, or w2 with N = H, K = I) -> FP8MOE_WEIGHTS_MFMA_TILED, the layout
@@ -308,7 +342,8 @@ int moe_gemm2_weighted_mxfp4(const void* q, const uint8_t* q_sf,
  * own data layout choice: the pages' kernels read row-major weights).
  * Requires E >= 1, N % 16 == 0, K % 128 == 0, in and out non-NULL and not
  * overlapping (FP8MOE_ERR_SHAPE otherwise); out is caller-owned device memory
- * of E*N*K bytes.  Asynchronous on `stream`.
+ * of E*N*K bytes.  Asynchronous on `stream`.  K counts bytes: e2m1 codes
+ * (two per byte) pass K/2 elements' bytes, bf16 weights 2K.
  */
 int moe_pack_weights(const void* in, int64_t E, int32_t N, int32_t K, void* out, void* stream);
 

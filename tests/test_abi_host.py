@@ -155,6 +155,53 @@ def test_stage_validation(fmt):
     assert L.moe_combine(NULL, NULL, 0, 128, 4, 2, NULL, NULL) == OK
 
 
+def test_bf16_validation():
+    L = lib()
+    def fused(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, tn=-1, out=FAKE, layout=0):
+        return L.moe_fused_bf16(ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, tn, layout, NULL)
+    assert fused(T=-1) == E_SHAPE
+    assert fused(H=200) == E_ALIGN
+    assert fused(I=64) == E_ALIGN
+    assert fused(K=0) == E_TOPK
+    assert fused(E=1025, K=2) == E_LIMIT
+    assert fused(tm=48) == E_TILE
+    assert fused(tn=128) == E_TILE
+    assert fused(layout=2) == E_SHAPE
+    assert fused(ptr=NULL) == E_NULL
+    assert fused(out=NULL) == E_NULL
+    assert fused(ws=NULL) == E_WS
+    assert fused(wsb=1024) == E_WS
+    assert fused(T=0, ptr=NULL, ws=NULL, out=NULL) == OK
+    # no scale arguments: the stages need only data, routing and outputs
+    g1 = lambda **k: L.moe_gemm1_swiglu_bf16(k.get("x", FAKE), FAKE, FAKE, FAKE, k.get("T", 16), 256, 128, 4, 2,
+                                             k.get("align", 16), k.get("q", FAKE), k.get("cap", 100),
+                                             k.get("tm", -1), k.get("layout", 0), NULL)
+    assert g1(align=24) == E_ALIGN
+    assert g1(tm=96) == E_TILE
+    assert g1(cap=-1) == E_SHAPE
+    assert g1(x=NULL) == E_NULL
+    assert g1(q=NULL) == E_NULL
+    assert g1(T=0) == OK
+    g2 = lambda **k: L.moe_gemm2_weighted_bf16(FAKE, FAKE, FAKE, FAKE, FAKE, 16, k.get("H", 256), 128, 4, 2,
+                                               k.get("align", 16), k.get("Y", FAKE), 100, k.get("tm", -1),
+                                               k.get("tn", -1), k.get("layout", 0), NULL)
+    assert g2(tn=64) == E_TILE
+    assert g2(H=100) == E_ALIGN
+    assert g2(Y=NULL) == E_NULL
+    assert g2(layout=3) == E_SHAPE
+
+
+def test_workspace_size_bf16():
+    nb = fm.fused_bf16_workspace_size(16, 256, 128, 4, 2)
+    R, cap = 32, 32 + 4 * 127
+    # q holds 2 bytes per element and has no scales; Y and sorted_src as for the other formats
+    assert nb >= cap * 256 + R * 256 * 2 + cap * 4
+    assert nb > fm.fused_workspace_size(16, 256, 128, 4, 2)
+    assert fm.fused_bf16_workspace_size(8192, 7168, 2048, 256, 8) < 2 ** 31
+    with pytest.raises(fm.Fp8MoeError):
+        fm.fused_bf16_workspace_size(16, 256, 100, 4, 2)
+
+
 def test_pack_mx_scales_validation():
     L = lib()
     assert L.moe_pack_mx_scales_bytes(256, 4096, 7168) == 256 * 4096 * 7168 // 32
