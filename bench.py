@@ -28,15 +28,18 @@ The line also carries:
                 prefill and decode shapes: us, TFLOP/s, GB/s and stage times.
   mxfp4         the same for the MXFP4 (W4A4: e2m1 codes, 1x32 E8M0 scales)
                 variant, priced against the dense fp4 MFMA peak (10.1 PFLOP/s).
+  bf16          the same for the unquantised bf16 variant, priced against the
+                dense bf16 MFMA peak (2.5 PFLOP/s).
   cpu_baseline  the CPU oracle timed on a bounded sample of prefill tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                      [--no-extras] [--profile {prefill,decode,gated,mx,mxfp4}] [--traffic-kib F,W,SF,SW]
+                      [--no-extras] [--profile {prefill,decode,gated,mx,mxfp4,bf16}]
+                      [--traffic-kib F,W,SF,SW]
 
 --profile runs one workload only, for rocprofv3 passes: prefill (the layer,
 its stages and the 2 GiB stream kernel), decode (prefill, then the decode
-layer), gated (the gated-act sweep), mx (the MXFP8 layer) or mxfp4 (the MXFP4
-layer).  --traffic-kib takes GEMM1's
+layer), gated (the gated-act sweep), mx (the MXFP8 layer), mxfp4 (the MXFP4
+layer) or bf16 (the bf16 layer).  --traffic-kib takes GEMM1's
 FETCH_SIZE and WRITE_SIZE per dispatch and the stream kernel's (KiB, as
 rocprofv3 --pmc reports them) and fills roofline.traffic from them instead of
 the readings recorded in TRAFFIC_COUNTERS.
@@ -68,11 +71,11 @@ METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roof
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "37ecebad71241c3e259cfca277a181e0283c9eb814eb36c65221538518c5550f",
-    "gemm1_fetch_kib": 5638232, "gemm1_write_kib": 157863,
+    "gemm_sources_sha256": "4cebae1191ac83d93453b528418918b2adb843f734434f50806d15e850335964",
+    "gemm1_fetch_kib": 5647966, "gemm1_write_kib": 157742,
     # GRBM_COUNT (FETCH_SIZE pass): GPU clock cycles per dispatch summed over
     # the 8 XCDs, and the dispatch's average duration under that pass
-    "gemm1_grbm_count": 35763830, "gemm1_grbm_dur_us": 2601.48,
+    "gemm1_grbm_count": 35799305, "gemm1_grbm_dur_us": 2564.16,
     "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm_kernels.h", "fp8_block_scaled_moe_amd/csrc/gemm1.hip",
@@ -98,6 +101,7 @@ def traffic_from(g1f, g1w, sf, sw):
     return traffic, note
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published (2.4 GHz)
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_CLOCK_GHZ = 2.4
 NUM_XCD = 8
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
@@ -388,6 +392,50 @@ def mx_bench(fmt, steps, warmup):
     return res
 
 
+def bf16_bench(steps, warmup):
+    """The unquantised bf16 layer on the prefill and decode shapes (packed weights, auto tiles)."""
+    d = synth.LARGE_DIMS
+    log("generating 256-expert bf16 weights on the device")
+    w13 = synth.expert_weight_set_bf16(d["E"], 2 * d["I"], d["H"], synth.CFG_LARGE, synth.TAG_W13, "cuda")
+    w2 = synth.expert_weight_set_bf16(d["E"], d["H"], d["I"], synth.CFG_LARGE, synth.TAG_W2, "cuda")
+    w13_p, w2_p = fm.pack_weights(w13), fm.pack_weights(w2)
+    del w13, w2
+    torch.cuda.empty_cache()
+    L = fm.WEIGHTS_MFMA_TILED
+    res = {}
+    for name, T, cfg in (("prefill", 8192, synth.CFG_PREFILL), ("decode", 64, synth.CFG_LARGE)):
+        x, ids, w = synth.moe_tokens_bf16(T, d["H"], d["E"], d["K"], cfg, device="cuda")
+        H, I, E, K = d["H"], d["I"], d["E"], d["K"]
+        ws = fm.alloc_workspace_bf16(T, H, I, E, K, "cuda")
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        ms = event_time_ms(lambda: fm.moe_fused_bf16(x, w13_p, w2_p, ids, w, out=out, workspace=ws, weight_layout=L),
+                           steps if name == "prefill" else max(steps, 10), warmup)
+        align = 16
+        route = fm.route_permute(ids, E, align)
+        q = fm.gemm1_swiglu_bf16(x, w13_p, route, T, K, align, weight_layout=L)
+        Y = fm.gemm2_weighted_bf16(q, w2_p, route, w, T, K, align, weight_layout=L)
+        n = max(3, steps // 2)
+        g1 = event_time_ms(lambda: fm.gemm1_swiglu_bf16(x, w13_p, route, T, K, align, weight_layout=L, q=q), n, 1)
+        g2 = event_time_ms(lambda: fm.gemm2_weighted_bf16(q, w2_p, route, w, T, K, align, weight_layout=L, Y=Y), n, 1)
+        idh = ids.cpu().numpy()
+        active = int(np.unique(idh[(idh >= 0) & (idh < E)]).size)
+        nbytes = active * 3 * H * I * 2 + 2 * T * H + 8 * T * K + 2 * T * H
+        flops = 6.0 * T * K * H * I
+        g1_tflops = 4.0 * T * K * H * I / (g1 * 1e-3) / 1e12
+        res[name] = {"us_per_layer": round(ms * 1e3, 2), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak_TFLOPs": PEAK_BF16_TFLOPS,
+                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4), "gemm1_TFLOPs": round(g1_tflops, 1),
+                     "algorithmic_bytes": int(nbytes), "active_experts": active,
+                     "workload": f"{name} T={T} H=7168 I=2048 E=256 top-8, unquantised bf16 operands"}
+        log(f"bf16 {name}", res[name])
+        del ws, out, q, Y, x
+    del w13_p, w2_p
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(p, ntok=20):
     """The CPU oracle, as it stands, on a bounded sample of prefill tokens."""
     from oracle.moe import moe_reference
@@ -418,10 +466,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the gated-act and skewed sweeps")
-    ap.add_argument("--profile", choices=("prefill", "decode", "gated", "mx", "mxfp4"), default=None,
+    ap.add_argument("--profile", choices=("prefill", "decode", "gated", "mx", "mxfp4", "bf16"), default=None,
                     help="one workload only, for rocprofv3 passes: prefill (+ stages, stream kernel), "
-                         "decode (+ stages), gated (the gated-act sweep), mx (the MXFP8 layer) or "
-                         "mxfp4 (the MXFP4 layer)")
+                         "decode (+ stages), gated (the gated-act sweep), mx (the MXFP8 layer), "
+                         "mxfp4 (the MXFP4 layer) or bf16 (the bf16 layer)")
     ap.add_argument("--traffic-kib", default=None,
                     help="gemm1_fetch,gemm1_write,stream_fetch,stream_write (KiB per dispatch, rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -432,6 +480,9 @@ def main():
     torch.cuda.init()
     if args.profile == "gated":
         print(json.dumps({"profile": "gated", "gated_act": gated_act_bench(iters=5)}), flush=True)
+        return
+    if args.profile == "bf16":
+        print(json.dumps({"profile": "bf16", "bf16": bf16_bench(args.steps, args.warmup)}), flush=True)
         return
     if args.profile in ("mx", "mxfp4"):
         fmt = "mxfp8" if args.profile == "mx" else "mxfp4"
@@ -554,6 +605,8 @@ def main():
         for fmt in ("mxfp8", "mxfp4"):
             log(f"{fmt} layer")
             result[fmt] = mx_bench(fmt, max(3, args.steps // 2), 1)
+        log("bf16 layer")
+        result["bf16"] = bf16_bench(max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = cpu_baseline(pre)
