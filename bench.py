@@ -534,7 +534,7 @@ def main():
     g1_tflops = g1_flop / (pst["gemm1_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(g1_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g1_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                "kernel": f"gemm1_swiglu_quant_kernel<{pst['tile_m_gemm1']}, true> (MFMA-tiled weights)",
+                "kernel": f"gemm1_swiglu_quant_kernel<{pst['tile_m_gemm1']}, true, false, false> (MFMA-tiled weights, FP8 block scales)",
                 "per_launch": f"4*R*H*I = {g1_flop:.4g} FLOP (R=T*K={pre.T * pre.K})",
                 "avg_launch_ms": round(pst["gemm1_ms"], 4)}
 
