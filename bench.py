@@ -18,7 +18,9 @@ The line also carries:
                 captured in one HIP graph (us_graph: no host launch overhead,
                 inputs warm in cache).
   skewed        Zipf-skewed routing (H=2048, I=768, E=128, top-8) at
-                T=1/33/512/4096: auto tile vs every forced tile_m (regret).
+                T=1/33/512/4096: auto tile vs every forced tile_m (regret),
+                and the GEMM-pair tile heights measured by tune_tiles_fp8
+                on the same routing (regret_tuned).
   stream_GBps   a plain elementwise kernel reading and writing 2 GiB each: the
                 achievable-bandwidth reference, and the kernel whose HBM
                 counters calibrate the traffic figure.
@@ -122,11 +124,13 @@ def problem(T, cfg, weights, packed=None):
     return p
 
 
-def fused(p, out, ws, packed=True, tile_m=-1):
-    """One layer call: packed weights (the production layout) or the row-major ones."""
+def fused(p, out, ws, packed=True, tile_m=-1, tile_m2=None):
+    """One layer call: packed weights (the production layout) or the row-major ones; tile_m2
+    given: separate tile heights for GEMM1 (tile_m) and GEMM2."""
     if packed:
         return fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_p, p.w13_s, p.w2_p, p.w2_s, p.topk_ids, p.topk_weights,
-                                out=out, workspace=ws, tile_m=tile_m, weight_layout=fm.WEIGHTS_MFMA_TILED)
+                                out=out, workspace=ws, tile_m=tile_m, weight_layout=fm.WEIGHTS_MFMA_TILED,
+                                tile_m2=tile_m2)
     return fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids, p.topk_weights,
                             out=out, workspace=ws, tile_m=tile_m)
 
@@ -230,7 +234,8 @@ def gated_act_bench(iters=20):
 
 
 def skewed_bench(iters=10):
-    """Zipf-skewed routing, H=2048 I=768 E=128 top-8: auto tile vs every forced tile_m, caches flushed."""
+    """Zipf-skewed routing, H=2048 I=768 E=128 top-8: auto tile vs every forced tile_m and vs the
+    measured GEMM-pair choice (tune_tiles_fp8, on the same routing), caches flushed."""
     d = synth.SKEWED_DIMS
     w13 = synth.expert_weight_set(d["E"], 2 * d["I"], d["H"], synth.CFG_SKEWED, synth.TAG_W13, "cuda")
     w2 = synth.expert_weight_set(d["E"], d["H"], d["I"], synth.CFG_SKEWED, synth.TAG_W2, "cuda")
@@ -245,8 +250,11 @@ def skewed_bench(iters=10):
         ws = fm.alloc_workspace(T, d["H"], d["I"], d["E"], d["K"], "cuda")
         o = torch.empty((T, d["H"]), dtype=torch.bfloat16, device="cuda")
         forced = (16, 32, 64, 128, 160)   # 160: GEMM1 runs 128 (its largest body)
-        configs = (-1,) + forced
-        fns = {tm: (lambda tm=tm: fused(p, o, ws, tile_m=tm)) for tm in configs}
+        t1, t2, _, _ = fm.tune_tiles_fp8(p.x_q, p.x_s, p.w13_p, p.w13_s, p.w2_p, p.w2_s, p.topk_ids,
+                                         p.topk_weights, workspace=ws, iters=5, weight_layout=fm.WEIGHTS_MFMA_TILED)
+        configs = (-1,) + forced + ("tuned",)
+        fns = {tm: (lambda tm=tm: fused(p, o, ws, tile_m=tm)) for tm in configs if tm != "tuned"}
+        fns["tuned"] = lambda: fused(p, o, ws, tile_m=t1, tile_m2=t2)
         for _ in range(3):   # warm-up of every configuration (also lets the clocks settle)
             for tm in configs:
                 fns[tm]()
@@ -261,7 +269,10 @@ def skewed_bench(iters=10):
         out.append({"T": T, "active_experts": int(active), "auto_tile_class_gemm1": auto_tm,
                     "us_auto": round(res[-1] * 1e3, 2),
                     "us_by_tile_m": {str(t): round(res[t] * 1e3, 2) for t in forced},
-                    "regret": round(res[-1] / best, 3), "GBps_auto": round(nbytes / (res[-1] * 1e-3) / 1e9, 1),
+                    "regret": round(res[-1] / best, 3),
+                    "tuned_tiles": [t1, t2], "us_tuned": round(res["tuned"] * 1e3, 2),
+                    "regret_tuned": round(res["tuned"] / best, 3),
+                    "GBps_auto": round(nbytes / (res[-1] * 1e-3) / 1e9, 1),
                     "TFLOPs_auto": round(6.0 * T * d["K"] * d["H"] * d["I"] / (res[-1] * 1e-3) / 1e12, 2)})
     return out
 

@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8moe.s
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 _pi32 = ctypes.POINTER(ctypes.c_int32)
 _psz = ctypes.POINTER(ctypes.c_size_t)
+_pi32, _pf32 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)
 
 # name -> (restype, argtypes)
 SIGNATURES = {
@@ -43,6 +44,12 @@ SIGNATURES = {
                                                     _i32, _vp, _vp, _i64, _i32, _i32, _vp]),
     "moe_gemm2_weighted_mxfp4": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                                 _i32, _vp, _i64, _i32, _i32, _i32, _vp]),
+    # x, x_scale, w13, w13_scale, w2, w2_scale, ids, weights, T, H, I, E, K, out, ws, bytes, tm1, tm2, layout, stream
+    "moe_fused_fp8_tiles": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                           _vp, _vp, _sz, _i32, _i32, _i32, _vp]),
+    # ... T, H, I, E, K, ws, bytes, layout, iters, stream, *tile_m1, *tile_m2, *ms1, *ms2
+    "moe_tune_tiles_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                          _vp, _sz, _i32, _i32, _vp, _pi32, _pi32, _pf32, _pf32]),
     "moe_fused_bf16_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
     # x, w13, w2, topk_ids, topk_weights, T, H, I, E, K, out, workspace, bytes, tile_m, tile_n, layout, stream
     "moe_fused_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _i32,

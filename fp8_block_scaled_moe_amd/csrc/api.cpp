@@ -154,21 +154,33 @@ hipError_t gemm2_launch(const uint8_t* q, const scale_ptr_t<F>* qs, const uint8_
                                 I, Y, tm, 256, packed, st);
 }
 
+// A validated fused call: the carved workspace and the launch geometry.
 template <int F>
-int fused_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, const scale_ptr_t<F>* w13_scale,
-               const void* w2, const scale_ptr_t<F>* w2_scale, const int32_t* topk_ids, const float* topk_weights,
-               int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, void* workspace,
-               size_t workspace_bytes, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
+struct FusedPlan {
+  int32_t *counts, *m_indptr, *padded, *sorted_src, *src_to_sorted;
+  uint8_t* q;
+  scale_ptr_t<F>* q_scale;
+  uint16_t* Y;
+  int64_t R, cap;
+  int align;
+  bool packed;
+};
+
+// Checks shared by the fused call and the tile tuner (everything except the
+// tile requests; the tuner writes no output); carves the workspace.  T == 0
+// passes with no plan.
+template <int F>
+int fused_prepare(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, const scale_ptr_t<F>* w13_scale,
+                  const void* w2, const scale_ptr_t<F>* w2_scale, const int32_t* topk_ids,
+                  const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, bool need_out,
+                  const void* out, void* workspace, size_t workspace_bytes, int32_t weight_layout, FusedPlan<F>& P) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;
   if ((st = check_format_dims<F>(H, I))) return st;
   if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
-  const bool packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
-  if (tile_m != -1 && !valid_tile_m(tile_m))
-    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m);
-  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
-  if (T == 0) return ok();
-  if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !out ||
+  P.packed = weight_layout == FP8MOE_WEIGHTS_MFMA_TILED;
+  if (T == 0) return FP8MOE_OK;
+  if (!x || !w13 || !w2 || !topk_ids || !topk_weights || (need_out && !out) ||
       (F != kFmtBf16 && (!x_scale || !w13_scale || !w2_scale)))
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
   const WsLayout L = ws_layout(T, H, I, E, K, F);
@@ -176,38 +188,154 @@ int fused_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, co
   if ((uintptr_t)workspace % kAlignWs) return fail(FP8MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < L.total)
     return fail(FP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
-
-  const int64_t R = T * K;
-  const int tm1 = pick_tile_m(tile_m, R, I, H, E, true);
-  const int tm2 = pick_tile_m(tile_m, R, H, I, E, false);
   // segments padded to 16 rows only: the GEMMs cover each expert with tiles
-  // of up to tm rows and one shorter last tile
-  const int align = 16;
-  const int64_t cap = R + (int64_t)E * (align - 1);
-
+  // of equal height up to the tile height
+  P.R = T * K;
+  P.align = 16;
+  P.cap = P.R + (int64_t)E * (P.align - 1);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  int32_t* m_indptr = reinterpret_cast<int32_t*>(ws + L.m_indptr);
-  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
-  int32_t* sorted_src = reinterpret_cast<int32_t*>(ws + L.sorted_src);
-  int32_t* src_to_sorted = reinterpret_cast<int32_t*>(ws + L.src_to_sorted);
-  uint8_t* q = ws + L.q;
-  scale_ptr_t<F>* q_scale = reinterpret_cast<scale_ptr_t<F>*>(ws + L.q_scale);
-  uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
-  hipStream_t s = (hipStream_t)stream;
+  P.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  P.m_indptr = reinterpret_cast<int32_t*>(ws + L.m_indptr);
+  P.padded = reinterpret_cast<int32_t*>(ws + L.padded);
+  P.sorted_src = reinterpret_cast<int32_t*>(ws + L.sorted_src);
+  P.src_to_sorted = reinterpret_cast<int32_t*>(ws + L.src_to_sorted);
+  P.q = ws + L.q;
+  P.q_scale = reinterpret_cast<scale_ptr_t<F>*>(ws + L.q_scale);
+  P.Y = reinterpret_cast<uint16_t*>(ws + L.Y);
+  return FP8MOE_OK;
+}
 
-  hipError_t err = launch_route_permute(topk_ids, (int)R, E, align, (int)cap, counts, m_indptr, padded,
-                                        sorted_src, src_to_sorted, s);
+int check_tile_requests(int32_t tile_m1, int32_t tile_m2, int32_t tile_n) {
+  if (tile_m1 != -1 && !valid_tile_m(tile_m1))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m1);
+  if (tile_m2 != -1 && !valid_tile_m(tile_m2))
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64,128,144,160}", tile_m2);
+  if (tile_n != -1 && tile_n != 256) return fail(FP8MOE_ERR_TILE, "tile_n %d not in {-1,256}", tile_n);
+  return FP8MOE_OK;
+}
+
+// The fused layer with tile height requests for GEMM1 (tile_m1) and GEMM2
+// (tile_m2); -1 = the cost model's choice.
+template <int F>
+int fused_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, const scale_ptr_t<F>* w13_scale,
+               const void* w2, const scale_ptr_t<F>* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+               int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, void* workspace,
+               size_t workspace_bytes, int32_t tile_m1, int32_t tile_m2, int32_t tile_n, int32_t weight_layout,
+               void* stream) {
+  FusedPlan<F> P{};
+  int st = fused_prepare<F>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, true,
+                            out, workspace, workspace_bytes, weight_layout, P);
+  if (st) return st;
+  if ((st = check_tile_requests(tile_m1, tile_m2, tile_n))) return st;
+  if (T == 0) return ok();
+  const int tm1 = pick_tile_m(tile_m1, P.R, I, H, E, true);
+  const int tm2 = pick_tile_m(tile_m2, P.R, H, I, E, false);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_route_permute(topk_ids, (int)P.R, E, P.align, (int)P.cap, P.counts, P.m_indptr, P.padded,
+                                        P.sorted_src, P.src_to_sorted, s);
   if (err != hipSuccess) return hip_fail(err, "route_permute launch");
-  GroupedRows g{padded, sorted_src, cap, E, K, R, device_num_cu()};
+  GroupedRows g{P.padded, P.sorted_src, P.cap, E, K, P.R, device_num_cu()};
   err = gemm1_launch<F>(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale, g, H,
-                        I, q, q_scale, tm1, packed, s);
+                        I, P.q, P.q_scale, tm1, P.packed, s);
   if (err != hipSuccess) return hip_fail(err, "gemm1 launch");
-  err = gemm2_launch<F>(q, q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, Y, tm2,
-                        packed, s);
+  err = gemm2_launch<F>(P.q, P.q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, P.Y, tm2,
+                        P.packed, s);
   if (err != hipSuccess) return hip_fail(err, "gemm2 launch");
-  err = launch_combine(Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
+  err = launch_combine(P.Y, topk_ids, (int)T, H, E, K, static_cast<uint16_t*>(out), s);
   if (err != hipSuccess) return hip_fail(err, "combine launch");
+  return ok();
+}
+
+// Average time (ms) of `iters` launches of fn after one warm-up launch, timed
+// with events on stream s; a negative value if a launch failed.
+template <typename Fn>
+float time_launches(Fn fn, int iters, hipStream_t s, hipEvent_t a, hipEvent_t b, hipError_t* err) {
+  *err = fn();
+  if (*err != hipSuccess) return -1.f;
+  if ((*err = hipEventRecord(a, s)) != hipSuccess) return -1.f;
+  for (int i = 0; i < iters; ++i)
+    if ((*err = fn()) != hipSuccess) return -1.f;
+  if ((*err = hipEventRecord(b, s)) != hipSuccess) return -1.f;
+  if ((*err = hipEventSynchronize(b)) != hipSuccess) return -1.f;
+  float ms = 0.f;
+  if ((*err = hipEventElapsedTime(&ms, a, b)) != hipSuccess) return -1.f;
+  return ms / iters;
+}
+
+// Staged GEMM-pair tuning (cuTile page, review notes on its autotuner: GEMM1
+// and GEMM2 tuned as a pair, an explicit error when no candidate survives):
+// route once, time GEMM1 at every tile height, then GEMM2 at every tile
+// height on GEMM1's output.  Every tile height gives bit-identical results,
+// so the choice is purely one of speed.
+template <int F>
+int tune_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, const scale_ptr_t<F>* w13_scale,
+              const void* w2, const scale_ptr_t<F>* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+              int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* workspace, size_t workspace_bytes,
+              int32_t weight_layout, int32_t iters, void* stream, int32_t* tile_m1, int32_t* tile_m2, float* ms1,
+              float* ms2) {
+  if (!tile_m1 || !tile_m2) return fail(FP8MOE_ERR_NULL, "null tile output");
+  if (iters < 1 || iters > 1000) return fail(FP8MOE_ERR_SHAPE, "iters %d not in [1, 1000]", iters);
+  FusedPlan<F> P{};
+  int st = fused_prepare<F>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, false,
+                            nullptr, workspace, workspace_bytes, weight_layout, P);
+  if (st) return st;
+  if (T == 0) {   // nothing to time: the cost model's choice for no rows, the narrow class
+    *tile_m1 = *tile_m2 = mi355x_classes(true).narrow;
+    if (ms1) *ms1 = 0.f;
+    if (ms2) *ms2 = 0.f;
+    return ok();
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_route_permute(topk_ids, (int)P.R, E, P.align, (int)P.cap, P.counts, P.m_indptr, P.padded,
+                                        P.sorted_src, P.src_to_sorted, s);
+  if (err != hipSuccess) return hip_fail(err, "route_permute launch");
+  GroupedRows g{P.padded, P.sorted_src, P.cap, E, K, P.R, device_num_cu()};
+  hipEvent_t a, b;
+  if ((err = hipEventCreate(&a)) != hipSuccess) return hip_fail(err, "hipEventCreate");
+  if ((err = hipEventCreate(&b)) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return hip_fail(err, "hipEventCreate");
+  }
+  static const int kTiles1[] = {16, 32, 64, 128};
+  static const int kTiles2[] = {16, 32, 64, 128, 144, 160};
+  int best1 = -1, best2 = -1;
+  float t1 = 0.f, t2 = 0.f;
+  hipError_t last = hipSuccess;
+  for (int tm : kTiles1) {
+    if (tm > kMaxTileGemm1) continue;
+    const float ms = time_launches([&] {
+      return gemm1_launch<F>(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale, g,
+                             H, I, P.q, P.q_scale, tm, P.packed, s);
+    }, iters, s, a, b, &err);
+    if (ms < 0.f) {
+      last = err;
+      continue;
+    }
+    if (best1 < 0 || ms < t1) best1 = tm, t1 = ms;
+  }
+  // GEMM2 reads the intermediate the last GEMM1 launch wrote (identical for every tile height)
+  if (best1 > 0) {
+    for (int tm : kTiles2) {
+      const float ms = time_launches([&] {
+        return gemm2_launch<F>(P.q, P.q_scale, static_cast<const uint8_t*>(w2), w2_scale, topk_weights, g, H, I, P.Y,
+                               tm, P.packed, s);
+      }, iters, s, a, b, &err);
+      if (ms < 0.f) {
+        last = err;
+        continue;
+      }
+      if (best2 < 0 || ms < t2) best2 = tm, t2 = ms;
+    }
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  if (best1 < 0 || best2 < 0)
+    return fail(FP8MOE_ERR_TILE, "no tile candidate of %s ran (%s)", best1 < 0 ? "GEMM1" : "GEMM2",
+                hipGetErrorString(last));
+  *tile_m1 = best1;
+  *tile_m2 = best2;
+  if (ms1) *ms1 = t1;
+  if (ms2) *ms2 = t2;
   return ok();
 }
 
@@ -331,7 +459,25 @@ int moe_fused_fp8(const void* x, const float* x_scale, const void* w13, const fl
                   void* out, void* workspace, size_t workspace_bytes, int32_t tile_m, int32_t tile_n,
                   int32_t weight_layout, void* stream) {
   return fused_impl<kFmtFp8>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, out,
-                           workspace, workspace_bytes, tile_m, tile_n, weight_layout, stream);
+                           workspace, workspace_bytes, tile_m, tile_m, tile_n, weight_layout, stream);
+}
+
+int moe_fused_fp8_tiles(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, const int32_t* topk_ids,
+                        const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                        void* out, void* workspace, size_t workspace_bytes, int32_t tile_m1, int32_t tile_m2,
+                        int32_t weight_layout, void* stream) {
+  return fused_impl<kFmtFp8>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, out,
+                             workspace, workspace_bytes, tile_m1, tile_m2, -1, weight_layout, stream);
+}
+
+int moe_tune_tiles_fp8(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                       const void* w2, const float* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+                       int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* workspace,
+                       size_t workspace_bytes, int32_t weight_layout, int32_t iters, void* stream,
+                       int32_t* tile_m1, int32_t* tile_m2, float* ms1, float* ms2) {
+  return tune_impl<kFmtFp8>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K,
+                            workspace, workspace_bytes, weight_layout, iters, stream, tile_m1, tile_m2, ms1, ms2);
 }
 
 int moe_fused_mxfp8(const void* x, const uint8_t* x_sf, const void* w13, const uint8_t* w13_sf, const void* w2,
@@ -339,7 +485,7 @@ int moe_fused_mxfp8(const void* x, const uint8_t* x_sf, const void* w13, const u
                     int32_t I, int32_t E, int32_t K, void* out, void* workspace, size_t workspace_bytes,
                     int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
   return fused_impl<kFmtMx8>(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, T, H, I, E, K, out, workspace,
-                          workspace_bytes, tile_m, tile_n, weight_layout, stream);
+                          workspace_bytes, tile_m, tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_gemm1_swiglu_quant(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
@@ -386,7 +532,7 @@ int moe_fused_bf16(const void* x, const void* w13, const void* w2, const int32_t
                    int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, void* workspace,
                    size_t workspace_bytes, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
   return fused_impl<kFmtBf16>(x, nullptr, w13, nullptr, w2, nullptr, topk_ids, topk_weights, T, H, I, E, K, out,
-                              workspace, workspace_bytes, tile_m, tile_n, weight_layout, stream);
+                              workspace, workspace_bytes, tile_m, tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_gemm1_swiglu_bf16(const void* x, const void* w13, const int32_t* padded_indptr, const int32_t* sorted_src,
@@ -500,7 +646,7 @@ int moe_fused_mxfp4(const void* x, const uint8_t* x_sf, const void* w13, const u
                     int32_t I, int32_t E, int32_t K, void* out, void* workspace, size_t workspace_bytes,
                     int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream) {
   return fused_impl<kFmtMx4>(x, x_sf, w13, w13_sf, w2, w2_sf, topk_ids, topk_weights, T, H, I, E, K, out, workspace,
-                             workspace_bytes, tile_m, tile_n, weight_layout, stream);
+                             workspace_bytes, tile_m, tile_m, tile_n, weight_layout, stream);
 }
 
 int moe_gemm1_swiglu_quant_mxfp4(const void* x, const uint8_t* x_sf, const void* w13, const uint8_t* w13_sf,

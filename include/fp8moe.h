@@ -407,6 +407,50 @@ int moe_select_tile_classes(int64_t total_rows, int32_t n, int32_t k, int32_t E,
                             int32_t narrow, int32_t tile_n_narrow, int32_t tile_n_32,
                             int32_t tile_n_64, int32_t tile_n_128, int32_t* tile_m);
 
+/* ---------------------------------------------------------------- measured tile choice
+ * moe_tune_tiles_fp8: staged GEMM-pair tuning for one concrete problem (the
+ * cuTile page's autotuner, which tunes GEMM1 and GEMM2 as a pair; its
+ * review notes ask for an explicit error when no candidate survives).
+ *
+ * Runs routing once. It then times GEMM1 at every tile height (16, 32, 64,
+ * 128), and GEMM2 at every tile height (16, 32, 64, 128, 144, 160) on GEMM1's
+ * output. Each candidate gets one warm-up launch and then `iters` timed
+ * launches, in [1, 1000], with HIP events on `stream`.
+ *
+ * Outputs:
+ *   *tile_m1, *tile_m2  the fastest tile height of each GEMM;
+ *   *ms1, *ms2          their average launch times (nullable).
+ * Every tile height gives bit-identical results, so the choice is only one
+ * of speed. It holds for the routing it was measured on, and serves routings
+ * of the same shape and skew.
+ *
+ * Arguments, layouts and the workspace (moe_fused_fp8_workspace_size bytes,
+ * overwritten) are as for moe_fused_fp8; no output tensor is written. T == 0
+ * times nothing and returns 16 for both (the cost model's choice for no rows).
+ *
+ * This is a set-up call, not one for the hot path: it waits on events (the
+ * host blocks), creates and destroys two events, and allocates no device
+ * memory. Candidates whose launch fails are skipped. FP8MOE_ERR_TILE (with
+ * the last launch error in moe_last_error) if no candidate of a GEMM ran;
+ * other errors as for moe_fused_fp8.
+ */
+int moe_tune_tiles_fp8(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                       const void* w2, const float* w2_scale, const int32_t* topk_ids,
+                       const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                       void* workspace, size_t workspace_bytes, int32_t weight_layout, int32_t iters,
+                       void* stream, int32_t* tile_m1, int32_t* tile_m2, float* ms1, float* ms2);
+
+/* moe_fused_fp8_tiles: moe_fused_fp8 with separate tile heights for GEMM1
+ * (tile_m1) and GEMM2 (tile_m2), e.g. those moe_tune_tiles_fp8 returned.
+ * Each is -1 (the cost model's choice) or one of 16, 32, 64, 128, 144 and
+ * 160; GEMM1 caps it at 128. tile_n is 256. Everything else is as for
+ * moe_fused_fp8. */
+int moe_fused_fp8_tiles(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, const int32_t* topk_ids,
+                        const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                        void* out, void* workspace, size_t workspace_bytes, int32_t tile_m1, int32_t tile_m2,
+                        int32_t weight_layout, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

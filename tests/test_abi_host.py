@@ -191,6 +191,37 @@ def test_bf16_validation():
     assert g2(layout=3) == E_SHAPE
 
 
+def test_tune_tiles_and_fused_tiles_validation():
+    L = lib()
+    t1, t2 = ctypes.c_int32(-7), ctypes.c_int32(-7)
+    m1, m2 = ctypes.c_float(-1), ctypes.c_float(-1)
+    def tune(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, layout=0, iters=3, o1=None, o2=None):
+        return L.moe_tune_tiles_fp8(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, ws, wsb, layout, iters,
+                                    NULL, ctypes.byref(t1) if o1 is None else o1,
+                                    ctypes.byref(t2) if o2 is None else o2, ctypes.byref(m1), ctypes.byref(m2))
+    assert tune(iters=0) == E_SHAPE
+    assert tune(iters=1001) == E_SHAPE
+    assert tune(o1=ctypes.POINTER(ctypes.c_int32)()) == E_NULL
+    assert tune(o2=ctypes.POINTER(ctypes.c_int32)()) == E_NULL
+    assert tune(H=200) == E_ALIGN
+    assert tune(K=9) == E_TOPK
+    assert tune(layout=2) == E_SHAPE
+    assert tune(ptr=NULL) == E_NULL
+    assert tune(ws=NULL) == E_WS
+    assert tune(wsb=1024) == E_WS
+    # nothing to time: the narrow class for both, no device call
+    assert tune(T=0, ptr=NULL, ws=NULL) == OK
+    assert (t1.value, t2.value, m1.value, m2.value) == (16, 16, 0.0, 0.0)
+
+    def fused(tm1=-1, tm2=-1, T=16, ptr=FAKE, out=FAKE):
+        return L.moe_fused_fp8_tiles(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, 256, 128, 4, 2, out, FAKE, 1 << 40,
+                                     tm1, tm2, 0, NULL)
+    assert fused(tm1=48) == E_TILE
+    assert fused(tm2=96) == E_TILE
+    assert fused(out=NULL) == E_NULL
+    assert fused(T=0, ptr=NULL, out=NULL) == OK
+
+
 def test_workspace_size_bf16():
     nb = fm.fused_bf16_workspace_size(16, 256, 128, 4, 2)
     R, cap = 32, 32 + 4 * 127
