@@ -11,7 +11,8 @@ The line also carries:
                 per launch / average launch time, against the dense fp8 MFMA
                 peak (5.0 PFLOP/s).
   decode        the same layer at T=64 (HBM-bound: expert weights streamed),
-                us per layer and algorithmic GB/s against 8 TB/s.
+                us per layer and algorithmic GB/s against 8 TB/s; also the
+                two-launch small-T layer (us_per_layer_two_launch).
   gated_act     the standalone SwiGLU + MXFP8 quantiser on the four shapes and
                 two input distributions: one launch with the caches flushed
                 before it (us, GBps), and the per-launch time of 100 launches
@@ -20,7 +21,8 @@ The line also carries:
   skewed        Zipf-skewed routing (H=2048, I=768, E=128, top-8) at
                 T=1/33/512/4096: auto tile vs every forced tile_m (regret),
                 and the GEMM-pair tile heights measured by tune_tiles_fp8
-                on the same routing (regret_tuned).
+                on the same routing (regret_tuned), and the two-launch
+                small-T layer (us_two_launch, T*K <= 4096).
   stream_GBps   a plain elementwise kernel reading and writing 2 GiB each: the
                 achievable-bandwidth reference, and the kernel whose HBM
                 counters calibrate the traffic figure.
@@ -252,9 +254,16 @@ def skewed_bench(iters=10):
         forced = (16, 32, 64, 128, 160)   # 160: GEMM1 runs 128 (its largest body)
         t1, t2, _, _ = fm.tune_tiles_fp8(p.x_q, p.x_s, p.w13_p, p.w13_s, p.w2_p, p.w2_s, p.topk_ids,
                                          p.topk_weights, workspace=ws, iters=5, weight_layout=fm.WEIGHTS_MFMA_TILED)
-        configs = (-1,) + forced + ("tuned",)
-        fns = {tm: (lambda tm=tm: fused(p, o, ws, tile_m=tm)) for tm in configs if tm != "tuned"}
+        small = T * d["K"] <= 4096   # the two-launch layer's limit
+        configs = (-1,) + forced + ("tuned",) + (("two_launch",) if small else ())
+        fns = {tm: (lambda tm=tm: fused(p, o, ws, tile_m=tm)) for tm in configs if tm not in ("tuned", "two_launch")}
         fns["tuned"] = lambda: fused(p, o, ws, tile_m=t1, tile_m2=t2)
+        if small:
+            wss = torch.empty(fm.fused_small_workspace_size(T, d["H"], d["I"], d["E"], d["K"]), dtype=torch.uint8,
+                              device="cuda")
+            fns["two_launch"] = lambda: fm.moe_fused_fp8_small(p.x_q, p.x_s, p.w13_p, p.w13_s, p.w2_p, p.w2_s,
+                                                               p.topk_ids, p.topk_weights, out=o, workspace=wss,
+                                                               weight_layout=fm.WEIGHTS_MFMA_TILED)
         for _ in range(3):   # warm-up of every configuration (also lets the clocks settle)
             for tm in configs:
                 fns[tm]()
@@ -272,6 +281,7 @@ def skewed_bench(iters=10):
                     "regret": round(res[-1] / best, 3),
                     "tuned_tiles": [t1, t2], "us_tuned": round(res["tuned"] * 1e3, 2),
                     "regret_tuned": round(res["tuned"] / best, 3),
+                    "us_two_launch": round(res["two_launch"] * 1e3, 2) if small else None,
                     "GBps_auto": round(nbytes / (res[-1] * 1e-3) / 1e9, 1),
                     "TFLOPs_auto": round(6.0 * T * d["K"] * d["H"] * d["I"] / (res[-1] * 1e-3) / 1e12, 2)})
     return out
@@ -581,8 +591,18 @@ def main():
     dbytes, dactive = algorithmic_bytes(dec)
     dgbs = dbytes / (dms * 1e-3) / 1e9
     dst = stage_times(dec, max(5, args.steps // 2), 2)
-    log(f"decode {dms * 1e3:.1f} us/layer, {dgbs:.0f} GB/s ({dactive} active experts)", dst)
+    # the same layer in two launches (routing + one persistent cooperative kernel)
+    wss = torch.empty(fm.fused_small_workspace_size(dec.T, dec.H, dec.I, dec.E, dec.K), dtype=torch.uint8,
+                      device="cuda")
+    sms = event_time_ms(lambda: fm.moe_fused_fp8_small(dec.x_q, dec.x_s, dec.w13_p, dec.w13_s, dec.w2_p, dec.w2_s,
+                                                       dec.topk_ids, dec.topk_weights, out=outd, workspace=wss,
+                                                       weight_layout=fm.WEIGHTS_MFMA_TILED),
+                        max(args.steps, 10), args.warmup)
+    del wss
+    log(f"decode {dms * 1e3:.1f} us/layer, {dgbs:.0f} GB/s ({dactive} active experts); two-launch "
+        f"{sms * 1e3:.1f} us", dst)
     decode = {"us_per_layer": round(dms * 1e3, 2), "GBps": round(dgbs, 1), "frac_hbm": round(dgbs / PEAK_HBM_GBS, 4),
+              "us_per_layer_two_launch": round(sms * 1e3, 2),
               "algorithmic_bytes": dbytes, "active_experts": int(dactive), "stages_ms": dst,
               "workload": "decode T=64 H=7168 I=2048 E=256 top-8"}
     if args.profile == "decode":

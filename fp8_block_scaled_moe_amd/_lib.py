@@ -50,6 +50,10 @@ SIGNATURES = {
     # ... T, H, I, E, K, ws, bytes, layout, iters, stream, *tile_m1, *tile_m2, *ms1, *ms2
     "moe_tune_tiles_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                           _vp, _sz, _i32, _i32, _vp, _pi32, _pi32, _pf32, _pf32]),
+    "moe_fused_fp8_small_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
+    # x, x_scale, w13, w13_scale, w2, w2_scale, ids, weights, T, H, I, E, K, out, ws, bytes, tile_m, layout, stream
+    "moe_fused_fp8_small": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                           _vp, _vp, _sz, _i32, _i32, _vp]),
     "moe_fused_bf16_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
     # x, w13, w2, topk_ids, topk_weights, T, H, I, E, K, out, workspace, bytes, tile_m, tile_n, layout, stream
     "moe_fused_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _i32,

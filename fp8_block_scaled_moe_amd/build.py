@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8moe.so")
 
 SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm1.hip", "gemm2.hip", "gemm1_mx.hip", "gemm2_mx.hip", "gemm1_mxfp4.hip",
-           "gemm2_mxfp4.hip", "gemm1_bf16.hip", "gemm2_bf16.hip", "gemm_plain.hip",
+           "gemm2_mxfp4.hip", "gemm1_bf16.hip", "gemm2_bf16.hip", "gemm_plain.hip", "fused_small.hip",
            "combine.hip", "gated_act.hip", "pack.hip"]
 
 ARCH = "gfx950"

@@ -471,6 +471,54 @@ int moe_fused_fp8_tiles(const void* x, const float* x_scale, const void* w13, co
                              workspace, workspace_bytes, tile_m1, tile_m2, -1, weight_layout, stream);
 }
 
+int moe_fused_fp8_small_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, size_t* bytes) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (!bytes) return fail(FP8MOE_ERR_NULL, "bytes is null");
+  *bytes = ws_layout(T, H, I, E, K, kFmtFp8).total + kAlignWs;   // + barrier counter and error flag
+  return ok();
+}
+
+int moe_fused_fp8_small(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, const int32_t* topk_ids,
+                        const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                        void* out, void* workspace, size_t workspace_bytes, int32_t tile_m, int32_t weight_layout,
+                        void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  if (T * K > kRouteOneBlockRows)
+    return fail(FP8MOE_ERR_LIMIT, "the small-T layer takes T*K <= %d routed rows (got %lld)", kRouteOneBlockRows,
+                (long long)(T * K));
+  if (tile_m != -1 && tile_m != 16 && tile_m != 32 && tile_m != 64)
+    return fail(FP8MOE_ERR_TILE, "tile_m %d not in {-1,16,32,64}", tile_m);
+  const size_t need = ws_layout(T, H, I, E, K, kFmtFp8).total;
+  if (T > 0 && workspace_bytes < need + kAlignWs)
+    return fail(FP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need + kAlignWs);
+  FusedPlan<kFmtFp8> P{};
+  st = fused_prepare<kFmtFp8>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, true,
+                              out, workspace, workspace_bytes, weight_layout, P);
+  if (st) return st;
+  if (T == 0) return ok();
+  // one tile height for both GEMMs: the requested one, else the larger of the cost model's two, at most 64
+  int tm = tile_m;
+  if (tm == -1) {
+    const int a = pick_tile_m(-1, P.R, I, H, E, true), b = pick_tile_m(-1, P.R, H, I, E, false);
+    tm = a > b ? a : b;
+    tm = tm > 64 ? 64 : tm;
+  }
+  uint32_t* ctr_err = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + need);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_route_permute(topk_ids, (int)P.R, E, P.align, (int)P.cap, P.counts, P.m_indptr, P.padded,
+                                        P.sorted_src, P.src_to_sorted, s, ctr_err);
+  if (err != hipSuccess) return hip_fail(err, "route_permute launch");
+  GroupedRows g{P.padded, P.sorted_src, P.cap, E, K, P.R, device_num_cu()};
+  err = launch_moe_small(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13), w13_scale,
+                         static_cast<const uint8_t*>(w2), w2_scale, topk_ids, topk_weights, g, (int)T, H, I, P.q,
+                         P.q_scale, P.Y, static_cast<uint16_t*>(out), ctr_err, tm, P.packed, s);
+  if (err != hipSuccess) return hip_fail(err, "small-T layer cooperative launch");
+  return ok();
+}
+
 int moe_tune_tiles_fp8(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
                        const void* w2, const float* w2_scale, const int32_t* topk_ids, const float* topk_weights,
                        int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* workspace,

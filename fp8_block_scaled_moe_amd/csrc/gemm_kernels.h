@@ -77,6 +77,7 @@
 // takes tile (b % 8) * per_xcd + b / 8 of the expert-major (m-tile, n-tile)
 // list, so each XCD streams a contiguous range of experts and the m-tiles of
 // one expert run together, sharing every weight tile through that L2.
+#include "combine_body.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -282,11 +283,11 @@ struct ChunkTiles {
 // ordered expert-major, then N run, then M tile, so expert e's items start at
 // NG * (tiles of experts before e).  One round of coalesced loads per 256
 // experts and a wave scan (all waves compute the same values).
+// Work items (M tiles x N runs) of a launch: the first chunk of experts'
+// tile counts (kept for the search in tile_coord_from) and the item count.
 template <int TMAX>
-__device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
-                                           const int32_t* __restrict__ sorted_src, int E, int NG, TileCoord& tc) {
+__device__ __forceinline__ int tile_items(const int32_t* __restrict__ padded, int E, int NG, ChunkTiles<TMAX>& ch) {
   const int lane = threadIdx.x & 63;
-  ChunkTiles<TMAX> ch;
   ch.load(padded, E, 0, lane);
   int tot = ch.total;
   for (int c = 256; c < E; c += 256) {   // more than 256 experts: one more round per 256
@@ -294,9 +295,33 @@ __device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
     more.load(padded, E, c, lane);
     tot += more.total;
   }
-  const int items = __builtin_amdgcn_readfirstlane(tot) * NG;   // uniform: every lane holds the totals
+  return __builtin_amdgcn_readfirstlane(tot) * NG;   // uniform: every lane holds the totals
+}
+
+// Workgroup slots the XCD-aware mapping spreads `items` over.
+__device__ __forceinline__ int tile_slots(int items) { return (items + kNumXcd - 1) / kNumXcd * kNumXcd; }
+
+template <int TMAX>
+__device__ __forceinline__ bool tile_coord_from(const int32_t* __restrict__ padded,
+                                                const int32_t* __restrict__ sorted_src, int E, int NG, int items,
+                                                int b, ChunkTiles<TMAX> ch, TileCoord& tc);
+
+template <int TMAX>
+__device__ __forceinline__ bool tile_coord(const int32_t* __restrict__ padded,
+                                           const int32_t* __restrict__ sorted_src, int E, int NG, TileCoord& tc) {
+  ChunkTiles<TMAX> ch;
+  const int items = tile_items<TMAX>(padded, E, NG, ch);
+  return tile_coord_from<TMAX>(padded, sorted_src, E, NG, items, blockIdx.x, ch, tc);
+}
+
+// The tile of workgroup slot b (b % 8 = its XCD); ch holds the first chunk of
+// experts' tile counts, as tile_items left it.
+template <int TMAX>
+__device__ __forceinline__ bool tile_coord_from(const int32_t* __restrict__ padded,
+                                                const int32_t* __restrict__ sorted_src, int E, int NG, int items,
+                                                int b, ChunkTiles<TMAX> ch, TileCoord& tc) {
+  const int lane = threadIdx.x & 63;
   const int per_xcd = (items + kNumXcd - 1) / kNumXcd;
-  const int b = blockIdx.x;
   const int slot = b / kNumXcd;
   const int L = (b % kNumXcd) * per_xcd + slot;
   if (slot >= per_xcd || L >= items) return false;
@@ -1244,6 +1269,107 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_plain_kernel(
 #undef FP8MOE_PP_BODY
   }
 }
+// ------------------------------------------------------------------------------------------
+// The FP8 layer for small T in one persistent launch (after routing): the
+// GEMM1 tiles, a grid barrier, the GEMM2 tiles, a grid barrier, the combine.
+// Launched cooperatively with at most as many workgroups as can be resident
+// (and no more than the tiles need), each looping over the workgroup slots
+// b, b + gridDim.x, ... of the XCD-aware tile mapping (gridDim.x is a
+// multiple of 8, so every slot a workgroup takes lies on its own XCD).  The arithmetic of every output is
+// that of the separate kernels, so the results are bit-identical.
+
+// Spin limit of the grid barrier (~1 s); only reached if a workgroup never
+// arrives, which a cooperative launch rules out.
+constexpr long kGridBarrierSpins = 1L << 24;
+
+// Barrier words of the small-T layer (zeroed by the routing launch): one
+// arrival counter per group of workgroups (blockIdx.x % 8, the XCD the
+// workgroup runs on), a top counter of completed groups, the error flag.
+constexpr int kBarrierGroups = kNumXcd;
+constexpr int kBarrierTop = kBarrierGroups, kBarrierErr = kBarrierGroups + 1, kBarrierWords = kBarrierGroups + 2;
+static_assert(kBarrierWords <= kSmallBarrierWords, "the routing launch zeroes the barrier words");
+
+// Grid barrier number `phase` (1, 2, ...; the counters count up across the
+// launch).  Each workgroup arrives on its group's counter; the last arrival of
+// a group (gridDim.x / 8 workgroups) bumps the top counter, and everyone polls
+// the top counter until all 8 groups are in: 32 + 8 contending atomics
+// instead of 256 on one address.  Thread 0 releases the workgroup's global
+// writes at agent scope (all XCDs) before it arrives, polls with relaxed loads
+// (an acquire per poll would invalidate the XCD's L2 under the workgroups
+// still computing), then acquires once.  On a timeout it sets the error flag
+// and goes on, so every workgroup still ends.
+__device__ __forceinline__ void grid_barrier(uint32_t* words, uint32_t phase) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores complete (the tile bodies end with vmcnt(0) too)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t per_group = gridDim.x / kBarrierGroups;
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(words + blockIdx.x % kBarrierGroups, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived + 1 == per_group * phase)
+      __hip_atomic_fetch_add(words + kBarrierTop, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = kBarrierGroups * phase;
+    long spins = 0;
+    while (__hip_atomic_load(words + kBarrierTop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++spins > kGridBarrierSpins) {
+        __hip_atomic_store(words + kBarrierErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+template <int TMAX, bool PACKED>
+__global__ __launch_bounds__(kThreads) void moe_small_kernel(
+    const uint8_t* __restrict__ x, const float* __restrict__ x_scale, const uint8_t* __restrict__ w13,
+    const float* __restrict__ w13_scale, const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
+    const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_weights, const int32_t* __restrict__ padded,
+    const int32_t* __restrict__ sorted_src, int T, int E, int K, int H, int I, int NB1, int NB2,
+    uint8_t* __restrict__ q, float* __restrict__ q_scale, uint16_t* __restrict__ Y, uint16_t* __restrict__ out,
+    uint32_t* __restrict__ ctr_err) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  FP8MOE_TOKEN_BUFFERS(TMAX);
+  {  // GEMM1 + SwiGLU + requant over every tile
+    const int NT = I / 128, NG = (NT + NB1 - 1) / NB1;
+    ChunkTiles<TMAX> ch;
+    const int items = tile_items<TMAX>(padded, E, NG, ch);
+    for (int b = blockIdx.x; b < tile_slots(items); b += gridDim.x) {
+      TileCoord tc;
+      if (!tile_coord_from<TMAX>(padded, sorted_src, E, NG, items, b, ch, tc)) continue;
+#define FP8MOE_S1_BODY(TMV) \
+  gemm1_tile<TMV, PACKED, false>(smem, tb, tc, x, x_scale, w13, w13_scale, sorted_src, K, H, I, NB1, q, q_scale)
+      FP8MOE_BODIES(FP8MOE_S1_BODY)
+#undef FP8MOE_S1_BODY
+      __syncthreads();   // the next tile restages the LDS
+    }
+  }
+  grid_barrier(ctr_err, 1u);
+  {  // GEMM2 with the top-k weight epilogue over every tile
+    const int NT = (H + kTN - 1) / kTN, NG = (NT + NB2 - 1) / NB2;
+    ChunkTiles<TMAX> ch;
+    const int items = tile_items<TMAX>(padded, E, NG, ch);
+    for (int b = blockIdx.x; b < tile_slots(items); b += gridDim.x) {
+      TileCoord tc;
+      if (!tile_coord_from<TMAX>(padded, sorted_src, E, NG, items, b, ch, tc)) continue;
+#define FP8MOE_S2_BODY(TMV) \
+  gemm2_tile<TMV, PACKED, false>(smem, tb, tc, q, q_scale, w2, w2_scale, topk_weights, sorted_src, H, I, NB2, Y)
+      FP8MOE_BODIES(FP8MOE_S2_BODY)
+#undef FP8MOE_S2_BODY
+      __syncthreads();
+    }
+  }
+  grid_barrier(ctr_err, 2u);
+  // combine: one 8-column chunk per thread and step
+  const int chunks = H / 8;
+  const int64_t total = (int64_t)T * chunks;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int t = (int)(i / chunks);
+    combine_chunk(Y, topk_ids, t, (int)(i - (int64_t)t * chunks), H, E, K, out);
+  }
+}
+
 #undef FP8MOE_TOKEN_BUFFERS
 #undef FP8MOE_BODIES
 
@@ -1392,84 +1518,6 @@ static hipError_t launch_gemm2_t(const uint8_t* q, const scale_t<MX>* q_scale, c
     default: return hipErrorInvalidValue;
   }
 #undef FP8MOE_G2
-  return hipGetLastError();
-}
-
-// bf16 launchers: KT = 2H / 128 (GEMM1) and 2I / 128 (GEMM2) 128-byte K
-// steps; same tiles, runs and grids as the quantised variants.
-static hipError_t launch_gemm1_bf16_t(const uint8_t* x, const uint8_t* w13, const GroupedRows& g, int H, int I,
-                                      uint16_t* q, int tile_m, bool packed, hipStream_t stream) {
-  static const hipError_t attr = [] {
-    hipError_t e = hipSuccess;
-#define FP8MOE_ATTR(TMV)                                                              \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_bf16_kernel<TMV, false>);    \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm1_swiglu_bf16_kernel<TMV, true>)
-    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128);
-#undef FP8MOE_ATTR
-    return e;
-  }();
-  if (attr != hipSuccess) return attr;
-  if (tile_m > kMaxTileGemm1) return hipErrorInvalidValue;
-  const int KT = 2 * H / kKB;
-  const int NT = I / 128, NB = fit_run<false, false, true>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
-  const size_t lds = gemm_lds_bytes<false, false, true>(tile_m, KT, NB);
-  if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
-#define FP8MOE_B1(TMV)                                                                                          \
-  if (packed)                                                                                                   \
-    hipLaunchKernelGGL((gemm1_swiglu_bf16_kernel<TMV, true>), grid, block, lds, stream, x, w13, g.padded_indptr, \
-                       g.sorted_src, g.E, g.K, H, I, NB, q);                                                     \
-  else                                                                                                          \
-    hipLaunchKernelGGL((gemm1_swiglu_bf16_kernel<TMV, false>), grid, block, lds, stream, x, w13, g.padded_indptr, \
-                       g.sorted_src, g.E, g.K, H, I, NB, q)
-  switch (tile_m) {
-    case 16: FP8MOE_B1(16); break;
-    case 32: FP8MOE_B1(32); break;
-    case 64: FP8MOE_B1(64); break;
-    case 128: FP8MOE_B1(128); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef FP8MOE_B1
-  return hipGetLastError();
-}
-
-static hipError_t launch_gemm2_bf16_t(const uint16_t* q, const uint8_t* w2, const float* topk_weights,
-                                      const GroupedRows& g, int H, int I, uint16_t* Y, int tile_m, int tile_n,
-                                      bool packed, hipStream_t stream) {
-  if (tile_n != kTN) return hipErrorInvalidValue;
-  static const hipError_t attr = [] {
-    hipError_t e = hipSuccess;
-#define FP8MOE_ATTR(TMV)                                                               \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_bf16_kernel<TMV, false>);   \
-    if (e == hipSuccess) e = allow_lds<TMV>(gemm2_weighted_bf16_kernel<TMV, true>)
-    FP8MOE_ATTR(16); FP8MOE_ATTR(32); FP8MOE_ATTR(64); FP8MOE_ATTR(128); FP8MOE_ATTR(144); FP8MOE_ATTR(160);
-#undef FP8MOE_ATTR
-    return e;
-  }();
-  if (attr != hipSuccess) return attr;
-  if (tile_m > kMaxTileGemm2) return hipErrorInvalidValue;
-  const int KT = 2 * I / kKB;
-  const int NT = (H + kTN - 1) / kTN, NB = fit_run<false, false, true>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
-  const size_t lds = gemm_lds_bytes<false, false, true>(tile_m, KT, NB);
-  if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(g, tile_m, NG)), block(kThreads);
-#define FP8MOE_B2(TMV)                                                                                            \
-  if (packed)                                                                                                     \
-    hipLaunchKernelGGL((gemm2_weighted_bf16_kernel<TMV, true>), grid, block, lds, stream, q, w2, topk_weights,     \
-                       g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y);                                           \
-  else                                                                                                            \
-    hipLaunchKernelGGL((gemm2_weighted_bf16_kernel<TMV, false>), grid, block, lds, stream, q, w2, topk_weights,    \
-                       g.padded_indptr, g.sorted_src, g.E, H, I, NB, Y)
-  switch (tile_m) {
-    case 16: FP8MOE_B2(16); break;
-    case 32: FP8MOE_B2(32); break;
-    case 64: FP8MOE_B2(64); break;
-    case 128: FP8MOE_B2(128); break;
-    case 144: FP8MOE_B2(144); break;
-    case 160: FP8MOE_B2(160); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef FP8MOE_B2
   return hipGetLastError();
 }
 

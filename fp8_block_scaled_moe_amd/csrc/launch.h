@@ -22,9 +22,15 @@ struct GroupedRows {
 };
 
 size_t route_lds_bytes(int E);
+// zero2 (nullable): kSmallBarrierWords words the one-workgroup path
+// (R <= 4096) sets to zero in the same launch (the small-T layer's barrier
+// counters and error flag); hipErrorInvalidValue if given with more rows.
+constexpr int kRouteOneBlockRows = 4096;
+constexpr int kSmallBarrierWords = 16;   // 8 group counters, the top counter, the error flag, spare
 hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int cap,
                                 int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
-                                int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream);
+                                int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream,
+                                uint32_t* zero2 = nullptr);
 
 // Largest tile heights.  GEMM2's body fits 256 VGPRs up to 160 rows.  GEMM1's
 // body (with its SwiGLU/requant epilogue) reaches the VGPR limit at 144 rows
@@ -97,6 +103,19 @@ hipError_t launch_pack_mx_scales(const uint8_t* in, int64_t E, int N, int K, int
 
 hipError_t launch_combine(const uint16_t* Y, const int32_t* topk_ids, int T, int H, int E, int K,
                           uint16_t* out, hipStream_t stream);
+
+// The FP8 layer for small T in one cooperative persistent launch (after the
+// routing launch, which zeroes ctr_err[0..1]): GEMM1 + SwiGLU + requant over
+// every tile, a grid barrier, GEMM2 over every tile, a grid barrier, the
+// combine.  Tiles of at most tile_m rows (16, 32 or 64) for both GEMMs.  The
+// barriers give up after a spin limit and set ctr_err[9] = 1 (they never
+// wait that long when every workgroup is resident, which the cooperative
+// launch guarantees).
+hipError_t launch_moe_small(const uint8_t* x, const float* x_scale, const uint8_t* w13, const float* w13_scale,
+                            const uint8_t* w2, const float* w2_scale, const int32_t* topk_ids,
+                            const float* topk_weights, const GroupedRows& g, int T, int H, int I, uint8_t* q,
+                            float* q_scale, uint16_t* Y, uint16_t* out, uint32_t* ctr_err, int tile_m, bool packed,
+                            hipStream_t stream);
 
 hipError_t launch_gated_act(const uint16_t* in, int64_t M, int N, uint8_t* out, uint8_t* scale,
                             int variant, hipStream_t stream);

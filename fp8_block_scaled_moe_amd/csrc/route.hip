@@ -28,8 +28,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_permute_kernel(
     const int32_t* __restrict__ ids, int R, int E, int align, int cap,
     int32_t* __restrict__ counts, int32_t* __restrict__ m_indptr,
     int32_t* __restrict__ padded_indptr, int32_t* __restrict__ sorted_src,
-    int32_t* __restrict__ src_to_sorted) {
+    int32_t* __restrict__ src_to_sorted, uint32_t* __restrict__ zero2) {
   extern __shared__ int smem[];
+  // the persistent small-T layer's barrier words start at zero
+  if (zero2 != nullptr && threadIdx.x < kSmallBarrierWords) zero2[threadIdx.x] = 0u;
   int* cnt = smem;                 // [E]
   int* pad = cnt + E;              // [E+1]
   int* run = pad + E + 1;          // [E]
@@ -127,6 +129,7 @@ size_t route_lds_bytes(int E) { return (size_t)(E + (E + 1) + E + kRouteWaves * 
 //            together write -1 into every padding slot
 //   inverse: src_to_sorted[s] = position of row s, -1 for dropped slots
 constexpr int kChunk = 2048;
+static_assert(2 * kChunk == kRouteOneBlockRows, "one-workgroup routing limit");
 
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
                                                                    int32_t* __restrict__ cc) {
@@ -249,7 +252,8 @@ __global__ __launch_bounds__(256) void route_inverse_kernel(const int32_t* __res
 
 hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int cap,
                                 int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
-                                int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream) {
+                                int32_t* sorted_src, int32_t* src_to_sorted, hipStream_t stream,
+                                uint32_t* zero2) {
   const size_t lds = route_lds_bytes(E);
   // raise the dynamic-LDS limit once (thread-safe static initialisation)
   static const hipError_t attr = hipFuncSetAttribute((const void*)route_permute_kernel,
@@ -258,9 +262,10 @@ hipError_t launch_route_permute(const int32_t* ids, int R, int E, int align, int
   if (attr != hipSuccess) return attr;
   if (R <= 2 * kChunk) {   // small: one workgroup, one launch
     hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(kRouteThreads), lds, stream, ids, R, E,
-                       align, cap, counts, m_indptr, padded_indptr, sorted_src, src_to_sorted);
+                       align, cap, counts, m_indptr, padded_indptr, sorted_src, src_to_sorted, zero2);
     return hipGetLastError();
   }
+  if (zero2 != nullptr) return hipErrorInvalidValue;   // only the one-workgroup path zeroes them
   static const hipError_t attr2 = [] {
     const int big = (int)((2 + kRouteWaves) * (size_t)kMaxExperts * sizeof(int));
     hipError_t e = hipFuncSetAttribute((const void*)route_place_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, big);

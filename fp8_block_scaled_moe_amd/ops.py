@@ -148,6 +148,41 @@ def tune_tiles_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weig
     return t1.value, t2.value, m1.value, m2.value
 
 
+def fused_small_workspace_size(T, H, I, E, K):
+    n = ctypes.c_size_t(0)
+    check(lib().moe_fused_fp8_small_workspace_size(T, H, I, E, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def moe_fused_fp8_small(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, out=None, workspace=None,
+                        tile_m=-1, weight_layout=WEIGHTS_ROW_MAJOR):
+    """The FP8 layer for small T (T*K <= 4096) in two launches (moe_fused_fp8_small): routing,
+    then one persistent kernel.  Same results as moe_fused_fp8.  Returns bf16 [T, H]; the
+    workspace's last 256 bytes hold the barrier counter and error flag (small_layer_flag)."""
+    x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
+    T, H, I, E, K = _check_fp8_layer(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", 2)
+    if workspace is None:
+        workspace = torch.empty(fused_small_workspace_size(T, H, I, E, K), dtype=torch.uint8, device=dev)
+    check(lib().moe_fused_fp8_small(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
+                                    _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
+                                    workspace.numel() * workspace.element_size(), tile_m, weight_layout,
+                                    _stream(dev)))
+    return out
+
+
+def small_layer_flag(workspace, T, H, I, E, K):
+    """(top barrier counter, error flag) a moe_fused_fp8_small call left in its workspace (host
+    copy; synchronises with the device).  After a complete call the counter is 16 (8 groups
+    x 2 barriers) and the flag 0."""
+    need = fused_small_workspace_size(T, H, I, E, K) - 256
+    w = workspace[need:need + 64].view(torch.int32).cpu()
+    return int(w[8]), int(w[9])
+
+
 def moe_fused_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
                   out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR, tile_m2=None):
     """Fused W8A8 FP8 block-scaled MoE layer.  Returns bf16 [T, H].  weight_layout 1: w13 and w2

@@ -440,6 +440,43 @@ int moe_tune_tiles_fp8(const void* x, const float* x_scale, const void* w13, con
                        void* workspace, size_t workspace_bytes, int32_t weight_layout, int32_t iters,
                        void* stream, int32_t* tile_m1, int32_t* tile_m2, float* ms1, float* ms2);
 
+/* ---------------------------------------------------------------- small-T layer in two launches
+ * moe_fused_fp8_small: the moe_fused_fp8 layer for small T in two launches
+ * instead of four. It follows the AlphaMoE page's single fused kernel ("Key
+ * optimisation") as far as a grid-wide dependency allows.
+ *
+ * The first launch is the routing, which also zeroes a barrier counter and
+ * an error flag. The second is one cooperative persistent kernel: GEMM1 +
+ * SwiGLU + requant over every tile, a grid barrier, GEMM2 over every tile, a
+ * grid barrier, then the combine.
+ *
+ * Results are bit-identical to moe_fused_fp8's: the same tile bodies do the
+ * same arithmetic.
+ *
+ * tile_m: -1 (the larger of the cost model's two choices, capped at 64), or
+ * 16, 32 or 64, used for both GEMMs.
+ *
+ * Limits:
+ *   T*K <= 4096 routed rows (FP8MOE_ERR_LIMIT otherwise).
+ *   The workspace is moe_fused_fp8_small_workspace_size bytes, the
+ *   moe_fused_fp8 layout plus 256. Its last 256 bytes start with the
+ *   barrier words (uint32): 8 group counters, then the top counter (word 8,
+ *   16 after a complete call), then the error flag (word 9).
+ *
+ * The flag becomes 1 only if a barrier gave up waiting after its spin limit
+ * (about a second). The cooperative launch makes every workgroup resident,
+ * so that is not expected; a caller may read the flag after the stream
+ * completes. Other errors are as for moe_fused_fp8, plus FP8MOE_ERR_HIP when
+ * the device refuses the cooperative launch.
+ */
+int moe_fused_fp8_small_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                       size_t* bytes);
+int moe_fused_fp8_small(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, const int32_t* topk_ids,
+                        const float* topk_weights, int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                        void* out, void* workspace, size_t workspace_bytes, int32_t tile_m,
+                        int32_t weight_layout, void* stream);
+
 /* moe_fused_fp8_tiles: moe_fused_fp8 with separate tile heights for GEMM1
  * (tile_m1) and GEMM2 (tile_m2), e.g. those moe_tune_tiles_fp8 returned.
  * Each is -1 (the cost model's choice) or one of 16, 32, 64, 128, 144 and

@@ -222,6 +222,26 @@ def test_tune_tiles_and_fused_tiles_validation():
     assert fused(T=0, ptr=NULL, out=NULL) == OK
 
 
+def test_small_layer_validation():
+    L = lib()
+    def small(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, out=FAKE, layout=0):
+        return L.moe_fused_fp8_small(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, ws, wsb, tm, layout,
+                                     NULL)
+    assert small(T=513, K=8, E=16) == E_LIMIT          # 4104 routed rows > 4096
+    assert small(tm=128) == E_TILE
+    assert small(tm=48) == E_TILE
+    assert small(H=200) == E_ALIGN
+    assert small(wsb=1024) == E_WS
+    need = fm.fused_workspace_size(16, 256, 128, 4, 2)
+    assert small(wsb=need) == E_WS                     # the barrier words need 256 more bytes
+    assert small(ptr=NULL) == E_NULL
+    assert small(out=NULL) == E_NULL
+    assert small(ws=NULL) == E_WS
+    assert small(layout=2) == E_SHAPE
+    assert small(T=0, ptr=NULL, ws=NULL, out=NULL) == OK
+    assert fm.fused_small_workspace_size(16, 256, 128, 4, 2) == need + 256
+
+
 def test_workspace_size_bf16():
     nb = fm.fused_bf16_workspace_size(16, 256, 128, 4, 2)
     R, cap = 32, 32 + 4 * 127
