@@ -1414,6 +1414,16 @@ static inline size_t max_dyn_lds(int tm) { return kMaxGemmLds - 4 * (size_t)tm *
 constexpr int kRing = Cfg<16>::D;   // the weight ring depth of every tile body
 static_assert(Cfg<128>::D == kRing && Cfg<160>::D == kRing, "one ring depth");
 
+// The largest tile body at most tile_m rows whose LDS fits for KT steps (a run
+// of one N tile): the token scales of a tile grow with KT, and at the largest
+// depths only bodies up to 128 rows fit.  Every height gives the same results.
+template <bool MX, bool FP4 = false, bool BF = false>
+static inline int fit_tile(int tile_m, int KT) {
+  while (tile_m > 128 && gemm_lds_bytes<MX, FP4, BF>(tile_m, KT, 1) > max_dyn_lds(tile_m))
+    tile_m = tile_m == 160 ? 144 : 128;
+  return tile_m;
+}
+
 // run_length, shortened until the run's weight scales fit in LDS; one N tile
 // per workgroup unless the K steps fill whole rounds of the weight ring
 template <bool MX, bool FP4 = false, bool BF = false>
@@ -1497,6 +1507,7 @@ static hipError_t launch_gemm2_t(const uint8_t* q, const scale_t<MX>* q_scale, c
   if (attr != hipSuccess) return attr;
   if (tile_m > kMaxTileGemm2) return hipErrorInvalidValue;
   const int KT = I / (FP4 ? 2 : 1) / kKB;
+  tile_m = fit_tile<MX, FP4>(tile_m, KT);
   const int NT = (H + kTN - 1) / kTN, NB = fit_run<MX, FP4>(g, tile_m, NT, KT), NG = (NT + NB - 1) / NB;
   const size_t lds = gemm_lds_bytes<MX, FP4>(tile_m, KT, NB);
   if (lds > max_dyn_lds(tile_m)) return hipErrorInvalidValue;
