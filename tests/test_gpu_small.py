@@ -96,3 +96,16 @@ def test_small_decode_256_experts_against_oracle():
     oref = moe_reference(x_q.numpy(), x_s.numpy(), dev_experts(w13), dev_experts(w13s), dev_experts(w2),
                          dev_experts(w2s), ids.numpy(), w.numpy(), tokens=tokens)[1]
     assert_close_to_oracle(out[tokens], oref, "small decode sampled tokens")
+
+
+@pytest.mark.parametrize("T,H,I,E,K", [(512, 256, 256, 1024, 8), (24, 16384, 256, 4, 2), (24, 256, 16384, 4, 2)])
+def test_small_at_the_limits(T, H, I, E, K):
+    """E = 1024 (the tile search walks four chunks of 256 experts in each phase) and the
+    largest depths, bit-identical to the four-launch layer."""
+    ph = synth.moe_problem(T, H, I, E, K, synth.CFG_TINY, extra=(13,))
+    p = ph.to("cuda")
+    ref = fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids, p.topk_weights)
+    for tm in (-1, 16, 64):
+        say("small limits", T, H, I, E, K, "tile_m", tm)
+        out = small(p, p.w13_q, p.w2_q, tm)
+        assert torch.equal(out, ref), (T, H, I, E, K, tm)
