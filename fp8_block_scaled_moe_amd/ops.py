@@ -187,52 +187,24 @@ def moe_fused_fp8(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weigh
                   out=None, workspace=None, tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR, tile_m2=None):
     """Fused W8A8 FP8 block-scaled MoE layer.  Returns bf16 [T, H].  weight_layout 1: w13 and w2
     packed by pack_weights (same shapes).  tile_m2 given: tile_m is GEMM1's tile height and
-    tile_m2 GEMM2's (moe_fused_fp8_tiles)."""
+    tile_m2 GEMM2's (moe_fused_fp8_tiles, tile_n 256)."""
     x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
-    if tile_m2 is not None:
-        T, H, I, E, K = _check_fp8_layer(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights)
-        dev = x.device
-        if out is None:
-            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        _need(out, torch.bfloat16, "out", 2)
-        if workspace is None:
-            workspace = alloc_workspace(T, H, I, E, K, dev)
-        if tile_n not in (-1, 256):
-            raise Fp8MoeError(-5, f"tile_n {tile_n} not in (-1, 256)")
-        check(lib().moe_fused_fp8_tiles(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
-                                        _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
-                                        workspace.numel() * workspace.element_size(), tile_m, tile_m2,
-                                        weight_layout, _stream(dev)))
-        return out
-    _need(x, torch.uint8, "x", 2)
-    _need(x_scale, torch.float32, "x_scale", 2)
-    _need(w13, torch.uint8, "w13", 3)
-    _need(w13_scale, torch.float32, "w13_scale", 3)
-    _need(w2, torch.uint8, "w2", 3)
-    _need(w2_scale, torch.float32, "w2_scale", 3)
-    _need(topk_ids, torch.int32, "topk_ids", 2)
-    _need(topk_weights, torch.float32, "topk_weights", 2)
-    T, H = x.shape
-    E, I2, H2 = w13.shape
-    I = I2 // 2
-    K = topk_ids.shape[1]
-    if H2 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
-        raise ValueError("inconsistent x / w13 / w2 shapes")
-    if tuple(x_scale.shape) != (T, H // 128) or tuple(w13_scale.shape) != (E, 2 * I // 128, H // 128) \
-            or tuple(w2_scale.shape) != (E, H // 128, I // 128):
-        raise ValueError("inconsistent scale shapes")
-    if tuple(topk_ids.shape) != (T, K) or tuple(topk_weights.shape) != (T, K):
-        raise ValueError("topk_ids / topk_weights must be [T, K]")
+    T, H, I, E, K = _check_fp8_layer(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights)
     dev = x.device
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, torch.bfloat16, "out", 2)
     if workspace is None:
         workspace = alloc_workspace(T, H, I, E, K, dev)
-    check(lib().moe_fused_fp8(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
-                              _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), _p(workspace),
-                              workspace.numel() * workspace.element_size(), tile_m, tile_n, weight_layout,
-                              _stream(dev)))
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale), _p(topk_ids), _p(topk_weights),
+            T, H, I, E, K, _p(out), _p(workspace), nbytes)
+    if tile_m2 is None:
+        check(lib().moe_fused_fp8(*args, tile_m, tile_n, weight_layout, _stream(dev)))
+    else:
+        if tile_n not in (-1, 256):
+            raise ValueError(f"tile_n {tile_n} not in (-1, 256)")
+        check(lib().moe_fused_fp8_tiles(*args, tile_m, tile_m2, weight_layout, _stream(dev)))
     return out
 
 
