@@ -81,3 +81,24 @@ def test_random_shape(fmt, seed):
         outs.append(out)
     for o in outs[1:]:
         assert torch.equal(o, outs[0]), f"{fmt} seed {seed}: tiles or layouts change the result"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_stages_equal_fused(seed):
+    """Route (random alignment) -> GEMM1 -> GEMM2 -> combine through the stage entry points, at
+    random tile heights, reproduces the fused FP8 layer bit for bit (each output row's arithmetic
+    is independent of alignment, tile height and padding)."""
+    T, H, I, E, K, drop = draw(100 + seed, False)
+    ph = problem("fp8", T, H, I, E, K, drop, 100 + seed)
+    p = ph.to("cuda")
+    rng = np.random.default_rng(seed)
+    align = int(rng.choice([16, 32, 64, 128]))
+    t1, t2 = int(rng.choice([16, 32, 64, 128])), int(rng.choice([16, 32, 64, 128, 144, 160]))
+    say("stages seed", seed, "T H I E K", T, H, I, E, K, "align", align, "tiles", t1, t2)
+    fused = fm.moe_fused_fp8(p.x_q, p.x_s, p.w13_q, p.w13_s, p.w2_q, p.w2_s, p.topk_ids, p.topk_weights)
+    r = fm.route_permute(p.topk_ids, E, align)
+    q, qs = fm.gemm1_swiglu_quant(p.x_q, p.x_s, p.w13_q, p.w13_s, r, T, K, align, tile_m=t1)
+    Y = fm.gemm2_weighted(q, qs, p.w2_q, p.w2_s, r, p.topk_weights, T, K, align, tile_m=t2)
+    out = fm.combine(Y, p.topk_ids, E)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fused)
