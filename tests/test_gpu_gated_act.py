@@ -76,3 +76,22 @@ def test_gated_act_zero_gate_and_boundaries():
 def test_gated_act_empty():
     q, s = fm.gated_act_fp8_quant(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
     assert q.shape == (0, 32) and s.shape == (0, 1)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gated_act_random_shapes(seed):
+    """Seeded random shapes (M up to 2000 rows, N up to 2048 columns in 32-column blocks), both
+    input distributions, every variant: E8M0 scales identical, codes within the one-step bound."""
+    rng = np.random.default_rng(300 + seed)
+    M, N = int(rng.integers(1, 2001)), int(32 * rng.integers(1, 65))
+    block_scaled = bool(rng.integers(0, 2))
+    x = synth.gated_act_input(M, N, block_scaled=block_scaled, extra=(300 + seed,))
+    rq, rs = gated_act_reference(x.view(torch.int16).numpy().view(np.uint16))
+    for variant in (-1, 0, 1):
+        say("gated_act random", seed, M, N, block_scaled, "variant", variant)
+        q, s = fm.gated_act_fp8_quant(x.cuda(), variant)
+        torch.cuda.synchronize()
+        q, s = q.cpu().numpy(), s.cpu().numpy()
+        assert np.array_equal(s, rs), f"E8M0 differs in {np.count_nonzero(s != rs)} blocks"
+        d = np.abs(e4m3_ordinal(q) - e4m3_ordinal(rq))
+        assert d.max() <= 1 and np.count_nonzero(d) <= 1e-3 * d.size
