@@ -354,3 +354,21 @@ def test_select_tile_page_golden_through_abi():
 ])
 def test_select_tile_at_the_workloads(R, n, k, E, gated, expect):
     assert fm.select_tile(R, n, k, E, 256, gated)[0] == expect
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/fp8moe.h is a plain C header: a C99 translation unit including it compiles with
+    -pedantic and links against the library."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use.c"
+    src.write_text('#include "fp8moe.h"\nint main(void) { size_t b = 0; '
+                   'return moe_fused_fp8_workspace_size(1, 128, 128, 1, 1, &b) != 0 || b == 0; }\n')
+    libdir = os.path.dirname(fm.LIB_PATH)
+    exe = tmp_path / "use"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", libdir, "-lfp8moe", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    assert exe.exists()
