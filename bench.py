@@ -75,11 +75,11 @@ METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roof
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "f06f4063b02a3fa9c1e6933980b1e412680aec1dd962b7af099c38fe66baf71b",
-    "gemm1_fetch_kib": 5598538, "gemm1_write_kib": 157903,
+    "gemm_sources_sha256": "ded682118939231ffeaeb1892508e2e68a41ef9900c13eab834a1690e1f10610",
+    "gemm1_fetch_kib": 5623343, "gemm1_write_kib": 157576,
     # GRBM_COUNT (FETCH_SIZE pass): GPU clock cycles per dispatch summed over
     # the 8 XCDs, and the dispatch's average duration under that pass
-    "gemm1_grbm_count": 35795256, "gemm1_grbm_dur_us": 2556.77,
+    "gemm1_grbm_count": 35703984, "gemm1_grbm_dur_us": 2679.34,
     "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm_kernels.h", "fp8_block_scaled_moe_amd/csrc/gemm1.hip",

@@ -49,7 +49,8 @@ constexpr size_t kAlignWs = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout of moe_fused_fp8 (each part 256-byte aligned).
+// Workspace layout of the fused layer in every operand format (each part
+// 256-byte aligned); the small-T call adds one aligned block of barrier words.
 struct WsLayout {
   size_t counts, m_indptr, padded, sorted_src, src_to_sorted, q, q_scale, Y, total;
 };

@@ -520,8 +520,8 @@ __device__ __forceinline__ void stage_token_scales_mx(uint8_t* SX, int KT, RowSf
 // Dynamic LDS layout (the four token buffers [TM][128] are static arrays of
 // the main loop): the M tile's token scales (FP8: fp32 [KT][TSLOT]; MX:
 // E8M0 [SPB*KT][4][16][4*TSW]), the run's weight block scales (FP8 only: fp32
-// [NB][KT][2]; MXFP8 weight scales stream from global memory with the
-// weights), the epilogue scratch (GEMM1: per-wave row max [8][TM]; GEMM2:
+// [NB][KT][2]; MX weight scales, MXFP8 or MXFP4, stream from global
+// memory with the weights), the epilogue scratch (GEMM1: per-wave row max [8][TM]; GEMM2:
 // source row and top-k weight [2][TM]).
 template <int TM, bool MX, bool FP4 = false, bool BF = false>
 struct Lds {
@@ -563,7 +563,7 @@ struct Lds {
 //
 // wband(n, w) gives the first row of sub-tile w's 16-row band in N tile n
 // within the expert's weight block `wrsrc`; kdim is the K extent in bytes (H
-// for GEMM1, I for GEMM2).  MXFP8: `srsrc` covers the expert's E8M0 weight
+// for GEMM1, I for GEMM2).  MX: `srsrc` covers the expert's E8M0 weight
 // scales.  Row-major ([rows][kdim / 32]): lane l's scale of a K step is one
 // byte at row band + l % 16, block 4k + l / 16, loaded with the step's
 // weights into the same ring.  MFMA-tiled: the first step of each round (K
@@ -791,7 +791,7 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     publish_wait(s);
     step_barrier();
   };
-  // MXFP8, MFMA-tiled scales: the next round's scale dwords become current
+  // MX, MFMA-tiled scales: the next round's scale dwords become current
   auto next_round = [&]() __attribute__((always_inline)) {
     if constexpr (MXT) {
 #pragma unroll
