@@ -84,6 +84,7 @@ WsLayout ws_layout(int64_t T, int H, int I, int E, int K, int fmt) {
 
 int check_dims(int64_t T, int H, int I, int E, int K) {
   if (T < 0) return fail(FP8MOE_ERR_SHAPE, "T must be >= 0 (got %lld)", (long long)T);
+  if (T >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "T=%lld overflows the int32 row space", (long long)T);
   if (H <= 0 || I <= 0) return fail(FP8MOE_ERR_SHAPE, "H and I must be positive (got %d, %d)", H, I);
   if (H % 128 || I % 128)
     return fail(FP8MOE_ERR_ALIGN, "H and I must be multiples of 128 (got %d, %d)", H, I);
@@ -415,6 +416,8 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 int64_t moe_route_capacity(int64_t T, int32_t K, int32_t E, int32_t align) {
   if (T < 0 || K < 1 || E < 1) return fail(FP8MOE_ERR_SHAPE, "invalid T/K/E");
+  if (T >= kMaxRows || K > FP8MOE_MAX_EXPERTS || E > FP8MOE_MAX_EXPERTS)
+    return fail(FP8MOE_ERR_LIMIT, "T=%lld K=%d E=%d beyond the int32 row space or the expert limit", (long long)T, K, E);
   if (!valid_align(align)) return fail(FP8MOE_ERR_ALIGN, "align %d not in {16,32,64,128}", align);
   ok();
   return T * K + (int64_t)E * (align - 1);
@@ -424,6 +427,7 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
                       int32_t* counts, int32_t* m_indptr, int32_t* padded_indptr,
                       int32_t* sorted_src, int32_t* src_to_sorted, void* stream) {
   if (T < 0) return fail(FP8MOE_ERR_SHAPE, "T must be >= 0");
+  if (T >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "T=%lld overflows the int32 row space", (long long)T);
   if (E < 1) return fail(FP8MOE_ERR_SHAPE, "E must be >= 1");
   if (E > FP8MOE_MAX_EXPERTS) return fail(FP8MOE_ERR_LIMIT, "E=%d exceeds %d", E, FP8MOE_MAX_EXPERTS);
   if (K < 1 || K > E) return fail(FP8MOE_ERR_TOPK, "top-k K=%d outside [1, E=%d]", K, E);

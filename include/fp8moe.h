@@ -74,7 +74,8 @@ const char* moe_last_error(void);
  * "aligned" MoE of the AlphaMoE page; m_indptr as on the SM120 page, section 1).
  *
  * moe_route_capacity: rows the padded map can need, T*K + E*(align-1);
- *   negative status on invalid arguments (host only, no GPU needed).
+ *   negative status on invalid arguments, FP8MOE_ERR_LIMIT for T >= 2^31 or
+ *   K or E above FP8MOE_MAX_EXPERTS (host only, no GPU needed).
  *
  * moe_route_permute outputs (device, int32, all fully written):
  *   counts        [E]        rows per expert

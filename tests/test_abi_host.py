@@ -47,6 +47,13 @@ def test_route_capacity():
     assert fm.route_capacity(0, 8, 128, 128) == 128 * 127
     assert lib().moe_route_capacity(4, 2, 4, 24) == E_ALIGN
     assert lib().moe_route_capacity(-1, 2, 4, 16) == E_SHAPE
+    # a huge T is rejected before any product T*K is formed
+    assert lib().moe_route_capacity(1 << 62, 8, 256, 16) == E_LIMIT
+    assert lib().moe_route_capacity(4, 1 << 30, 256, 16) == E_LIMIT
+    n = ctypes.c_size_t(0)
+    assert lib().moe_fused_fp8_workspace_size(1 << 62, 7168, 2048, 256, 8, ctypes.byref(n)) == E_SHAPE
+    dummy = ctypes.c_void_p(16)
+    assert lib().moe_route_permute(dummy, 1 << 62, 8, 256, 16, dummy, dummy, dummy, dummy, dummy, None) == E_SHAPE
 
 
 def test_route_permute_validation():
