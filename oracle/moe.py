@@ -83,9 +83,16 @@ def expert_ffn(xq_rows, xs_rows, w13_q, w13_s, w2_q, w2_s, stages=None):
 
 
 def _layer(expert_fn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights, tokens, return_stages,
-           H=None):
+           H=None, workers=None):
     """Route rows to experts, run expert_fn on each expert's rows, combine (H: output
-    width, by default the width of x_q)."""
+    width, by default the width of x_q).
+
+    workers > 1 evaluates up to that many experts at once on a thread pool.  The
+    experts are independent (each reads only its own rows and weights), every
+    expert's arithmetic is unchanged and the combine below runs after all of
+    them in its fixed order, so the result is the same bit for bit.  The expert
+    weights are fetched (w13_q[e], ...) on the calling thread, a bounded number
+    ahead of the pool."""
     ids = np.asarray(topk_ids)
     wts = np.asarray(topk_weights, dtype=np.float32)
     T, K = ids.shape
@@ -97,17 +104,36 @@ def _layer(expert_fn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights
     rows = expert_rows(ids, E, toks)
     Ysl = {}                      # (t, j) -> float64 [H]
     stages = {}
-    for e in sorted(rows):
+
+    def args_of(e):
+        tok_idx = np.array([t for t, _ in rows[e]], dtype=np.int64)
+        return (np.asarray(x_q)[tok_idx], np.asarray(x_s)[tok_idx], w13_q[e], w13_s[e], w2_q[e], w2_s[e])
+
+    def keep(e, Y, st):
         tj = rows[e]
-        tok_idx = np.array([t for t, _ in tj], dtype=np.int64)
-        st = {} if return_stages else None
-        Y = expert_fn(np.asarray(x_q)[tok_idx], np.asarray(x_s)[tok_idx],
-                      w13_q[e], w13_s[e], w2_q[e], w2_s[e], st)
         for r, (t, j) in enumerate(tj):
             Ysl[(t, j)] = Y[r]
         if return_stages:
             st["rows"] = tj
             stages[e] = st
+
+    experts = sorted(rows)
+    if workers is None or workers <= 1:
+        for e in experts:
+            st = {} if return_stages else None
+            keep(e, expert_fn(*args_of(e), st), st)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            pending = []
+            for e in experts:
+                st = {} if return_stages else None
+                pending.append((e, st, pool.submit(expert_fn, *args_of(e), st)))
+                while len(pending) > 2 * workers:          # bounded look-ahead of fetched weights
+                    e0, st0, f0 = pending.pop(0)
+                    keep(e0, f0.result(), st0)
+            for e0, st0, f0 in pending:
+                keep(e0, f0.result(), st0)
 
     # combine: weighted sum over the token's valid slots in ascending j
     acc = np.zeros((len(toks), H), dtype=np.float64)
@@ -123,7 +149,7 @@ def _layer(expert_fn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights
 
 
 def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
-                  tokens=None, return_stages=False):
+                  tokens=None, return_stages=False, workers=None):
     """Reference fused MoE layer.
 
     Returns (out_bits, out) for the requested tokens (all tokens by default,
@@ -132,7 +158,7 @@ def moe_reference(x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
     item maps each expert to its rows and per-stage intermediates.
     """
     return _layer(expert_ffn, x_q, x_s, w13_q, w13_s, w2_q, w2_s, topk_ids, topk_weights,
-                  tokens, return_stages)
+                  tokens, return_stages, workers=workers)
 
 
 # ---------------------------------------------------------------- MXFP8 variant
@@ -168,11 +194,11 @@ def expert_ffn_mx(xq_rows, xsf_rows, w13_q, w13_sf, w2_q, w2_sf, stages=None):
 
 
 def moe_reference_mx(x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
-                     tokens=None, return_stages=False):
+                     tokens=None, return_stages=False, workers=None):
     """Reference MXFP8 MoE layer; arguments and results as moe_reference, with
     E8M0 scale codes (uint8) x_sf [T, H/32], w13_sf [E][2I, H/32], w2_sf [E][H, I/32]."""
     return _layer(expert_ffn_mx, x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
-                  tokens, return_stages)
+                  tokens, return_stages, workers=workers)
 
 
 # ---------------------------------------------------------------- MXFP4 (W4A4) variant
@@ -204,12 +230,12 @@ def expert_ffn_mxfp4(xq_rows, xsf_rows, w13_q, w13_sf, w2_q, w2_sf, stages=None)
 
 
 def moe_reference_mxfp4(x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
-                        tokens=None, return_stages=False):
+                        tokens=None, return_stages=False, workers=None):
     """Reference MXFP4 (W4A4) MoE layer: x_q uint8 [T, H/2] (two e2m1 codes per byte,
     the even element in the low nibble), x_sf [T, H/32]; w13_q [E][2I, H/2], w13_sf
     [E][2I, H/32]; w2_q [E][H, I/2], w2_sf [E][H, I/32]."""
     return _layer(expert_ffn_mxfp4, x_q, x_sf, w13_q, w13_sf, w2_q, w2_sf, topk_ids, topk_weights,
-                  tokens, return_stages, H=2 * np.asarray(x_q).shape[1])
+                  tokens, return_stages, H=2 * np.asarray(x_q).shape[1], workers=workers)
 
 
 # ---------------------------------------------------------------- bf16 experts
@@ -240,10 +266,10 @@ def expert_ffn_bf16(x_rows, _xs_rows, w13, _w13_s, w2, _w2_s, stages=None):
     return Y
 
 
-def moe_reference_bf16(x, w13, w2, topk_ids, topk_weights, tokens=None, return_stages=False):
+def moe_reference_bf16(x, w13, w2, topk_ids, topk_weights, tokens=None, return_stages=False, workers=None):
     """Reference bf16 MoE layer: x uint16 [T, H], w13 [E][2I, H], w2 [E][H, I] bf16 bit
     patterns; results as moe_reference."""
     T = np.asarray(x).shape[0]
     no_scales = [None] * len(w13)
     return _layer(expert_ffn_bf16, x, np.zeros((T, 0), np.float32), w13, no_scales, w2, no_scales, topk_ids,
-                  topk_weights, tokens, return_stages)
+                  topk_weights, tokens, return_stages, workers=workers)

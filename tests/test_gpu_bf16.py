@@ -21,7 +21,7 @@ import fp8_block_scaled_moe_amd as fm
 import synth
 from oracle import moe as OM
 from oracle.route import route_reference
-from tests.gpu_helpers import say, assert_close_to_oracle, swiglu_error_bound
+from tests.gpu_helpers import say, assert_close_to_oracle, assert_rows_close_to_oracle, swiglu_error_bound, oracle_workers
 
 pytestmark = pytest.mark.gpu
 
@@ -47,9 +47,10 @@ def run_bf16(p, tile_m=-1, packed=None):
                              weight_layout=fm.WEIGHTS_MFMA_TILED)
 
 
-def oracle_bf16(ph, tokens=None, stages=False):
+def oracle_bf16(ph, tokens=None, stages=False, workers=None):
     r = OM.moe_reference_bf16(synth.bf16_bits(ph.x_q), synth.bf16_bits(ph.w13_q), synth.bf16_bits(ph.w2_q),
-                              ph.topk_ids.numpy(), ph.topk_weights.numpy(), tokens=tokens, return_stages=stages)
+                              ph.topk_ids.numpy(), ph.topk_weights.numpy(), tokens=tokens, return_stages=stages,
+                              workers=workers)
     return r if stages else r[1]
 
 
@@ -207,15 +208,13 @@ def test_skewed_bf16(T, skewed_weights_bf16):
     ph = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x, None, h13, None, h2, None, ids, w)
     pd = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x.cuda(), None, d13, None, d2, None, ids.cuda(),
                          w.cuda())
-    tokens = None if T <= 512 else sorted(np.random.default_rng(T).choice(T, 48, replace=False).tolist())
-    ref = oracle_bf16(ph, tokens)
+    ref = oracle_bf16(ph, workers=oracle_workers())        # every token
     outs = []
     for tm in (-1,) + TILES:
         say("skewed bf16 T", T, "tile_m", tm)
         out = run_bf16(pd, tm)
         torch.cuda.synchronize()
-        got = out if tokens is None else out[tokens]
-        assert_close_to_oracle(got, ref, f"skewed bf16 T={T} tile_m={tm}")
+        assert_rows_close_to_oracle(out, ref, f"skewed bf16 T={T} tile_m={tm}")
         outs.append(out)
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
@@ -233,24 +232,29 @@ def large_weights_bf16():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name,T,cfg,ntok", [("decode", 64, synth.CFG_LARGE, 6), ("prefill", 8192, synth.CFG_PREFILL, 4)])
-def test_large_bf16_sampled(name, T, cfg, ntok, large_weights_bf16):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,T,cfg", [("decode", 64, synth.CFG_LARGE), ("prefill", 8192, synth.CFG_PREFILL)])
+def test_large_bf16_full_oracle(name, T, cfg, large_weights_bf16):
+    """Every token of the bf16 decode and prefill layers against the oracle, in the
+    benchmark's launch configuration (MFMA-tiled weights, auto tiles); the row-major
+    layout must give the same bits."""
     d = synth.LARGE_DIMS
     x, ids, w = synth.moe_tokens_bf16(T, d["H"], d["E"], d["K"], cfg)
     w13, w2 = large_weights_bf16
     pd = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x.cuda(), None, w13, None, w2, None, ids.cuda(),
                          w.cuda())
-    say(name, "bf16 fused auto tile")
-    out = run_bf16(pd)
-    torch.cuda.synchronize()
-    tokens = sorted(np.random.default_rng(T + 3).choice(T, ntok, replace=False).tolist())
-    ref = OM.moe_reference_bf16(synth.bf16_bits(pd.x_q), dev_bits(pd.w13_q), dev_bits(pd.w2_q),
-                                pd.topk_ids.cpu().numpy(), pd.topk_weights.cpu().numpy(), tokens=tokens)[1]
-    assert_close_to_oracle(out[tokens], ref, f"{name} bf16 sampled tokens {tokens}")
-    say(name, "bf16 determinism and packed weights")
-    assert torch.equal(out, run_bf16(pd))
     packed = (fm.pack_weights(pd.w13_q), fm.pack_weights(pd.w2_q))
+    say(name, "bf16 fused auto tile, MFMA-tiled weights")
+    out = run_bf16(pd, packed=packed)
+    torch.cuda.synchronize()
+    say(name, "bf16 oracle over all", T, "tokens")
+    ref = OM.moe_reference_bf16(synth.bf16_bits(pd.x_q), dev_bits(pd.w13_q), dev_bits(pd.w2_q),
+                                pd.topk_ids.cpu().numpy(), pd.topk_weights.cpu().numpy(),
+                                workers=oracle_workers())[1]
+    assert_rows_close_to_oracle(out, ref, f"{name} bf16 all {T} tokens")
+    say(name, "bf16 determinism and row-major weights")
     assert torch.equal(out, run_bf16(pd, packed=packed))
+    assert torch.equal(out, run_bf16(pd))
     del packed
     if name == "decode":
         for tm in TILES:

@@ -2,10 +2,12 @@
 
 Tolerance for the fused output: relative Frobenius error <= 1e-2 and max abs
 error <= 0.05 * max|ref|.  Exact cases (crafted closed form, integer GEMM)
-must match bit for bit.  At the full decode / prefill sizes the oracle runs
-on a sample of tokens (each token's output depends only on its own row and
-its experts) and the rest is checked through properties that hold at any
-size (token-permutation equivariance, determinism, tile invariance).
+must match bit for bit.  At the full decode, prefill and skewed sizes every
+token of the output is compared with the oracle (test_large_full_oracle,
+test_skewed), in the launch configuration the benchmark times (MFMA-tiled
+weights, auto tiles); the faster sampled variant (test_large_sampled) and
+properties that hold at any size (token-permutation equivariance,
+determinism, tile invariance) run beside it.
 """
 
 import numpy as np
@@ -18,7 +20,8 @@ from oracle import moe as OM
 from oracle import formats as F
 from oracle.route import route_reference
 from tests.cases import crafted_exact_case
-from tests.gpu_helpers import say, assert_close_to_oracle, e4m3_ordinal, dev_experts
+from tests.gpu_helpers import (say, assert_close_to_oracle, assert_rows_close_to_oracle, e4m3_ordinal, dev_experts,
+                               oracle_workers)
 
 pytestmark = pytest.mark.gpu
 
@@ -194,15 +197,15 @@ def test_skewed(T, skewed_weights):
     ph = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q, x_s, h13, h13s, h2, h2s, ids, w)
     pd = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), d13, d13s, d2, d2s,
                          ids.cuda(), w.cuda())
-    tokens = None if T <= 512 else sorted(np.random.default_rng(T).choice(T, 48, replace=False).tolist())
-    ref = oracle_out(ph, tokens)
+    a = (ph.x_q.numpy(), ph.x_s.numpy(), ph.w13_q.numpy(), ph.w13_s.numpy(), ph.w2_q.numpy(), ph.w2_s.numpy(),
+         ph.topk_ids.numpy(), ph.topk_weights.numpy())
+    ref = OM.moe_reference(*a, workers=oracle_workers())[1]     # every token
     outs = []
     for tm in (-1,) + TILES:
         say("skewed T", T, "tile_m", tm)
         out = run_fused(pd, tile_m=tm)
         torch.cuda.synchronize()
-        got = out if tokens is None else out[tokens]
-        assert_close_to_oracle(got, ref, f"skewed T={T} tile_m={tm}")
+        assert_rows_close_to_oracle(out, ref, f"skewed T={T} tile_m={tm}")
         outs.append(out)
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
@@ -245,6 +248,33 @@ def test_large_sampled(name, T, cfg, ntok, large_weights):
     assert_close_to_oracle(out[tokens], ref, f"{name} sampled tokens {tokens}")
     say(name, "determinism")
     assert torch.equal(out, run_fused(pd))
+
+
+@pytest.fixture(scope="module")
+def large_packed(large_weights):
+    w13_q, _, w2_q, _ = large_weights
+    say("packing the 256-expert weights")
+    return fm.pack_weights(w13_q), fm.pack_weights(w2_q)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,T,cfg", [("decode", 64, synth.CFG_LARGE), ("prefill", 8192, synth.CFG_PREFILL)])
+def test_large_full_oracle(name, T, cfg, large_weights, large_packed):
+    """Every token of the decode (T=64) and prefill (T=8192) layers against the oracle,
+    element by element, in the launch configuration the benchmark times: MFMA-tiled
+    weights and the auto tile choice.  The oracle evaluates the experts one at a time
+    (a few at once on a thread pool), reading each expert's weights from the device."""
+    pd = _large_problem(T, cfg, large_weights)
+    w13_p, w2_p = large_packed
+    say(name, "fused auto tile, MFMA-tiled weights")
+    out = fm.moe_fused_fp8(pd.x_q, pd.x_s, w13_p, pd.w13_s, w2_p, pd.w2_s, pd.topk_ids, pd.topk_weights,
+                           weight_layout=fm.WEIGHTS_MFMA_TILED)
+    torch.cuda.synchronize()
+    say(name, "oracle over all", T, "tokens")
+    ref = OM.moe_reference(pd.x_q.cpu().numpy(), pd.x_s.cpu().numpy(), dev_experts(pd.w13_q), dev_experts(pd.w13_s),
+                           dev_experts(pd.w2_q), dev_experts(pd.w2_s), pd.topk_ids.cpu().numpy(),
+                           pd.topk_weights.cpu().numpy(), workers=oracle_workers())[1]
+    assert_rows_close_to_oracle(out, ref, f"{name} all {T} tokens")
 
 
 def test_prefill_token_permutation_equivariance(large_weights):

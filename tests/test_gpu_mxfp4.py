@@ -19,7 +19,8 @@ import synth
 from oracle import formats as F
 from oracle import moe as OM
 from oracle.route import route_reference
-from tests.gpu_helpers import say, assert_close_to_oracle, dev_experts, swiglu_error_bound
+from tests.gpu_helpers import (say, assert_close_to_oracle, assert_rows_close_to_oracle, dev_experts, swiglu_error_bound,
+                               oracle_workers)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +42,10 @@ def pack_all(p):
             fm.pack_mxfp4_scales(p.w2_s))
 
 
-def oracle_fp4(ph, tokens=None, stages=False):
+def oracle_fp4(ph, tokens=None, stages=False, workers=None):
     a = (ph.x_q.numpy(), ph.x_s.numpy(), ph.w13_q.numpy(), ph.w13_s.numpy(), ph.w2_q.numpy(), ph.w2_s.numpy(),
          ph.topk_ids.numpy(), ph.topk_weights.numpy())
-    r = OM.moe_reference_mxfp4(*a, tokens=tokens, return_stages=stages)
+    r = OM.moe_reference_mxfp4(*a, tokens=tokens, return_stages=stages, workers=workers)
     return r if stages else r[1]
 
 
@@ -243,15 +244,13 @@ def test_skewed_mxfp4(T, skewed_weights_fp4):
     ph = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q, x_s, h13, h13s, h2, h2s, ids, w)
     pd = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), d13, d13s, d2, d2s,
                          ids.cuda(), w.cuda())
-    tokens = None if T <= 512 else sorted(np.random.default_rng(T).choice(T, 48, replace=False).tolist())
-    ref = oracle_fp4(ph, tokens)
+    ref = oracle_fp4(ph, workers=oracle_workers())         # every token
     outs = []
     for tm in (-1,) + TILES:
         say("skewed mxfp4 T", T, "tile_m", tm)
         out = run_fp4(pd, tm)
         torch.cuda.synchronize()
-        got = out if tokens is None else out[tokens]
-        assert_close_to_oracle(got, ref, f"skewed mxfp4 T={T} tile_m={tm}")
+        assert_rows_close_to_oracle(out, ref, f"skewed mxfp4 T={T} tile_m={tm}")
         outs.append(out)
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
@@ -267,25 +266,30 @@ def large_weights_fp4():
     return w13_q, w13_s, w2_q, w2_s
 
 
-@pytest.mark.parametrize("name,T,cfg,ntok", [("decode", 64, synth.CFG_LARGE, 6), ("prefill", 8192, synth.CFG_PREFILL, 4)])
-def test_large_mxfp4_sampled(name, T, cfg, ntok, large_weights_fp4):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,T,cfg", [("decode", 64, synth.CFG_LARGE), ("prefill", 8192, synth.CFG_PREFILL)])
+def test_large_mxfp4_full_oracle(name, T, cfg, large_weights_fp4):
+    """Every token of the MXFP4 decode and prefill layers against the oracle, in the
+    benchmark's launch configuration (MFMA-tiled weights and scales, auto tiles); the
+    row-major layout must give the same bits."""
     d = synth.LARGE_DIMS
     x_q, x_s, ids, w = synth.moe_tokens_mxfp4(T, d["H"], d["E"], d["K"], cfg)
     w13_q, w13_s, w2_q, w2_s = large_weights_fp4
     pd = synth.MoEInputs(T, d["H"], d["I"], d["E"], d["K"], x_q.cuda(), x_s.cuda(), w13_q, w13_s, w2_q, w2_s,
                          ids.cuda(), w.cuda())
-    say(name, "mxfp4 fused auto tile")
-    out = run_fp4(pd)
+    packed = pack_all(pd)
+    say(name, "mxfp4 fused auto tile, MFMA-tiled weights")
+    out = run_fp4(pd, packed=packed)
     torch.cuda.synchronize()
-    tokens = sorted(np.random.default_rng(T + 3).choice(T, ntok, replace=False).tolist())
+    say(name, "mxfp4 oracle over all", T, "tokens")
     ref = OM.moe_reference_mxfp4(pd.x_q.cpu().numpy(), pd.x_s.cpu().numpy(), dev_experts(pd.w13_q),
                                  dev_experts(pd.w13_s), dev_experts(pd.w2_q), dev_experts(pd.w2_s),
-                                 pd.topk_ids.cpu().numpy(), pd.topk_weights.cpu().numpy(), tokens=tokens)[1]
-    assert_close_to_oracle(out[tokens], ref, f"{name} mxfp4 sampled tokens {tokens}")
-    say(name, "mxfp4 determinism and packed weights")
-    assert torch.equal(out, run_fp4(pd))
-    packed = pack_all(pd)
+                                 pd.topk_ids.cpu().numpy(), pd.topk_weights.cpu().numpy(),
+                                 workers=oracle_workers())[1]
+    assert_rows_close_to_oracle(out, ref, f"{name} mxfp4 all {T} tokens")
+    say(name, "mxfp4 determinism and row-major weights")
     assert torch.equal(out, run_fp4(pd, packed=packed))
+    assert torch.equal(out, run_fp4(pd))
     del packed
     if name == "decode":
         for tm in TILES:

@@ -6,14 +6,13 @@ oracle within the fused tolerance. The tuner must return valid candidates
 with positive times.
 """
 
-import numpy as np
 import pytest
 import torch
 
 import fp8_block_scaled_moe_amd as fm
 import synth
 from oracle.moe import moe_reference
-from tests.gpu_helpers import say, assert_close_to_oracle
+from tests.gpu_helpers import say, assert_rows_close_to_oracle, oracle_workers
 
 pytestmark = pytest.mark.gpu
 
@@ -43,10 +42,9 @@ def test_tuned_tiles_reproduce_the_layer(T, skewed_weights):
         auto = fm.moe_fused_fp8(xd, xsd, w13, d13s, w2, d2s, idd, wd, weight_layout=layout)
         torch.cuda.synchronize()
         assert torch.equal(tuned, auto), f"tuned tiles ({t1}, {t2}) change the result"
-    tokens = None if T <= 64 else sorted(np.random.default_rng(T).choice(T, 24, replace=False).tolist())
     ref = moe_reference(x_q.numpy(), x_s.numpy(), h13.numpy(), h13s.numpy(), h2.numpy(), h2s.numpy(), ids.numpy(),
-                        w.numpy(), tokens=tokens)[1]
-    assert_close_to_oracle(tuned if tokens is None else tuned[tokens], ref, f"tuned layer T={T}")
+                        w.numpy(), workers=oracle_workers())[1]
+    assert_rows_close_to_oracle(tuned, ref, f"tuned layer T={T}")
 
 
 def test_mixed_tile_pairs_are_bit_identical(skewed_weights):

@@ -218,3 +218,39 @@ def test_scalar_brute_force_tiny():
     assert np.mean(got != ref) < 1e-3
     err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert err < 1e-3
+
+
+# ---------------------------------------------------------------- expert-parallel evaluation
+
+@pytest.mark.parametrize("variant", ["fp8", "mx", "mxfp4", "bf16"])
+def test_thread_pool_gives_the_same_bits(variant):
+    """The full-size comparisons evaluate experts on a thread pool; the result (and
+    every stage) must be the serial result bit for bit, with more experts than the
+    pool's look-ahead and with unused experts and dropped slots."""
+    T, H, I, E, K = 24, 256, 256, 12, 3
+    if variant == "fp8":
+        p, fn = synth.moe_problem(T, H, I, E, K, synth.CFG_TINY, extra=(91,)), M.moe_reference
+    elif variant == "mx":
+        p, fn = synth.moe_problem_mx(T, H, I, E, K, synth.CFG_TINY, extra=(91,)), M.moe_reference_mx
+    elif variant == "mxfp4":
+        p, fn = synth.moe_problem_mxfp4(T, H, I, E, K, synth.CFG_TINY, extra=(91,)), M.moe_reference_mxfp4
+    else:
+        p = synth.moe_problem_bf16(T, H, I, E, K, synth.CFG_TINY, extra=(91,))
+    ids = p.topk_ids.numpy().copy()
+    ids[ids == 5] = 4                       # expert 5 unused
+    ids[3, 1] = -1                          # a dropped slot
+    if variant == "bf16":
+        args = (synth.bf16_bits(p.x_q), synth.bf16_bits(p.w13_q), synth.bf16_bits(p.w2_q), ids,
+                p.topk_weights.numpy())
+        fn = M.moe_reference_bf16
+    else:
+        args = (p.x_q.numpy(), p.x_s.numpy(), p.w13_q.numpy(), p.w13_s.numpy(), p.w2_q.numpy(), p.w2_s.numpy(),
+                ids, p.topk_weights.numpy())
+    serial = fn(*args, return_stages=True)
+    for workers in (2, 3):
+        pooled = fn(*args, return_stages=True, workers=workers)
+        assert np.array_equal(serial[0], pooled[0])
+        assert sorted(serial[2]) == sorted(pooled[2])
+        for e in serial[2]:
+            for k, v in serial[2][e].items():
+                assert np.array_equal(np.asarray(v), np.asarray(pooled[2][e][k])), (variant, workers, e, k)
