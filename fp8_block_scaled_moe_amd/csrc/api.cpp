@@ -46,6 +46,10 @@ bool valid_layout(int l) { return l == FP8MOE_WEIGHTS_ROW_MAJOR || l == FP8MOE_W
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 constexpr size_t kAlignWs = 256;
+// The fused calls route with segments padded to 16 rows (the GEMMs cut each
+// expert into tiles of equal height themselves), so their workspace holds
+// cap = T*K + E*15 padded rows.
+constexpr int kFusedAlign = 16;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -64,7 +68,7 @@ enum Fmt { kFmtFp8 = 0, kFmtMx8 = 1, kFmtMx4 = 2, kFmtBf16 = 3 };
 // and there is no q_scale.
 WsLayout ws_layout(int64_t T, int H, int I, int E, int K, int fmt) {
   const int64_t R = T * K;
-  const int64_t cap = R + (int64_t)E * (128 - 1);  // worst case: align 128
+  const int64_t cap = R + (int64_t)E * (kFusedAlign - 1);
   WsLayout w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = round_up(off + bytes, kAlignWs); return at; };
@@ -193,7 +197,7 @@ int fused_prepare(const void* x, const scale_ptr_t<F>* x_scale, const void* w13,
   // segments padded to 16 rows only: the GEMMs cover each expert with tiles
   // of equal height up to the tile height
   P.R = T * K;
-  P.align = 16;
+  P.align = kFusedAlign;
   P.cap = P.R + (int64_t)E * (P.align - 1);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   P.counts = reinterpret_cast<int32_t*>(ws + L.counts);

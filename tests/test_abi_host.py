@@ -112,7 +112,7 @@ def test_fused_validation(fn, I0):
 @pytest.mark.parametrize("size", [fm.fused_workspace_size, fm.fused_mx_workspace_size])
 def test_workspace_size(size):
     n = size(16, 256, 128, 4, 2)
-    R, cap = 32, 32 + 4 * 127
+    R, cap = 32, 32 + 4 * 15      # segments padded to 16 rows
     # q, its scales (a float per 128 columns or an E8M0 byte per 32: the same bytes), Y, sorted_src
     assert n >= cap * 128 + cap * 4 + R * 256 * 2 + cap * 4
     big = size(8192, 7168, 2048, 256, 8)
@@ -124,7 +124,7 @@ def test_workspace_size(size):
 def test_workspace_size_mxfp4():
     n4 = fm.fused_mxfp4_workspace_size(16, 256, 256, 4, 2)
     n8 = fm.fused_mx_workspace_size(16, 256, 256, 4, 2)
-    R, cap = 32, 32 + 4 * 127
+    R, cap = 32, 32 + 4 * 15      # segments padded to 16 rows
     # q holds I/2 bytes a row (two e2m1 codes a byte), its scales I/32; Y and sorted_src as for MXFP8
     assert n4 >= cap * 128 + cap * 8 + R * 256 * 2 + cap * 4
     assert n4 < n8
@@ -251,7 +251,7 @@ def test_small_layer_validation():
 
 def test_workspace_size_bf16():
     nb = fm.fused_bf16_workspace_size(16, 256, 128, 4, 2)
-    R, cap = 32, 32 + 4 * 127
+    R, cap = 32, 32 + 4 * 15      # segments padded to 16 rows
     # q holds 2 bytes per element and has no scales; Y and sorted_src as for the other formats
     assert nb >= cap * 256 + R * 256 * 2 + cap * 4
     assert nb > fm.fused_workspace_size(16, 256, 128, 4, 2)
