@@ -197,8 +197,8 @@ def cold_once_ms(fn):
 
 
 def cold_time_ms(fn, iters):
-    """Average ms of fn with the caches flushed before each call (flush not timed)."""
-    return sum(cold_once_ms(fn) for _ in range(iters)) / iters
+    """Median ms of fn with the caches flushed before each call (flush not timed)."""
+    return float(np.median([cold_once_ms(fn) for _ in range(iters)]))
 
 
 STREAM_BYTES = 2 << 30
@@ -268,10 +268,11 @@ def skewed_bench(iters=10):
             for tm in configs:
                 fns[tm]()
         # configurations interleaved, so any drift in clocks or caches falls on all alike
-        res = {tm: 0.0 for tm in configs}
+        runs = {tm: [] for tm in configs}
         for _ in range(iters):
             for tm in configs:
-                res[tm] += cold_once_ms(fns[tm]) / iters
+                runs[tm].append(cold_once_ms(fns[tm]))
+        res = {tm: float(np.median(v)) for tm, v in runs.items()}
         nbytes, active = algorithmic_bytes(p)
         best = min(res[t] for t in forced)
         auto_tm = fm.select_tile(T * d["K"], d["I"], d["H"], d["E"], 256, True)[0]
@@ -296,6 +297,26 @@ def algorithmic_bytes(p):
     per_expert = 3 * H * I + 4 * (2 * I // 128) * (H // 128) + 4 * (H // 128) * (I // 128)
     io = p.T * H + 4 * p.T * (H // 128) + 8 * p.T * p.K + 2 * p.T * H
     return active * per_expert + io, active
+
+
+def gemm1_roofline(flop, nbytes, ms):
+    """Roofline of one launch: achieved FLOP/s and algorithmic bytes/s against both published
+    peaks.  The binding roof is the one whose time at 100 % is longer (FLOP / 5.0 PFLOP/s vs
+    bytes / 8 TB/s); `achieved`, `peak`, `unit` and `frac` are given against it."""
+    tflops = flop / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    t_mfma = flop / (PEAK_FP8_TFLOPS * 1e12) * 1e3
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    r = {"roof_ms": {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)},
+         "frac_mfma": round(tflops / PEAK_FP8_TFLOPS, 4), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+         "achieved_TFLOPs": round(tflops, 2), "achieved_GBps": round(gbs, 1)}
+    if t_hbm >= t_mfma:
+        r.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    else:
+        r.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(tflops / PEAK_FP8_TFLOPS, 4)})
+    return r
 
 
 def layer_flops(p):
@@ -457,27 +478,47 @@ def bf16_bench(steps, warmup):
     return res
 
 
-def cpu_baseline(p, ntok=20):
-    """The CPU oracle, as it stands, on a bounded sample of prefill tokens."""
+def cpu_baseline(pre, dec, experts_sampled=16):
+    """The CPU oracle, as it stands, on the host cores, one run per config:
+      decode  -- the whole layer (all 64 tokens, every active expert): seconds per layer;
+      prefill -- every routed row of `experts_sampled` experts spread over the 256 (the other
+                 slots dropped, so each sampled expert's weights and rows are the layer's own);
+                 seconds per layer = the sample's time x all rows / sampled rows (each
+                 expert's work is its weights' dequantisation plus its rows' GEMMs).
+    The oracle evaluates up to 8 experts at once on a thread pool (its BLAS uses every core).
+    value = prefill FLOP of the sampled rows / their time, in the metric's unit."""
     from oracle.moe import moe_reference
-    from tests.gpu_helpers import dev_experts
+    from tests.gpu_helpers import dev_experts, oracle_workers
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # noqa: BLE001
         blas_threads = None
-    tokens = sorted(np.random.default_rng(0).choice(p.T, ntok, replace=False).tolist())
-    args = (p.x_q.cpu().numpy(), p.x_s.cpu().numpy(), dev_experts(p.w13_q), dev_experts(p.w13_s),
-            dev_experts(p.w2_q), dev_experts(p.w2_s), p.topk_ids.cpu().numpy(), p.topk_weights.cpu().numpy())
-    t0 = time.perf_counter()
-    moe_reference(*args, tokens=tokens)
-    dt = time.perf_counter() - t0
-    flops = 6.0 * ntok * p.K * p.H * p.I
     cores = len(os.sched_getaffinity(0))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores, "kind": "oracle",
-            "sample": f"{ntok} of {p.T} prefill tokens ({ntok * p.K} expert evaluations, float64 numpy), "
-                      f"{dt:.1f} s; host affinity {cores} cores, BLAS threads {blas_threads}",
-            "seconds": dt}
+    workers = oracle_workers()
+
+    def run(p, ids):
+        args = (p.x_q.cpu().numpy(), p.x_s.cpu().numpy(), dev_experts(p.w13_q), dev_experts(p.w13_s),
+                dev_experts(p.w2_q), dev_experts(p.w2_s), ids, p.topk_weights.cpu().numpy())
+        t0 = time.perf_counter()
+        moe_reference(*args, workers=workers)
+        return time.perf_counter() - t0
+
+    dec_ids = dec.topk_ids.cpu().numpy()
+    dec_s = run(dec, dec_ids)
+    ids = pre.topk_ids.cpu().numpy()
+    keep = np.arange(0, pre.E, pre.E // experts_sampled)
+    sampled = np.where(np.isin(ids, keep), ids, -1).astype(np.int32)
+    rows = int(np.count_nonzero(sampled >= 0))
+    all_rows = int(np.count_nonzero((ids >= 0) & (ids < pre.E)))
+    pre_s = run(pre, sampled)
+    flops = 6.0 * rows * pre.H * pre.I
+    return {"value": flops / pre_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"prefill: all {rows} routed rows of {len(keep)} of {pre.E} experts (every "
+                      f"{pre.E // experts_sampled}th), {pre_s:.1f} s; decode: the whole layer, {dec_s:.1f} s; float64 "
+                      f"numpy, {workers} experts at once, BLAS threads {blas_threads}, host affinity {cores} cores",
+            "seconds_per_layer": {"decode": round(dec_s, 2), "prefill": round(pre_s * all_rows / rows, 1)},
+            "seconds": round(dec_s + pre_s, 2)}
 
 
 def main():
@@ -550,14 +591,17 @@ def main():
     ms_rm = event_time_ms(lambda: fused(pre, out, ws, packed=False), max(3, args.steps // 2), 1)
     log(f"prefill with row-major weights {ms_rm * 1e3:.1f} us/layer")
 
-    # dominant kernel: GEMM1 (+SwiGLU+requant) -- 4*R*H*I algorithmic FLOP per launch
+    # dominant kernel: GEMM1 (+SwiGLU+requant) -- 4*R*H*I algorithmic FLOP per launch, and its
+    # algorithmic bytes: every expert's W13 once, x and its scales, q and its scales written
     g1_flop = 4.0 * pre.T * pre.K * pre.H * pre.I
-    g1_tflops = g1_flop / (pst["gemm1_ms"] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(g1_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g1_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                "kernel": f"gemm1_swiglu_quant_kernel<{pst['tile_m_gemm1']}, true, false, false> (MFMA-tiled weights, FP8 block scales)",
-                "per_launch": f"4*R*H*I = {g1_flop:.4g} FLOP (R=T*K={pre.T * pre.K})",
-                "avg_launch_ms": round(pst["gemm1_ms"], 4)}
+    g1_bytes = int(pre.E * 2 * pre.I * pre.H + pre.T * pre.H + 4 * pre.T * (pre.H // 128)
+                   + pre.T * pre.K * pre.I + 4 * pre.T * pre.K * (pre.I // 128))
+    roofline = gemm1_roofline(g1_flop, g1_bytes, pst["gemm1_ms"])
+    roofline.update({
+        "kernel": f"gemm1_swiglu_quant_kernel<{pst['tile_m_gemm1']}, true, false, false> (MFMA-tiled weights, FP8 block scales)",
+        "per_launch": f"4*R*H*I = {g1_flop:.4g} FLOP (R=T*K={pre.T * pre.K}); {g1_bytes} algorithmic bytes "
+                      f"(W13 of all {pre.E} experts, x + scales, q + scales)",
+        "avg_launch_ms": round(pst["gemm1_ms"], 4), "traffic": None})
 
     tc = TRAFFIC_COUNTERS
     if args.traffic_kib:
@@ -571,10 +615,9 @@ def main():
         # the same peak at the clock GEMM1 actually sustains (power-limited under fp8 MFMA + HBM load)
         ghz = tc["gemm1_grbm_count"] / NUM_XCD / (tc["gemm1_grbm_dur_us"] * 1e3)
         peak_s = PEAK_FP8_TFLOPS * ghz / PEAK_CLOCK_GHZ
-        roofline.update({"sustained_clock_ghz": round(ghz, 3), "peak_at_sustained_clock": round(peak_s, 1),
-                         "frac_at_sustained_clock": round(g1_tflops / peak_s, 4)})
-    roofline["algorithmic_bytes"] = int(pre.E * 2 * pre.I * pre.H + pre.T * pre.H + 4 * pre.T * (pre.H // 128)
-                                        + pre.T * pre.K * pre.I + 4 * pre.T * pre.K * (pre.I // 128))
+        roofline.update({"sustained_clock_ghz": round(ghz, 3), "mfma_peak_at_sustained_clock": round(peak_s, 1),
+                         "frac_mfma_at_sustained_clock": round(roofline["achieved_TFLOPs"] / peak_s, 4)})
+    roofline["algorithmic_bytes"] = g1_bytes
     if args.profile == "prefill":
         log("stream kernel (counter calibration)")
         gbs = stream_bandwidth_gbs()
@@ -587,22 +630,32 @@ def main():
     wsd = fm.alloc_workspace(dec.T, dec.H, dec.I, dec.E, dec.K, "cuda")
     outd = torch.empty((dec.T, dec.H), dtype=torch.bfloat16, device="cuda")
     dstep = lambda: fused(dec, outd, wsd)
-    dms = event_time_ms(dstep, max(args.steps, 10), args.warmup)
+    # timing protocol of an HBM-bound shape: a 512 MB write flushes L2 and the Infinity Cache before
+    # every timed call (not timed), median over the calls; the warm back-to-back mean is kept beside it
+    dms_warm = event_time_ms(dstep, max(args.steps, 10), args.warmup)
+    dms = cold_time_ms(dstep, max(args.steps, 20))
     dbytes, dactive = algorithmic_bytes(dec)
     dgbs = dbytes / (dms * 1e-3) / 1e9
     dst = stage_times(dec, max(5, args.steps // 2), 2)
-    # the same layer in two launches (routing + one persistent cooperative kernel)
-    wss = torch.empty(fm.fused_small_workspace_size(dec.T, dec.H, dec.I, dec.E, dec.K), dtype=torch.uint8,
-                      device="cuda")
-    sms = event_time_ms(lambda: fm.moe_fused_fp8_small(dec.x_q, dec.x_s, dec.w13_p, dec.w13_s, dec.w2_p, dec.w2_s,
-                                                       dec.topk_ids, dec.topk_weights, out=outd, workspace=wss,
-                                                       weight_layout=fm.WEIGHTS_MFMA_TILED),
-                        max(args.steps, 10), args.warmup)
-    del wss
-    log(f"decode {dms * 1e3:.1f} us/layer, {dgbs:.0f} GB/s ({dactive} active experts); two-launch "
-        f"{sms * 1e3:.1f} us", dst)
+    # the same layer in two launches (routing + one persistent cooperative kernel); not in the
+    # counter passes (--profile decode), which measure the four-launch layer only
+    sms = None
+    if args.profile != "decode":
+        wss = torch.empty(fm.fused_small_workspace_size(dec.T, dec.H, dec.I, dec.E, dec.K), dtype=torch.uint8,
+                          device="cuda")
+        small = lambda: fm.moe_fused_fp8_small(dec.x_q, dec.x_s, dec.w13_p, dec.w13_s, dec.w2_p, dec.w2_s,
+                                               dec.topk_ids, dec.topk_weights, out=outd, workspace=wss,
+                                               weight_layout=fm.WEIGHTS_MFMA_TILED)
+        small()
+        sms = cold_time_ms(small, max(args.steps, 20))
+        del wss
+    log(f"decode {dms * 1e3:.1f} us/layer cold median, {dgbs:.0f} GB/s ({dactive} active experts); warm "
+        f"{dms_warm * 1e3:.1f} us; two-launch {sms * 1e3 if sms else float('nan'):.1f} us", dst)
     decode = {"us_per_layer": round(dms * 1e3, 2), "GBps": round(dgbs, 1), "frac_hbm": round(dgbs / PEAK_HBM_GBS, 4),
-              "us_per_layer_two_launch": round(sms * 1e3, 2),
+              "timing": f"median of {max(args.steps, 20)} calls, caches flushed (512 MB write) before each",
+              "us_per_layer_warm": round(dms_warm * 1e3, 2),
+              "GBps_warm": round(dbytes / (dms_warm * 1e-3) / 1e9, 1),
+              "us_per_layer_two_launch": round(sms * 1e3, 2) if sms else None,
               "algorithmic_bytes": dbytes, "active_experts": int(dactive), "stages_ms": dst,
               "workload": "decode T=64 H=7168 I=2048 E=256 top-8"}
     if args.profile == "decode":
@@ -639,8 +692,11 @@ def main():
         log("bf16 layer")
         result["bf16"] = bf16_bench(max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a token sample")
-        result["cpu_baseline"] = cpu_baseline(pre)
+        log("timing the CPU oracle: the decode layer, and a sample of the prefill experts")
+        cb = cpu_baseline(pre, dec)
+        cb["gpu_speedup"] = {"decode": round(cb["seconds_per_layer"]["decode"] / (dms * 1e-3)),
+                             "prefill": round(cb["seconds_per_layer"]["prefill"] / (ms * 1e-3))}
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 
