@@ -15,4 +15,5 @@ from .ops import (  # noqa: F401
     gemm1_swiglu_quant_mxfp4, gemm2_weighted_mxfp4, gemm1_swiglu_quant_mx, gemm2_weighted_mx,
     fused_bf16_workspace_size, alloc_workspace_bf16, moe_fused_bf16, gemm1_swiglu_bf16, gemm2_weighted_bf16,
     tune_tiles_fp8, moe_fused_fp8_small, fused_small_workspace_size, small_layer_flag,
+    moe_fused_fp8_noalloc, NOALLOC_SCRATCH_BYTES,
 )

@@ -22,6 +22,9 @@ SIGNATURES = {
     "moe_fused_fp8_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _psz]),
     "moe_fused_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                      _vp, _vp, _sz, _i32, _i32, _i32, _vp]),
+    # x, x_scale, w13, w13_scale, w2, w2_scale, ids, weights, T, H, I, E, K, out, tile_m, tile_n, layout, stream
+    "moe_fused_fp8_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                                             _vp, _i32, _i32, _i32, _vp]),
     "moe_gemm1_swiglu_quant": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
                                               _vp, _vp, _i64, _i32, _i32, _vp]),
     "moe_gemm2_weighted": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libfp8moe.so")
 
 SOURCES = ["api.cpp", "tile_select.cpp", "route.hip", "gemm1.hip", "gemm2.hip", "gemm1_mx.hip", "gemm2_mx.hip", "gemm1_mxfp4.hip",
            "gemm2_mxfp4.hip", "gemm1_bf16.hip", "gemm2_bf16.hip", "gemm_plain.hip", "fused_small.hip",
-           "combine.hip", "gated_act.hip", "pack.hip"]
+           "combine.hip", "gated_act.hip", "pack.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -454,6 +454,30 @@ int moe_fused_fp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int
   return ok();
 }
 
+int moe_fused_fp8_noalloc(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
+                          const void* w2, const float* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, void* out, int32_t tile_m,
+                          int32_t tile_n, int32_t weight_layout, void* stream) {
+  int st = check_dims(T, H, I, E, K);
+  if (st) return st;
+  const size_t need = ws_layout(T, H, I, E, K, kFmtFp8).total;
+  if (need > FP8MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(FP8MOE_ERR_LIMIT, "the layer needs %zu bytes of workspace; the allocation-free call holds %u",
+                need, (unsigned)FP8MOE_NOALLOC_SCRATCH_BYTES);
+  // everything fused_impl checks, before the one runtime query below
+  if ((st = check_tile_requests(tile_m, tile_m, tile_n))) return st;
+  if (!valid_layout(weight_layout)) return fail(FP8MOE_ERR_SHAPE, "weight_layout %d not 0 or 1", weight_layout);
+  if (T > 0 && (!x || !x_scale || !w13 || !w13_scale || !w2 || !w2_scale || !topk_ids || !topk_weights || !out))
+    return fail(FP8MOE_ERR_NULL, "null tensor argument");
+  void* ws = nullptr;
+  if (T > 0) {
+    const hipError_t err = noalloc_scratch(&ws);
+    if (err != hipSuccess) return hip_fail(err, "scratch array address");
+  }
+  return fused_impl<kFmtFp8>(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, T, H, I, E, K, out,
+                             ws, FP8MOE_NOALLOC_SCRATCH_BYTES, tile_m, tile_m, tile_n, weight_layout, stream);
+}
+
 int moe_fused_mxfp8_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K, size_t* bytes) {
   int st = check_dims(T, H, I, E, K);
   if (st) return st;

@@ -86,6 +86,10 @@ hipError_t launch_gemm1_bf16(const uint16_t* x, const uint16_t* w13, const Group
 hipError_t launch_gemm2_bf16(const uint16_t* q, const uint16_t* w2, const float* topk_weights, const GroupedRows& g,
                              int H, int I, uint16_t* Y, int tile_m, int tile_n, bool packed, hipStream_t stream);
 
+// Device address, on the current device, of the allocation-free layer's
+// scratch array (FP8MOE_NOALLOC_SCRATCH_BYTES; noalloc.hip).
+hipError_t noalloc_scratch(void** ptr);
+
 // Plain grouped GEMM: out[p] = a[p] . b[e]^T (fp32) for every padded row p of
 // expert e with sorted_src[p] >= 0; gated: out[p, c] = silu(h[c]) * h[n/2 + c]
 // ([rows][n/2]).  tile_m in {16, 32, 64, 128}.

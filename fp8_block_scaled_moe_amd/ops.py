@@ -174,6 +174,27 @@ def moe_fused_fp8_small(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20   # FP8MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_fused_fp8_noalloc(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, out,
+                          tile_m=-1, tile_n=-1, weight_layout=WEIGHTS_ROW_MAJOR):
+    """The fused FP8 layer with its workspace taken from the library's own device array
+    (moe_fused_fp8_noalloc): same results as moe_fused_fp8, no device allocation by the
+    library or here (the caller passes `out`).  Calls on one GPU share the array, so calls
+    that overlap in time race.  Raises Fp8MoeError (FP8MOE_ERR_LIMIT) when the shape's
+    workspace exceeds the array."""
+    x, w13, w2 = _u8(x), _u8(w13), _u8(w2)
+    T, H, I, E, K = _check_fp8_layer(x, x_scale, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H]")
+    check(lib().moe_fused_fp8_noalloc(_p(x), _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
+                                      _p(topk_ids), _p(topk_weights), T, H, I, E, K, _p(out), tile_m, tile_n,
+                                      weight_layout, _stream(x.device)))
+    return out
+
+
 def small_layer_flag(workspace, T, H, I, E, K):
     """(top barrier counter, error flag) a moe_fused_fp8_small call left in its workspace (host
     copy; synchronises with the device).  After a complete call the counter is 16 (8 groups

@@ -144,6 +144,35 @@ int moe_fused_fp8(const void* x, const float* x_scale,
                   void* out, void* workspace, size_t workspace_bytes,
                   int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream);
 
+/* ---------------------------------------------------------------- the fused layer without allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * moe_fused_fp8_noalloc computes exactly what moe_fused_fp8 computes, with
+ * the same kernels (bit-identical outputs), taking its workspace from a
+ * device array inside the library (FP8MOE_NOALLOC_SCRATCH_BYTES, 64 MiB)
+ * instead of a caller's buffer.  Each GPU the library runs on holds its own
+ * copy of that array from the first call on it until the process ends.  The
+ * caller still owns and passes the inputs and `out`; arguments mean what they
+ * mean for moe_fused_fp8.  No part of the array needs to start cleared: every
+ * kernel of the layer writes what the next one reads.
+ *
+ * Limit: the workspace moe_fused_fp8_workspace_size reports for the shape
+ * must fit the array, else FP8MOE_ERR_LIMIT before anything is enqueued (at
+ * H = 7168, I = 2048, E = 256, top-8: up to about 450 tokens).
+ * Calls that overlap in time on one GPU (two streams, or two host threads)
+ * share the array and race: serialise them.  Allocates nothing and never
+ * synchronises the host; the first call on a device looks the array's device
+ * address up once (a runtime query, no allocation).
+ */
+#define FP8MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_fused_fp8_noalloc(const void* x, const float* x_scale,
+                          const void* w13, const float* w13_scale,
+                          const void* w2, const float* w2_scale,
+                          const int32_t* topk_ids, const float* topk_weights,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                          void* out, int32_t tile_m, int32_t tile_n, int32_t weight_layout, void* stream);
+
 /* ---------------------------------------------------------------- stages of the fused layer
  * The three compute stages moe_fused_fp8 runs after routing, exposed so each
  * can be checked on its own.  They consume moe_route_permute's outputs (any

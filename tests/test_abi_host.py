@@ -229,6 +229,30 @@ def test_tune_tiles_and_fused_tiles_validation():
     assert fused(T=0, ptr=NULL, out=NULL) == OK
 
 
+def test_noalloc_validation():
+    """The allocation-free layer rejects, before any HIP call, a shape whose workspace does
+    not fit its 64 MiB array, and everything moe_fused_fp8 rejects; T = 0 is a no-op."""
+    L = lib()
+    def noalloc(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, out=FAKE, tm=-1, tn=-1, layout=0):
+        return L.moe_fused_fp8_noalloc(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, K, out, tm, tn, layout,
+                                       NULL)
+    assert fm.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the largest decode batch that fits at H=7168, I=2048, E=256, top-8, and the next one past it
+    fits = [T for T in range(1, 1024) if fm.fused_workspace_size(T, 7168, 2048, 256, 8) <= fm.NOALLOC_SCRATCH_BYTES]
+    tmax = max(fits)
+    assert 400 <= tmax < 512 and fits == list(range(1, tmax + 1))
+    assert noalloc(T=tmax + 1, H=7168, I=2048, E=256, K=8) == E_LIMIT
+    assert b"allocation-free" in L.moe_last_error()
+    assert noalloc(T=4096, H=2048, I=768, E=128, K=8) == E_LIMIT
+    assert noalloc(H=200) == E_ALIGN
+    assert noalloc(K=5) == E_TOPK
+    assert noalloc(tm=48) == E_TILE
+    assert noalloc(ptr=NULL) == E_NULL
+    assert noalloc(out=NULL) == E_NULL
+    assert noalloc(layout=2) == E_SHAPE
+    assert noalloc(T=0, ptr=NULL, out=NULL) == OK
+
+
 def test_small_layer_validation():
     L = lib()
     def small(T=16, H=256, I=128, E=4, K=2, ptr=FAKE, ws=FAKE, wsb=1 << 40, tm=-1, out=FAKE, layout=0):
