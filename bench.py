@@ -42,7 +42,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 --profile runs one workload only, for rocprofv3 passes: prefill (the layer,
 its stages and the 2 GiB stream kernel), decode (prefill, then the decode
-layer), gated (the gated-act sweep), mx (the MXFP8 layer), mxfp4 (the MXFP4
+layer and its stages, then the stream kernel), gated (the gated-act sweep), mx (the MXFP8 layer), mxfp4 (the MXFP4
 layer) or bf16 (the bf16 layer).  --traffic-kib takes GEMM1's
 FETCH_SIZE and WRITE_SIZE per dispatch and the stream kernel's (KiB, as
 rocprofv3 --pmc reports them) and fills roofline.traffic from them instead of
@@ -659,7 +659,9 @@ def main():
               "algorithmic_bytes": dbytes, "active_experts": int(dactive), "stages_ms": dst,
               "workload": "decode T=64 H=7168 I=2048 E=256 top-8"}
     if args.profile == "decode":
-        print(json.dumps({"profile": "decode", "decode": decode}), flush=True)
+        log("stream kernel (counter calibration)")
+        gbs = stream_bandwidth_gbs()
+        print(json.dumps({"profile": "decode", "decode": decode, "stream_GBps": round(gbs, 1)}), flush=True)
         return
 
     result = {
