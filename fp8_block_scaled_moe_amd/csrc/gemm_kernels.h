@@ -693,8 +693,20 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
     }
   };
 
-  // carried across the step boundary: the first two fragments and the scales of the next step
-  v8i af[3];
+  // FP8 bodies with at least four token sub-tiles pipeline the MFMAs across the
+  // step barrier: each step also issues the first two sub-tiles of the next
+  // step (their fragments come from the buffer published one barrier earlier)
+  // before its barrier, so the matrix pipe works through the barrier wait and
+  // the weight-ring reload; the products are folded after the barrier (after
+  // the epilogue when the step starts a new N tile).  Sub-tile ts of the
+  // round's step s is number u = s * TS + ts: its fragment lives in af[u % 4]
+  // and its product in pe[u % 2] (4 * TS is a multiple of both, so every slot
+  // is a constant of the unrolled round).
+  constexpr bool EARLY = !MX && !BF && TS >= 4;
+  // carried across the step boundary: fragments (the first two of the next
+  // step; EARLY: the third and fourth) and the scales of the next step
+  v8i af[4];
+  v4f pe[2][2];   // EARLY: products of the next step's first two sub-tiles
   float sa[TS];
   float sb0, sb1;
   uint32_t sx[SPB][TSW];   // MX token scale codes (per MFMA of the step)
@@ -729,9 +741,55 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   };
 
   static_assert(D == 4, "the token buffers follow the weight ring slot");
+  // EARLY: fold the product in pe slot `slot` of token sub-tile ts with this step's scales
+  auto efold = [&](int slot, int ts) __attribute__((always_inline)) {
+    acc[ts][0] += pe[slot][0] * (sa[ts] * sb0);
+    acc[ts][1] += pe[slot][1] * (sa[ts] * sb1);
+  };
+  auto emfma = [&](int slot, int ws, int fslot) __attribute__((always_inline)) {
+    pe[slot][0] = mfma16x16x128_fp8(wr[ws][0], af[fslot], zero);
+    pe[slot][1] = mfma16x16x128_fp8(wr[ws][1], af[fslot], zero);
+  };
+  // EARLY step j = (N tile n, K step k), round slot s: on entry the products of
+  // its sub-tiles 0 and 1 are in pe, the fragments of 2 and 3 are read (in
+  // flight) and sa/sb hold its scales; on exit the same holds for step j+1.
+  auto step_early = [&](int s, int nx, int kx) __attribute__((always_inline)) {
+    const int u0 = s * TS;   // sub-tile number of (this step, ts 0) within the round
+    dma_a((s + 3) & 3);      // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
+    __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
+    efold(u0 & 1, 0);
+#pragma unroll
+    for (int ts = 2; ts < TS; ++ts) {
+      // the fragment two sub-tiles ahead: this step's, or the next step's
+      // first two (same slot number: u0 + ts + 2)
+      af[(u0 + ts + 2) & 3] = ts + 2 < TS ? frag(s, ts + 2) : frag((s + 1) & 3, ts + 2 - TS);
+      emfma((u0 + ts) & 1, s, (u0 + ts) & 3);
+      efold((u0 + ts - 1) & 1, ts - 1);
+    }
+    // the next step's first two sub-tiles (weights of ring slot s + 1, loaded
+    // three steps ago), reading its fragments 2 and 3 two sub-tiles ahead
+    af[(u0 + TS + 2) & 3] = frag((s + 1) & 3, 2);
+    emfma((u0 + TS) & 1, (s + 1) & 3, (u0 + TS) & 3);
+    efold((u0 + TS - 1) & 1, TS - 1);
+    read_scales(nx, kx);     // the next step's scales, for the folds after the barrier
+    af[(u0 + TS + 3) & 3] = frag((s + 1) & 3, 3);
+    emfma((u0 + TS + 1) & 1, (s + 1) & 3, (u0 + TS + 1) & 3);
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) {
+      asm volatile("" : "+v"(acc[ts][0]));
+      asm volatile("" : "+v"(acc[ts][1]));
+    }
+    load_w(s);               // ring slot s was last read two MFMA pairs ago
+    publish_wait(s);
+    step_barrier();
+  };
   // one step j = (N tile n, K step k) with ring slot / buffer s = j % 4;
   // (nx, kx) is step j+1
   auto step = [&](int s, int nx, int kx) __attribute__((always_inline)) {
+    if constexpr (EARLY) {
+      step_early(s, nx, kx);
+      return;
+    }
     dma_a((s + 3) & 3);        // rows of step j+3 -> buffer (j+3) % 4, last read at step j-1
     __builtin_amdgcn_sched_barrier(0);   // the publish wait counts on these being the step's oldest
     if constexpr (BF) {
@@ -817,7 +875,17 @@ __device__ __forceinline__ void ws_mainloop(uint8_t* smem, const TokenBuffers& t
   vmcnt_wait<APW + wl(0) + wl(1) + wl(2) + wl(3)>();
   __syncthreads();
   next_round();
-  prefetch(0, 0, 0);
+  if constexpr (EARLY) {
+    af[0] = frag(0, 0);
+    af[1] = frag(0, 1);
+    read_scales(0, 0);
+    af[2] = frag(0, 2);
+    emfma(0, 0, 0);
+    af[3] = frag(0, 3);
+    emfma(1, 0, 1);
+  } else {
+    prefetch(0, 0, 0);
+  }
 
   // Rounds of D steps.  A run of several N tiles needs KT % D == 0 (the host
   // only forms such runs then), so N tiles end on round boundaries and the
