@@ -1080,8 +1080,20 @@ __device__ __forceinline__ void gemm1_tile(
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w * TM + row]);
         const float sc = amax > 0.f ? amax / kE4m3Max : 1.0f;
+        // q = e4m3(act / s) from the correctly rounded fp32 quotient (a bare
+        // multiply by 1/s can be one ulp off): one reciprocal per row, then
+        // Markstein's residual step, q0 = act * (1/s), q = q0 + (act - s q0) / s
+        // with both fmas rounded once, which gives the correctly rounded
+        // quotient when 1/s is and the residual does not underflow (|act|
+        // above about 2^-100; below it the quotient stays within an ulp)
         const float inv = 1.0f / sc;
-        *qd = pack4_e4m3(act[ts][0] * inv, act[ts][1] * inv, act[ts][2] * inv, act[ts][3] * inv);
+        float qv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float q0 = act[ts][r] * inv;
+          qv[r] = fmaf(fmaf(-sc, q0, act[ts][r]), inv, q0);
+        }
+        *qd = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
         if (wave == 0 && g == 0) q_scale[prow * IB + n0 / 128] = sc;
       }
     }

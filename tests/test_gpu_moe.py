@@ -21,7 +21,7 @@ from oracle import formats as F
 from oracle.route import route_reference
 from tests.cases import crafted_exact_case
 from tests.gpu_helpers import (say, assert_close_to_oracle, assert_rows_close_to_oracle, e4m3_ordinal, dev_experts,
-                               oracle_workers)
+                               oracle_workers, swiglu_error_bound, e4m3_rounding_interval)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +69,42 @@ def test_tiny_deterministic(tiny):
     assert torch.equal(a, b)
 
 
+def check_fp8_requant(q, q_s, st, A, W13):
+    """GPU intermediate (e4m3 codes q, fp32 1x128 scales q_s) of one expert's rows against
+    the oracle's stages st, with A the rows' dequantised activations and W13 the expert's
+    dequantised gate/up weights.  The GEMM1 outputs carry at most MFMA_REL_BOUND *
+    sum|terms| of error (the MFMA's measured precision), which SwiGLU carries into a band
+    around the oracle's activation: every scale must be amax/448 of some block in that
+    band, and every code the rounding (correctly rounded divide by the GPU's own scale)
+    of some activation in it.  Returns (codes differing from the oracle's, codes
+    compared where the two scales agree to 2^-16)."""
+    I = W13.shape[0] // 2
+    H1, act = st["H1"], st["act"].astype(np.float64)
+    S = np.abs(A) @ np.abs(W13).T
+    dact = swiglu_error_bound(H1[:, :I], H1[:, I:], S[:, :I], S[:, I:])
+    n = act.shape[0]
+    blk = lambda m: m.reshape(n, I // 128, 128)
+    amax = np.abs(blk(act)).max(axis=2)
+    damax = blk(dact).max(axis=2)
+    sg = q_s.astype(np.float64)
+    tol = 2.0 ** -22                                       # fp32 rounding of amax and of amax / 448
+    lo_s = np.maximum(amax - damax, 0.0) / 448.0 * (1 - tol)
+    hi_s = (amax + damax) / 448.0 * (1 + tol)
+    may_be_zero = amax - damax <= 0                        # an all-zero block has s = 1
+    assert np.all(((sg >= lo_s) & (sg <= hi_s)) | (may_be_zero & (sg == 1.0))), "scale outside the band"
+    lo, hi = e4m3_rounding_interval(q)
+    scale = np.repeat(sg, 128, axis=1)
+    ok = (act + dact >= lo * scale * (1 - tol)) & (act - dact <= hi * scale * (1 + tol))
+    assert np.all(ok), f"{np.count_nonzero(~ok)} codes are not a rounding of any activation in the band"
+    # the two scales come from the same amax through fp32 (GPU) and fp64 (oracle) sums, so
+    # they agree to a few ulps of fp32 wherever no rounding of the MFMA moved the block's amax
+    so = st["s"].astype(np.float64)
+    same = np.repeat(np.abs(sg - so) <= 2.0 ** -16 * so, 128, axis=1)
+    d = np.abs(e4m3_ordinal(q) - e4m3_ordinal(st["q"]))[same]
+    assert d.size == 0 or d.max() <= 1, "a code more than one e4m3 step from the oracle's under the same scale"
+    return int(np.count_nonzero(d)), int(d.size)
+
+
 def test_tiny_stages_match_oracle(tiny):
     ph, pd = tiny
     T, H, I, E, K = ph.T, ph.H, ph.I, ph.E, ph.K
@@ -85,15 +121,23 @@ def test_tiny_stages_match_oracle(tiny):
     ss = r["src_to_sorted"].cpu().numpy()
     qh, qsh, Yh = q.cpu().numpy(), qs.cpu().numpy(), Y.float().cpu().numpy()
     w = ph.topk_weights.numpy()
+    x_deq = F.dequant_rows(ph.x_q.numpy(), ph.x_s.numpy())
+    diff = total = 0
     for e, st in stages.items():
         pos = np.array([ss[t * K + j] for t, j in st["rows"]])
-        # requant scales: same amax/448 rule on activations that agree to fp32 accumulation order
-        np.testing.assert_allclose(qsh[pos], st["s"], rtol=1e-4)
-        d = np.abs(e4m3_ordinal(qh[pos]) - e4m3_ordinal(st["q"]))
-        assert d.max() <= 1 and np.count_nonzero(d) <= 0.01 * d.size
+        toks = [t for t, _ in st["rows"]]
+        W13 = F.dequant_blocks(ph.w13_q.numpy()[e], ph.w13_s.numpy()[e])
+        dd, nn = check_fp8_requant(qh[pos], qsh[pos], st, x_deq[toks], W13)
+        diff, total = diff + dd, total + nn
         ref_y = np.stack([w[t, j] * st["Y"][i] for i, (t, j) in enumerate(st["rows"])])
         srcs = [t * K + j for t, j in st["rows"]]
         assert_close_to_oracle(Yh[srcs], ref_y, f"Y expert {e}")
+    # where the two scales agree, codes differ only where the MFMA's rounding moved an
+    # activation across an e4m3 rounding boundary (the band check above bounds each one)
+    n_codes = sum(len(st["rows"]) for st in stages.values()) * I
+    say(f"tiny stages: {diff} of {total} codes differ from the oracle's ({n_codes} codes in all)")
+    assert n_codes > 0 and total >= 0.5 * n_codes, "scales disagree with the oracle's on too many blocks"
+    assert diff <= 0.01 * total
     assert torch.equal(out, run_fused(pd, tile_m=16))
 
 
