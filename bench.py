@@ -64,9 +64,6 @@ sys.path.insert(0, ROOT)
 import fp8_block_scaled_moe_amd as fm  # noqa: E402
 import synth  # noqa: E402
 
-# tile height (rows) each GEMM runs the cost model's 128-row class with
-CLASS128_TILE = {"gemm1": 128, "gemm2": 160}
-
 METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roofline"
 
 # HBM counters of the dominant kernel (GEMM1 at T=8192) and of the 2 GiB stream
@@ -275,8 +272,8 @@ def skewed_bench(iters=10):
         res = {tm: float(np.median(v)) for tm, v in runs.items()}
         nbytes, active = algorithmic_bytes(p)
         best = min(res[t] for t in forced)
-        auto_tm = fm.select_tile(T * d["K"], d["I"], d["H"], d["E"], 256, True)[0]
-        out.append({"T": T, "active_experts": int(active), "auto_tile_class_gemm1": auto_tm,
+        auto_t1, auto_t2 = fm.auto_tiles(T * d["K"], d["H"], d["I"], d["E"], 256)
+        out.append({"T": T, "active_experts": int(active), "auto_tiles": [auto_t1, auto_t2],
                     "us_auto": round(res[-1] * 1e3, 2),
                     "us_by_tile_m": {str(t): round(res[t] * 1e3, 2) for t in forced},
                     "regret": round(res[-1] / best, 3),
@@ -328,11 +325,11 @@ def stage_times(p, steps, warmup):
     layout as the fused call; outputs preallocated, so each timing is the stage's kernels only)."""
     T, H, I, E, K = p.T, p.H, p.I, p.E, p.K
     R = T * K
-    # tile_m -1 as in the fused call: the cost model's class, the 128-row class
-    # running with each GEMM's largest tile body
+    # tile_m -1 as in the fused call: the auto tiles (GEMM2 the cost model's class,
+    # GEMM1 one class above its own, the 128-row class running each GEMM's largest body)
     cls1, _ = fm.select_tile(R, I, H, E, 256, True)
     cls2, _ = fm.select_tile(R, H, I, E, 256, False)
-    eff1, eff2 = (CLASS128_TILE["gemm1"] if cls1 == 128 else cls1), (CLASS128_TILE["gemm2"] if cls2 == 128 else cls2)
+    eff1, eff2 = fm.auto_tiles(R, H, I, E, 256)
     tm1 = tm2 = -1
     align = 16
     L = fm.WEIGHTS_MFMA_TILED

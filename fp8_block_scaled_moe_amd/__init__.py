@@ -8,7 +8,7 @@ tensors into it.
 from ._lib import lib, Fp8MoeError, LIB_PATH  # noqa: F401
 from .ops import (  # noqa: F401
     route_capacity, route_permute, fused_workspace_size, alloc_workspace, moe_fused_fp8,
-    gemm1_swiglu_quant, gemm2_weighted, combine, gated_act_fp8_quant, select_tile,
+    gemm1_swiglu_quant, gemm2_weighted, combine, gated_act_fp8_quant, select_tile, auto_tiles,
     select_tile_classes, pack_weights, WEIGHTS_ROW_MAJOR, WEIGHTS_MFMA_TILED,
     fused_mx_workspace_size, alloc_workspace_mx, moe_fused_mxfp8, pack_mx_scales, grouped_gemm_fp8,
     fused_mxfp4_workspace_size, alloc_workspace_mxfp4, moe_fused_mxfp4, pack_mxfp4_scales,

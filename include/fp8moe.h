@@ -115,12 +115,11 @@ int moe_route_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, 
  *   workspace / workspace_bytes       device scratch of at least
  *                                     moe_fused_fp8_workspace_size() bytes,
  *                                     256-byte aligned, owned by the caller
- *   tile_m   -1 (auto, wave+residue cost model) or 16, 32, 64, 128, 144,
+ *   tile_m   -1 (auto, moe_auto_tiles) or 16, 32, 64, 128, 144,
  *            160: the largest number of token rows per GEMM tile (16 is the
  *            swap-AB class: tokens on the 16-wide MFMA side); applies to
  *            both GEMMs when given, GEMM1 capped at 128 rows (its largest
- *            tile body).  Auto runs the cost model's 128-row class with
- *            128-row tiles in GEMM1 and 160-row tiles in GEMM2.  The routing
+ *            tile body).  The routing
  *            pads each expert to 16 rows only, and the GEMMs cut each expert
  *            into ceil(rows / tile_m) tiles of equal height (a multiple of
  *            16, at most tile_m)
@@ -429,6 +428,18 @@ int gated_act_fp8_quant(const void* in, int64_t M, int32_t N, void* out, uint8_t
  */
 int moe_select_tile(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t num_cu,
                     int32_t gated, int32_t* tile_m, int32_t* tile_n);
+/* moe_auto_tiles: the tile heights the layer and the GEMM entry points run
+ * when the caller passes tile_m = -1, for `total_rows` routed rows (T*K),
+ * hidden size H, intermediate size I, E experts and num_cu compute units.
+ * GEMM2 (tile_m2) runs moe_select_tile's class; GEMM1 (tile_m1) one class
+ * above its own (16 -> 32 -> 64 -> 128, 128 stays): a measured MI355X
+ * departure from the ladder, which prices a balanced split of the rows while
+ * routing puts more than ceil(R/E) rows on many experts, and a GEMM1 tile that
+ * splits an expert measured far dearer than a GEMM2 one.  The 128-row class
+ * runs 128-row GEMM1 and 160-row GEMM2 tiles.  Pure host code. */
+int moe_auto_tiles(int64_t total_rows, int32_t H, int32_t I, int32_t E, int32_t num_cu, int32_t* tile_m1,
+                   int32_t* tile_m2);
+
 /* The same ladder with the tile classes given explicitly: the narrow
  * (swap-AB) class height and the tile width of each class (narrow, 32, 64,
  * 128).  Lets the ladder be checked against the outcomes the SM120 page
@@ -509,7 +520,7 @@ int moe_fused_fp8_small(const void* x, const float* x_scale, const void* w13, co
 
 /* moe_fused_fp8_tiles: moe_fused_fp8 with separate tile heights for GEMM1
  * (tile_m1) and GEMM2 (tile_m2), e.g. those moe_tune_tiles_fp8 returned.
- * Each is -1 (the cost model's choice) or one of 16, 32, 64, 128, 144 and
+ * Each is -1 (that GEMM's moe_auto_tiles height) or one of 16, 32, 64, 128, 144 and
  * 160; GEMM1 caps it at 128. tile_n is 256. Everything else is as for
  * moe_fused_fp8. */
 int moe_fused_fp8_tiles(const void* x, const float* x_scale, const void* w13, const float* w13_scale,
