@@ -390,6 +390,12 @@ __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The value of lane l ^ 16 (lanes 16 apart swap): ds_swizzle in bit mode
+// within each 32-lane half, and_mask 31, or_mask 0, xor_mask 16.
+__device__ __forceinline__ uint32_t swap_lane16(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+
 // s_waitcnt vmcnt(N) with the LDS and export counters unconstrained (gfx9
 // encoding: vmcnt low bits 3:0 and high bits 15:14).
 template <int N>
@@ -1244,22 +1250,26 @@ __device__ __forceinline__ void gemm2_tile(
       }
       return;
     }
+    // Lanes g and g ^ 1 (16 apart) hold the same token row: band 0 columns
+    // 4g..4g+3 and band 1 columns 16+4g..16+4g+3 each.  An even g keeps band 0
+    // and takes its partner's band 0 columns, an odd g keeps band 1 and takes
+    // its partner's, so each lane stores 8 consecutive columns with one
+    // 16-byte store instead of two 8-byte ones (the store count is what the
+    // epilogue costs).  H is a multiple of 128, so the wave's 32 columns lie
+    // wholly inside or outside the row.
+    const bool odd = g & 1;
+    const int col = c0 + (odd ? 16 + 4 * (g - 1) : 4 * g);
 #pragma unroll
     for (int ts = 0; ts < TS; ++ts) {
       const int src = srow[16 * ts + l16];
       const float wt = wrow_w[16 * ts + l16];
-      if (src < 0) continue;
-      uint16_t* yrow = Y + (size_t)src * H;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const int col = c0 + 16 * w + 4 * g;
-        if (col < H) {
-          uint2 v;
-          v.x = pack2_bf16(wt * acc[ts][w][0], wt * acc[ts][w][1]);
-          v.y = pack2_bf16(wt * acc[ts][w][2], wt * acc[ts][w][3]);
-          *reinterpret_cast<uint2*>(yrow + col) = v;
-        }
-      }
+      const uint32_t p0 = pack2_bf16(wt * acc[ts][0][0], wt * acc[ts][0][1]);
+      const uint32_t p1 = pack2_bf16(wt * acc[ts][0][2], wt * acc[ts][0][3]);
+      const uint32_t q0 = pack2_bf16(wt * acc[ts][1][0], wt * acc[ts][1][1]);
+      const uint32_t q1 = pack2_bf16(wt * acc[ts][1][2], wt * acc[ts][1][3]);
+      const uint32_t r0 = swap_lane16(odd ? p0 : q0), r1 = swap_lane16(odd ? p1 : q1);
+      if (src < 0 || c0 >= H) continue;
+      *reinterpret_cast<uint4*>(Y + (size_t)src * H + col) = odd ? uint4{r0, r1, q0, q1} : uint4{p0, p1, r0, r1};
     }
   };
 
