@@ -72,11 +72,11 @@ METRIC = "fused FP8 MoE layer µs + TFLOP/s (T=8192) and HBM GB/s (T=64), % roof
 # taken on the GEMM sources whose SHA-256 is recorded; reported as
 # roofline.traffic only while those sources are unchanged.
 TRAFFIC_COUNTERS = {
-    "gemm_sources_sha256": "ded682118939231ffeaeb1892508e2e68a41ef9900c13eab834a1690e1f10610",
-    "gemm1_fetch_kib": 5623343, "gemm1_write_kib": 157576,
+    "gemm_sources_sha256": "512591b86984a12c432c10238704ce60f6042689765c72457ef64f9b76549123",
+    "gemm1_fetch_kib": 5620039, "gemm1_write_kib": 157918,
     # GRBM_COUNT (FETCH_SIZE pass): GPU clock cycles per dispatch summed over
     # the 8 XCDs, and the dispatch's average duration under that pass
-    "gemm1_grbm_count": 35703984, "gemm1_grbm_dur_us": 2679.34,
+    "gemm1_grbm_count": 34917591, "gemm1_grbm_dur_us": 2592.23,
     "stream_fetch_kib": 1048591, "stream_write_kib": 2097152,
 }
 GEMM_SOURCES = ("fp8_block_scaled_moe_amd/csrc/gemm_kernels.h", "fp8_block_scaled_moe_amd/csrc/gemm1.hip",
