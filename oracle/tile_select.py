@@ -23,6 +23,12 @@ Readings (bodies absent on the page):
     one tile); the cheaper wins, a tie goes to 128.
   * the narrow side is 8 rows on the page's hardware; the caller passes it
     (16 on MI355X, the narrowest fp8 MFMA).
+
+Pinned against the outcomes the page states (tests/golden), except the upper
+part (193-207 rows per expert) of its "about 129-207 rows -> 64" band: there
+both classes cover 256 rows per expert in equally many tiles of equal area,
+so the cost ties and goes to 128 (parity unpinned for that part; it decides
+tile speed only, never results).
 """
 
 
