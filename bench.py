@@ -272,7 +272,7 @@ def skewed_bench(iters=10):
         res = {tm: float(np.median(v)) for tm, v in runs.items()}
         nbytes, active = algorithmic_bytes(p)
         best = min(res[t] for t in forced)
-        auto_t1, auto_t2 = fm.auto_tiles(T * d["K"], d["H"], d["I"], d["E"], 256)
+        auto_t1, auto_t2 = fm.auto_tiles(T, d["K"], d["H"], d["I"], d["E"], 256)
         out.append({"T": T, "active_experts": int(active), "auto_tiles": [auto_t1, auto_t2],
                     "us_auto": round(res[-1] * 1e3, 2),
                     "us_by_tile_m": {str(t): round(res[t] * 1e3, 2) for t in forced},
@@ -326,10 +326,11 @@ def stage_times(p, steps, warmup):
     T, H, I, E, K = p.T, p.H, p.I, p.E, p.K
     R = T * K
     # tile_m -1 as in the fused call: the auto tiles (GEMM2 the cost model's class,
-    # GEMM1 one class above its own, the 128-row class running each GEMM's largest body)
+    # GEMM1 one class above its own unless T fits it, the 128-row class running each
+    # GEMM's largest body)
     cls1, _ = fm.select_tile(R, I, H, E, 256, True)
     cls2, _ = fm.select_tile(R, H, I, E, 256, False)
-    eff1, eff2 = fm.auto_tiles(R, H, I, E, 256)
+    eff1, eff2 = fm.auto_tiles(T, K, H, I, E, 256)
     tm1 = tm2 = -1
     align = 16
     L = fm.WEIGHTS_MFMA_TILED

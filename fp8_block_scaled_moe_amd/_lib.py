@@ -73,7 +73,7 @@ SIGNATURES = {
     "moe_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "gated_act_fp8_quant": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _vp]),
     "moe_select_tile": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),
-    "moe_auto_tiles": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "moe_auto_tiles": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),
     "moe_select_tile_classes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32]),
 }
 

@@ -128,18 +128,20 @@ int class_tile_m(int cls, bool gated) {
 // H=7168: GEMM1 1.24x slower at 16 rows than at 32, GEMM2 1.03x).  Over uniform
 // routing at H=7168 and Zipf(1.2) routing at H=2048, T from 1 to 8192, one class
 // up was at most 4% slower than the class itself and up to 1.24x faster.
-int auto_tile_m(int64_t R, int n, int k, int E, int num_cu, bool gated) {
-  int cls = select_tile_m(R, n, k, E, num_cu, mi355x_classes(gated));
-  if (gated && cls < 128) cls *= 2;
+// With at most T tokens no expert holds more than T rows when each token's
+// top-k experts are distinct, so GEMM1 keeps the class when T fits it.
+int auto_tile_m(int64_t T, int K, int n, int k, int E, int num_cu, bool gated) {
+  int cls = select_tile_m(T * K, n, k, E, num_cu, mi355x_classes(gated));
+  if (gated && cls < 128 && T > cls) cls *= 2;
   return class_tile_m(cls, gated);
 }
 
 // Largest tile height a GEMM runs with: the requested one (GEMM1 at most
 // 128 rows), else the auto choice.
-int pick_tile_m(int requested, int64_t R, int n, int k, int E, bool gated) {
+int pick_tile_m(int requested, int64_t T, int K, int n, int k, int E, bool gated) {
   const int cap = gated ? kMaxTileGemm1 : kMaxTileGemm2;
   if (requested != -1) return requested < cap ? requested : cap;
-  return auto_tile_m(R, n, k, E, device_num_cu(), gated);
+  return auto_tile_m(T, K, n, k, E, device_num_cu(), gated);
 }
 
 // Scale pointer type of each format: fp32 block scales (FP8) or E8M0 codes
@@ -251,8 +253,8 @@ int fused_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, co
   if (st) return st;
   if ((st = check_tile_requests(tile_m1, tile_m2, tile_n))) return st;
   if (T == 0) return ok();
-  const int tm1 = pick_tile_m(tile_m1, P.R, I, H, E, true);
-  const int tm2 = pick_tile_m(tile_m2, P.R, H, I, E, false);
+  const int tm1 = pick_tile_m(tile_m1, T, K, I, H, E, true);
+  const int tm2 = pick_tile_m(tile_m2, T, K, H, I, E, false);
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = launch_route_permute(topk_ids, (int)P.R, E, P.align, (int)P.cap, P.counts, P.m_indptr, P.padded,
                                         P.sorted_src, P.src_to_sorted, s);
@@ -378,7 +380,7 @@ int gemm1_impl(const void* x, const scale_ptr_t<F>* x_scale, const void* w13, co
   if (T == 0 || cap == 0) return ok();
   if (!x || !w13 || !padded_indptr || !sorted_src || !q || (F != kFmtBf16 && (!x_scale || !w13_scale || !q_scale)))
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
-  int tm = pick_tile_m(tile_m, T * K, I, H, E, true);
+  int tm = pick_tile_m(tile_m, T, K, I, H, E, true);
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = gemm1_launch<F>(static_cast<const uint8_t*>(x), x_scale, static_cast<const uint8_t*>(w13),
                                    w13_scale, g, H, I, static_cast<uint8_t*>(q), q_scale, tm,
@@ -405,7 +407,7 @@ int gemm2_impl(const void* q, const scale_ptr_t<F>* q_scale, const void* w2, con
   if (!q || !w2 || !padded_indptr || !sorted_src || !topk_weights || !Y ||
       (F != kFmtBf16 && (!q_scale || !w2_scale)))
     return fail(FP8MOE_ERR_NULL, "null tensor argument");
-  int tm = pick_tile_m(tile_m, T * K, H, I, E, false);
+  int tm = pick_tile_m(tile_m, T, K, H, I, E, false);
   GroupedRows g{padded_indptr, sorted_src, cap, E, K, (int64_t)T * K, device_num_cu()};
   hipError_t err = gemm2_launch<F>(static_cast<const uint8_t*>(q), q_scale, static_cast<const uint8_t*>(w2), w2_scale,
                                    topk_weights, g, H, I, static_cast<uint16_t*>(Y), tm,
@@ -805,12 +807,13 @@ int moe_select_tile(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t
   return ok();
 }
 
-int moe_auto_tiles(int64_t total_rows, int32_t H, int32_t I, int32_t E, int32_t num_cu, int32_t* tile_m1,
+int moe_auto_tiles(int64_t T, int32_t K, int32_t H, int32_t I, int32_t E, int32_t num_cu, int32_t* tile_m1,
                    int32_t* tile_m2) {
-  if (total_rows < 0 || H <= 0 || I <= 0 || E < 1 || num_cu < 1) return fail(FP8MOE_ERR_SHAPE, "invalid arguments");
+  if (T < 0 || K < 1 || H <= 0 || I <= 0 || E < 1 || num_cu < 1) return fail(FP8MOE_ERR_SHAPE, "invalid arguments");
+  if (T >= kMaxRows || T * K >= kMaxRows) return fail(FP8MOE_ERR_SHAPE, "T*K overflows the int32 row space");
   if (!tile_m1 || !tile_m2) return fail(FP8MOE_ERR_NULL, "null output");
-  *tile_m1 = auto_tile_m(total_rows, I, H, E, num_cu, true);
-  *tile_m2 = auto_tile_m(total_rows, H, I, E, num_cu, false);
+  *tile_m1 = auto_tile_m(T, K, I, H, E, num_cu, true);
+  *tile_m2 = auto_tile_m(T, K, H, I, E, num_cu, false);
   return ok();
 }
 

@@ -599,10 +599,10 @@ def select_tile(total_rows, n, k, E, num_cu=256, gated=False):
     return tm.value, tn.value
 
 
-def auto_tiles(total_rows, H, I, E, num_cu=256):
-    """(GEMM1, GEMM2) tile heights the layer runs with tile_m = -1."""
+def auto_tiles(T, K, H, I, E, num_cu=256):
+    """(GEMM1, GEMM2) tile heights the layer runs with tile_m = -1 for T tokens of K slots."""
     t1, t2 = ctypes.c_int32(0), ctypes.c_int32(0)
-    check(lib().moe_auto_tiles(total_rows, H, I, E, num_cu, ctypes.byref(t1), ctypes.byref(t2)))
+    check(lib().moe_auto_tiles(T, K, H, I, E, num_cu, ctypes.byref(t1), ctypes.byref(t2)))
     return t1.value, t2.value
 
 

@@ -429,15 +429,18 @@ int gated_act_fp8_quant(const void* in, int64_t M, int32_t N, void* out, uint8_t
 int moe_select_tile(int64_t total_rows, int32_t n, int32_t k, int32_t E, int32_t num_cu,
                     int32_t gated, int32_t* tile_m, int32_t* tile_n);
 /* moe_auto_tiles: the tile heights the layer and the GEMM entry points run
- * when the caller passes tile_m = -1, for `total_rows` routed rows (T*K),
- * hidden size H, intermediate size I, E experts and num_cu compute units.
- * GEMM2 (tile_m2) runs moe_select_tile's class; GEMM1 (tile_m1) one class
- * above its own (16 -> 32 -> 64 -> 128, 128 stays): a measured MI355X
- * departure from the ladder, which prices a balanced split of the rows while
- * routing puts more than ceil(R/E) rows on many experts, and a GEMM1 tile that
- * splits an expert measured far dearer than a GEMM2 one.  The 128-row class
- * runs 128-row GEMM1 and 160-row GEMM2 tiles.  Pure host code. */
-int moe_auto_tiles(int64_t total_rows, int32_t H, int32_t I, int32_t E, int32_t num_cu, int32_t* tile_m1,
+ * when the caller passes tile_m = -1, for T tokens with K routed slots each
+ * (T*K rows), hidden size H, intermediate size I, E experts and num_cu compute
+ * units.  GEMM2 (tile_m2) runs moe_select_tile's class; GEMM1 (tile_m1) one
+ * class above its own (16 -> 32 -> 64 -> 128, 128 stays) unless T is at most
+ * the class's height (with distinct experts per token no expert then holds
+ * more rows than one tile of the class).  A measured MI355X departure from
+ * the ladder, which prices a balanced split of the rows while routing puts
+ * more than ceil(T*K/E) rows on many experts, and a GEMM1 tile that splits an
+ * expert measured far dearer than a GEMM2 one.  The 128-row class runs
+ * 128-row GEMM1 and 160-row GEMM2 tiles.  Pure host code; T*K must fit the
+ * int32 row space. */
+int moe_auto_tiles(int64_t T, int32_t K, int32_t H, int32_t I, int32_t E, int32_t num_cu, int32_t* tile_m1,
                    int32_t* tile_m2);
 
 /* The same ladder with the tile classes given explicitly: the narrow

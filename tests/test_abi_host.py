@@ -387,42 +387,51 @@ def test_select_tile_at_the_workloads(R, n, k, E, gated, expect):
     assert fm.select_tile(R, n, k, E, 256, gated)[0] == expect
 
 
-def _one_class_up(cls):
-    return min(2 * cls, 128)
+def _gemm1_class(T, cls):
+    """GEMM1's auto class: one above the ladder's unless T tokens fit the ladder's class."""
+    return cls if cls == 128 or T <= cls else 2 * cls
 
 
 def test_auto_tiles_follow_the_ladder_sweep():
-    """GEMM2's auto tile is the ladder's class, GEMM1's one class above its own; the
-    128-row class runs 128-row GEMM1 and 160-row GEMM2 tiles."""
+    """GEMM2's auto tile is the ladder's class, GEMM1's one class above its own unless T fits
+    it; the 128-row class runs 128-row GEMM1 and 160-row GEMM2 tiles."""
     rng = np.random.default_rng(1)
     for _ in range(3000):
         E = int(rng.choice([1, 4, 8, 32, 64, 128, 256, 512]))
-        R = int(rng.integers(0, 8 * 8192 + 1)) if rng.random() < 0.7 else int(rng.integers(0, 64))
+        K = int(rng.choice([1, 2, 4, 6, 8]))
+        T = int(rng.integers(0, 8192 + 1)) if rng.random() < 0.7 else int(rng.integers(0, 200))
         H = int(rng.choice([512, 2048, 4096, 7168]))
         I = int(rng.choice([256, 768, 2048]))
         cu = int(rng.choice([1, 84, 188, 256, 304]))
+        R = T * K
         c1 = S.select_tile_m(R, I, H, E, cu, 16, MI_GATED)
         c2 = S.select_tile_m(R, H, I, E, cu, 16, MI_PLAIN)
-        assert fm.auto_tiles(R, H, I, E, cu) == (_one_class_up(c1), 160 if c2 == 128 else c2), (R, H, I, E, cu)
+        assert fm.auto_tiles(T, K, H, I, E, cu) == (_gemm1_class(T, c1), 160 if c2 == 128 else c2), \
+            (T, K, H, I, E, cu)
 
 
 @pytest.mark.parametrize("T,H,I,E,expect", [
     (64, 7168, 2048, 256, (32, 16)),       # decode
     (8192, 7168, 2048, 256, (128, 160)),   # prefill
-    (1, 2048, 768, 128, (32, 16)),         # skewed T=1
+    (1, 2048, 768, 128, (16, 16)),         # skewed T=1: one token fits the 16-row class
+    (16, 2048, 768, 128, (16, 16)),        # 16 tokens still fit it
     (33, 2048, 768, 128, (32, 16)),        # skewed T=33
     (512, 2048, 768, 128, (64, 32)),       # skewed T=512
     (4096, 2048, 768, 128, (128, 160)),    # skewed T=4096
 ])
 def test_auto_tiles_at_the_workloads(T, H, I, E, expect):
-    assert fm.auto_tiles(T * 8, H, I, E, 256) == expect
+    assert fm.auto_tiles(T, 8, H, I, E, 256) == expect
 
 
 def test_auto_tiles_validation():
     with pytest.raises(fm.Fp8MoeError):
-        fm.auto_tiles(-1, 7168, 2048, 256)
+        fm.auto_tiles(-1, 8, 7168, 2048, 256)
     with pytest.raises(fm.Fp8MoeError):
-        fm.auto_tiles(16, 7168, 2048, 0)
+        fm.auto_tiles(16, 0, 7168, 2048, 256)
+    with pytest.raises(fm.Fp8MoeError):
+        fm.auto_tiles(16, 8, 7168, 2048, 0)
+    with pytest.raises(fm.Fp8MoeError):
+        fm.auto_tiles(1 << 29, 8, 7168, 2048, 256)
 
 
 def test_header_compiles_as_c_and_links(tmp_path):
