@@ -34,7 +34,9 @@ The line also carries:
                 variant, priced against the dense fp4 MFMA peak (10.1 PFLOP/s).
   bf16          the same for the unquantised bf16 variant, priced against the
                 dense bf16 MFMA peak (2.5 PFLOP/s).
-  cpu_baseline  the CPU oracle timed on a bounded sample of prefill tokens.
+  cpu_baseline  the CPU oracle on the host cores: the whole decode layer and every
+                routed row of 16 of the 256 prefill experts (seconds per layer for
+                both; value = the prefill sample's TFLOP/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                       [--no-extras] [--profile {prefill,decode,gated,mx,mxfp4,bf16}]
